@@ -1,0 +1,47 @@
+"""fp64 CPU oracle for shared-latent MLA attention.  TEST INFRASTRUCTURE ONLY.
+
+This package is the independent reference that the HIP path is checked
+against.  Only the test-suite, the package entry's smoke check and the
+benchmark's CPU-baseline leg may import or call it; the product path never
+does, and it shares no code with the HIP kernels or their binding.
+
+It computes the plain definitions the pages state, in float64 NumPy on the
+bfloat16-rounded inputs, with a two-pass exact softmax (full score row, max,
+exp, sum, divide).  Matrix products are done with NumPy's ``@``; no blocking,
+fusion or reordering is added beyond iterating over independent rows.
+
+Functions and the passages they follow:
+
+* :func:`attention`   -- softmax(scale * Q K^T + causal mask) V with the
+  log-sum-exp per row (TT-NN ``ring_mla`` description and "Returns";
+  Ascend ``RingMLAOperation`` members ``prevLse``, ``qkScale``, ``maskType``,
+  ``softmaxLse``).
+* :func:`dense_mla`   -- the shared-latent form: one KV head whose full width
+  is the key and whose first ``head_dim_v`` columns are the value (TT-NN
+  ``ring_mla`` description and ``head_dim_v``; TensorRT-LLM ``mla.py``,
+  ``MLA.__init__`` building the absorbed backend with
+  ``head_dim = kv_lora_rank + qk_rope_head_dim``, ``num_kv_heads=1``,
+  ``v_head_dim = kv_lora_rank``).
+* :func:`merge`       -- fold of two partial results over disjoint key sets
+  through their log-sum-exp (TensorRT-LLM ``mla.py``,
+  ``forward_context_with_chunked_prefill`` and its FP4 twin's docstring:
+  partial outputs merged with their softmax stats; Ascend ``calcType``:
+  ``prevOut``/``prevLse`` folded into the new output).
+* :func:`ring`        -- successive KV chunks on one device folded in ring
+  order (TensorRT-LLM ``forward_context_with_chunked_prefill``: cached chunks
+  with a FULL mask, the current chunk CAUSAL last; Ascend ``calcType``:
+  first ring step without prev).
+* :func:`split_mla`   -- the split query/key ring step with separate V,
+  per-sequence ``seqLen`` and optional prev fold (Ascend
+  ``AtbRingMLAGetWorkspaceSize`` member table).
+* :func:`sparse_mla`  -- per-query attention over the top-k listed latent
+  cache rows (NKI ``mla_sparse_attention_cte_kernel``, "Parameters" and
+  "Returns").
+
+Every function is pinned by ``tests/test_oracle.py`` against brute force on
+tiny inputs, ``torch.nn.functional.scaled_dot_product_attention`` in float64,
+closed forms, hand-worked values and the chunking invariants.
+"""
+from .mla_ref import attention, dense_mla, merge, ring, ring_order, split_mla, sparse_mla
+
+__all__ = ["attention", "dense_mla", "merge", "ring", "ring_order", "split_mla", "sparse_mla"]

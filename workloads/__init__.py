@@ -1,0 +1,187 @@
+"""Seeded synthetic inputs for shared-latent MLA attention.
+
+This module only draws random numbers and stores them as bfloat16 bit
+patterns.  It holds none of the attention arithmetic, so both the fp64 oracle
+(used by the tests) and the HIP path can be fed from it without sharing any of
+the method's code.
+
+Every tensor is drawn with ``numpy.random.default_rng(seed)`` as float32
+``standard_normal`` and rounded to bfloat16 round-to-nearest-even, in the order
+the workload lists its tensors.  The shapes follow the pages:
+
+* shared-latent rows of 512 latent + 64 RoPE columns with one KV head and
+  ``head_dim_v`` = 512 read from the KV prefix (TT-NN ``ring_mla``,
+  "Parameters" and ``head_dim_v``; TensorRT-LLM ``mla.py``, ``MLA.__init__``
+  building the absorbed ``mqa`` backend with ``num_kv_heads=1``);
+* the split query/key ring step with nope 128 + RoPE 64 and V 128, ``seqLen``
+  per sequence and ``prevOut``/``prevLse`` (Ascend ``RingMLAOperation``,
+  member table of ``AtbRingMLAGetWorkspaceSize``);
+* the sparse top-k latent path with ``q_lift``, ``q_pe``, ``c_kv``, ``k_pe``
+  and flat int32 indices (NKI ``mla_sparse_attention_cte_kernel``,
+  "Parameters").
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+SCALE_192 = 1.0 / math.sqrt(192.0)   # 1/sqrt(qk_nope 128 + qk_rope 64)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 storage helpers (bit manipulation only)
+# ---------------------------------------------------------------------------
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit pattern (uint16), round to nearest even.
+
+    Inputs are finite draws from a normal distribution, so no NaN handling is
+    needed."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+def normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 26) -> np.ndarray:
+    """Draw N(0,1) float32 and round to bf16 bits, in bounded chunks so that a
+    1.2 GB tensor does not need 3x its size of temporaries."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+@dataclass
+class DenseCase:
+    """Shared-latent causal attention: q [B,H,N,dk], kv [B,1,Nkv,dk] (bf16 bits)."""
+    q: np.ndarray
+    kv: np.ndarray
+    head_dim_v: int
+    scale: float
+    causal: bool = True
+    q_offset: int = 0
+    kv_offset: int = 0
+    n_chunks: int = 1      # >1: processed as a one-GPU ring of contiguous chunks
+    name: str = ""
+
+
+@dataclass
+class SplitCase:
+    """Split query/key ring step with per-sequence lengths, [T, H, D] layouts."""
+    seq_lens: np.ndarray   # int32 [n_seqs]
+    q1: np.ndarray         # [T, H, 128]
+    q2: np.ndarray         # [T, H, 64]
+    k1: np.ndarray         # [T, Hkv, 128]
+    k2: np.ndarray         # [T, Hkv, 64]
+    v: np.ndarray          # [T, Hkv, 128]
+    prev_out: Optional[np.ndarray]   # [T, H, 128] bf16 bits
+    prev_lse: Optional[np.ndarray]   # [H, T] float32
+    scale: float
+    causal: bool = True
+    name: str = ""
+
+
+@dataclass
+class SparseCase:
+    """Top-k sparse latent attention, B = 1."""
+    q_lift: np.ndarray     # [B, S, H, L]
+    q_pe: np.ndarray       # [B, S, H, R]
+    c_kv: np.ndarray       # [B, S_kv, L]
+    k_pe: np.ndarray       # [B, S_kv, R]
+    idx: np.ndarray        # int32 [B, S, K]
+    positions: np.ndarray  # int64 [S], query positions (the causal range of the draw)
+    scale: float
+    name: str = ""
+
+
+def dense_case(B: int = 1, H: int = 4, N: int = 128, Nkv: Optional[int] = None,
+               dk: int = 576, dv: int = 512, seed: int = 0, scale: float = SCALE_192,
+               causal: bool = True, q_offset: int = 0, kv_offset: int = 0,
+               n_chunks: int = 1, name: str = "") -> DenseCase:
+    rng = np.random.default_rng(seed)
+    Nkv = N if Nkv is None else Nkv
+    q = normal_bf16(rng, (B, H, N, dk))
+    kv = normal_bf16(rng, (B, 1, Nkv, dk))
+    return DenseCase(q, kv, dv, scale, causal, q_offset, kv_offset, n_chunks, name)
+
+
+def split_case(seq_lens: Optional[List[int]] = None, n_seqs: int = 8, len_lo: int = 1024,
+               len_hi: int = 8192, H: int = 32, Hkv: int = 32, d_nope: int = 128,
+               d_rope: int = 64, dv: int = 128, seed: int = 0, scale: float = SCALE_192,
+               causal: bool = True, with_prev: bool = True, lse_hi: float = 12.0,
+               name: str = "") -> SplitCase:
+    rng = np.random.default_rng(seed)
+    if seq_lens is None:
+        lens = rng.integers(len_lo, len_hi, n_seqs, endpoint=True).astype(np.int32)
+    else:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+    T = int(lens.sum())
+    q1 = normal_bf16(rng, (T, H, d_nope))
+    q2 = normal_bf16(rng, (T, H, d_rope))
+    k1 = normal_bf16(rng, (T, Hkv, d_nope))
+    k2 = normal_bf16(rng, (T, Hkv, d_rope))
+    v = normal_bf16(rng, (T, Hkv, dv))
+    prev_out = prev_lse = None
+    if with_prev:
+        prev_out = normal_bf16(rng, (T, H, dv))
+        prev_lse = rng.uniform(0.0, lse_hi, (H, T)).astype(np.float32)
+    return SplitCase(lens, q1, q2, k1, k2, v, prev_out, prev_lse, scale, causal, name)
+
+
+def sparse_case(S: int = 4096, S_kv: int = 16384, pos0: int = 12288, H: int = 128,
+                L: int = 512, R: int = 64, K: int = 2048, seed: int = 0,
+                scale: float = SCALE_192, name: str = "") -> SparseCase:
+    """Per query i at position pos0 + i, K distinct indices drawn uniformly from
+    the causal range [0, pos], kept in drawn order."""
+    if pos0 + 1 < K:
+        raise ValueError("the first query must have at least K visible rows")
+    rng = np.random.default_rng(seed)
+    q_lift = normal_bf16(rng, (1, S, H, L))
+    q_pe = normal_bf16(rng, (1, S, H, R))
+    c_kv = normal_bf16(rng, (1, S_kv, L))
+    k_pe = normal_bf16(rng, (1, S_kv, R))
+    pos = np.arange(pos0, pos0 + S, dtype=np.int64)
+    if pos[-1] >= S_kv:
+        raise ValueError("query positions must lie inside the cache")
+    idx = np.empty((1, S, K), dtype=np.int32)
+    for i in range(S):
+        idx[0, i] = rng.choice(int(pos[i]) + 1, K, replace=False)
+    return SparseCase(q_lift, q_pe, c_kv, k_pe, idx, pos, scale, name)
+
+
+# The five workloads the method is measured and checked on.
+def tiny(seed: int = 0) -> DenseCase:
+    return dense_case(B=1, H=4, N=128, seed=seed, name="tiny causal MLA H=4 N=128")
+
+
+def ring4(seed: int = 0) -> DenseCase:
+    return dense_case(B=1, H=16, N=4096, seed=seed, n_chunks=4,
+                      name="ring causal MLA H=16 N=4096 in 4 chunks of 1024")
+
+
+def dsv3_prefill(seed: int = 0) -> DenseCase:
+    return dense_case(B=1, H=128, N=8192, seed=seed,
+                      name="DeepSeek-V3 absorbed MLA prefill H=128 N=8192")
+
+
+def split_ring_step(seed: int = 0) -> SplitCase:
+    return split_case(seed=seed, name="split q/k varlen ring step 8 seqs H=32")
+
+
+def sparse_topk(seed: int = 0) -> SparseCase:
+    return sparse_case(seed=seed, name="sparse top-k MLA S=4096 S_kv=16384 H=128 K=2048")
