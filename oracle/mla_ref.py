@@ -216,17 +216,22 @@ def sparse_mla(q_lift, q_pe, c_kv, k_pe, idx, scale: float,
     Query i of batch b attends exactly the K cache rows idx[b, i, :] (a
     multiset: a repeated index counts as often as it is listed; the order is
     irrelevant) with score scale * (q_lift . c_kv + q_pe . k_pe); the value is
-    the latent row c_kv.  All heads of a query share its index list.
+    the latent row c_kv.  All heads of a query share its index list.  The
+    pages leave indices outside [0, S_kv) undefined; here such an entry is
+    not attended (like a -1 padding sentinel), and a query with no valid
+    entry gets out = 0 and lse = -inf.
     """
     B, S, H, L = q_lift.shape
+    S_kv = c_kv.shape[1]
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.zeros((B, len(rows), H * L))
-    lse = np.zeros((B, len(rows), H))
+    lse = np.full((B, len(rows), H), NEG_INF)
     for b in range(B):
         for ri, i in enumerate(rows):
             sel = np.asarray(idx[b, i], dtype=np.int64)
-            if sel.min() < 0 or sel.max() >= c_kv.shape[1]:
-                raise ValueError("top-k index out of range")
+            sel = sel[(sel >= 0) & (sel < S_kv)]
+            if sel.size == 0:
+                continue
             ck = _f64(c_kv[b, sel])                       # [K, L]
             kp = _f64(k_pe[b, sel])                       # [K, R]
             s = scale * (_f64(q_lift[b, i]) @ ck.T + _f64(q_pe[b, i]) @ kp.T)   # [H, K]

@@ -359,11 +359,22 @@ def test_sparse_indices_distinct_and_causal():
         assert row.min() >= 0 and row.max() <= c.positions[i]
 
 
-def test_sparse_rejects_out_of_range_index():
+def test_sparse_out_of_range_index_is_skipped():
+    """An index outside [0, S_kv) is not attended: the result equals the one
+    without that entry; a list with no valid entry gives (0, -inf)."""
     c = _small_sparse()
-    bad = c.idx.copy(); bad[0, 0, 0] = c.c_kv.shape[1]
-    with pytest.raises(ValueError):
-        oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, bad, c.scale)
+    bad = c.idx.copy()
+    bad[0, 0, 0] = c.c_kv.shape[1]
+    bad[0, 1, 3] = -1
+    a = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, bad, c.scale, rows=[0, 1])
+    r0 = oracle.sparse_mla(c.q_lift[:, 0:1], c.q_pe[:, 0:1], c.c_kv, c.k_pe, c.idx[:, 0:1, 1:], c.scale)
+    keep = [j for j in range(c.idx.shape[2]) if j != 3]
+    r1 = oracle.sparse_mla(c.q_lift[:, 1:2], c.q_pe[:, 1:2], c.c_kv, c.k_pe, c.idx[:, 1:2, keep], c.scale)
+    np.testing.assert_allclose(a[0][:, 0], r0[0][:, 0], atol=1e-13)
+    np.testing.assert_allclose(a[0][:, 1], r1[0][:, 0], atol=1e-13)
+    none = np.full_like(c.idx[:, :1], -1)
+    o, l = oracle.sparse_mla(c.q_lift[:, :1], c.q_pe[:, :1], c.c_kv, c.k_pe, none, c.scale)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
 
 
 # ---------------------------------------------------------------------------
