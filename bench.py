@@ -1,0 +1,254 @@
+"""Benchmark: causal shared-latent MLA prefill on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-rows]
+
+Headline workload: DeepSeek-V3-shaped absorbed MLA prefill, B=1, 128 query
+heads over one shared latent KV head, N=8192 causal, dk=576 (512 latent + 64
+RoPE), dv=512, bf16 inputs ~N(0,1) (seed 0), scale 1/sqrt(192).  A step is one
+mla_fwd call over that batch, inputs resident in HBM.  Throughput counts only
+algorithmic flops: visible (query, head, key) triples x (2*dk + 2*dv).
+
+Rank 0 prints ONE JSON line with the headline, its roofline against the
+dense bf16 MFMA peak, the fp64 CPU oracle timed on a bounded sample of the
+same workload, and measured lines for the other steps of the path (one-device
+ring with LSE folds, split varlen ring step, sparse top-k, standalone merge).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "causal MLA prefill TFLOP/s and % of bf16 MFMA peak on 1 MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_latent_dsv3_prefill_hbm_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "ring_chunk_attention_amd", "csrc", "mla_attn.hip")
+
+
+def causal_pairs(n_q: int, n_kv: int, q_offset: int = 0, kv_offset: int = 0) -> int:
+    """Visible (query, key) pairs of one head under the causal mask."""
+    i = np.arange(n_q, dtype=np.int64)
+    vis = np.clip(q_offset + i - kv_offset + 1, 0, n_kv)
+    return int(vis.sum())
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Warm up, then time `steps` calls with HIP events on the current stream;
+    returns (ms per step over the whole region, mean ms per launch)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for k in range(steps):
+        starts[k].record(stream)
+        fn()
+        ends[k].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    region = t0.elapsed_time(t1) / steps
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return region, float(np.mean(per)), float(np.min(per))
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """The fp64 oracle on whole heads of the same workload until the budget is
+    spent; throughput on the same algorithmic flop count."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    B, H, N, dk = case.q.shape
+    flops = 0
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < H and time.perf_counter() - t0 < budget_s:
+        oracle.dense_mla(case.q[:, heads:heads + 1], case.kv, 512, case.scale)
+        flops += causal_pairs(N, N) * (2 * 576 + 2 * 512)
+        heads += 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle on heads 0..{heads - 1} of {H} (all {N} causal rows each), "
+                      f"{dt:.1f} s wall, same flop count per head as the GPU"}
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-rows", action="store_true", help="headline only")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run one plain device copy of 1 GiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              f"multi-GPU path; the ring across GPUs is design-only.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ring_chunk_attention_amd as mla
+    import workloads as W
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    print("bench: generating the DeepSeek-V3 prefill inputs", file=sys.stderr, flush=True)
+    case = W.dsv3_prefill(0)
+    B, H, N, dk = case.q.shape
+    q, kv = to_dev(case.q), to_dev(case.kv)
+    out = torch.empty((B, H, N, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        mla.fwd(q, kv, scale=case.scale, head_dim_v=512, causal=True, out=out, lse=lse)
+
+    print("bench: timing", file=sys.stderr, flush=True)
+    region_ms, launch_ms, launch_min_ms = time_launches(step, args.steps, args.warmup)
+    flops = B * H * causal_pairs(N, N) * (2 * dk + 2 * 512)
+    value = flops / (region_ms * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(region_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": "DeepSeek-V3-shaped absorbed MLA prefill, causal",
+                   "batch": B, "q_heads": H, "kv_heads": 1, "seq_len": N, "dk": dk, "dv": 512,
+                   "scale": "1/sqrt(192)", "inputs": "bf16 N(0,1), seed 0",
+                   "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_fwd_kernel<LatentCfg, LATENT>",
+                     "launch_ms_mean": round(launch_ms, 4), "launch_ms_min": round(launch_min_ms, 4)},
+    }
+    del q, kv, out, lse
+    torch.cuda.empty_cache()
+
+    if not args.no_rows:
+        result["rows"] = measure_rows(mla, W, to_dev, args.steps, args.warmup)
+    if not args.no_cpu:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(result), flush=True)
+
+
+def measure_rows(mla, W, to_dev, steps, warmup):
+    """Time the other steps of the path at their workload shapes."""
+    import torch
+    rows = {}
+    steps = max(3, min(steps, 10))
+
+    # one-device ring: 16 heads, N = 4096 as 4 chunks of 1024, folds in place
+    print("bench: ring workload", file=sys.stderr, flush=True)
+    c = W.ring4(0)
+    q, kv = to_dev(c.q), to_dev(c.kv)
+    o = torch.empty((1, 16, 4096, 512), dtype=torch.bfloat16, device="cuda")
+    l = torch.empty((1, 16, 4096), dtype=torch.float32, device="cuda")
+    ms, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l), steps, warmup)
+    fl = 16 * causal_pairs(4096, 4096) * 2176
+    rows["ring_4x1024_h16"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+                               "calls": 10, "folds_in_epilogue": 6}
+    # the same workload unchunked, for the cost of chunking
+    ms1, _, _ = time_launches(lambda: mla.fwd(q, kv, scale=c.scale, out=o, lse=l), steps, warmup)
+    rows["ring_4x1024_h16"]["unchunked_ms"] = round(ms1, 4)
+    # standalone merge of two [1, 16, 1024, 512] partials (HBM-bound)
+    a, b = o[:, :, :1024].contiguous(), o[:, :, 1024:2048].contiguous()
+    la, lb = l[:, :, :1024].contiguous(), l[:, :, 1024:2048].contiguous()
+    mo, ml = torch.empty_like(a), torch.empty_like(la)
+    ms, _, _ = time_launches(lambda: mla.merge(a, la, b, lb, out=mo, lse=ml), steps, warmup)
+    nbytes = 3 * a.numel() * 2 + 3 * la.numel() * 4
+    rows["merge_h16_1024x512"] = {"ms": round(ms, 4), "GBps": round(nbytes / ms / 1e6, 1),
+                                  "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    del q, kv, o, l, a, b, la, lb, mo, ml
+
+    # split q/k varlen ring step: 8 sequences, 32 heads, prev fold
+    print("bench: split varlen workload", file=sys.stderr, flush=True)
+    c = W.split_ring_step(0)
+    args = [to_dev(x) for x in (c.q1, c.q2, c.k1, c.k2, c.v)]
+    sl = torch.from_numpy(c.seq_lens).cuda()
+    prev = (to_dev(c.prev_out), torch.from_numpy(c.prev_lse).cuda())
+    T = int(c.seq_lens.sum())
+    so = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
+    sL = torch.empty((32, T), dtype=torch.float32, device="cuda")
+    ms, _, _ = time_launches(lambda: mla.split_fwd(*args, scale=c.scale, seq_lens=sl, prev=prev,
+                                                   out=so, lse=sL), steps, warmup)
+    fl = 32 * sum(causal_pairs(int(L), int(L)) for L in c.seq_lens) * (2 * 192 + 2 * 128)
+    rows["split_varlen_8seq_h32"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+                                     "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                                     "tokens": T}
+    del args, sl, prev, so, sL
+
+    # sparse top-k: 4096 queries x 128 heads x 2048 gathered rows
+    print("bench: sparse workload", file=sys.stderr, flush=True)
+    c = W.sparse_topk(0)
+    t = [to_dev(x) for x in (c.q_lift, c.q_pe, c.c_kv, c.k_pe)]
+    idx = torch.from_numpy(c.idx).cuda()
+    so = torch.empty((1, 4096, 128 * 512), dtype=torch.bfloat16, device="cuda")
+    sL = torch.empty((1, 4096, 128), dtype=torch.float32, device="cuda")
+    ms, _, _ = time_launches(lambda: mla.sparse_fwd(*t, idx, scale=c.scale, out=so, lse=sL), steps, warmup)
+    fl = 4096 * 128 * 2048 * 2176
+    gathered = 4096 * 2048 * 1152
+    rows["sparse_topk_s4096_k2048_h128"] = {
+        "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+        "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+        "gather_GBps": round(gathered / ms / 1e6, 1)}
+    return rows
+
+
+if __name__ == "__main__":
+    main()

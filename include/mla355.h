@@ -1,0 +1,206 @@
+/*
+ * mla355.h -- C ABI of the shared-latent MLA attention forward library for
+ * AMD Instinct MI355X (gfx950).  libmla355.so exports exactly the functions
+ * declared here.
+ *
+ * The operation (TT-NN ttnn.transformer.ring_mla, description, "Parameters"
+ * and "Returns"; TensorRT-LLM mla.py, MLA.__init__ building the absorbed
+ * backend with head_dim = kv_lora_rank + qk_rope_head_dim, num_kv_heads = 1,
+ * v_head_dim = kv_lora_rank):
+ *
+ *   causal flash-style attention of many query heads over one shared KV head.
+ *   The score of query row i and key row j is scale * <q_i, kv_j> over the
+ *   full KV width (512 latent + 64 RoPE columns); the value is the first
+ *   head_dim_v columns of the same KV row.  Every call returns the output and
+ *   the per-row natural log-sum-exp of the scaled visible scores (LSE).
+ *
+ * Around it: a fold of a previous (out, LSE) pair into a new one (Ascend
+ * RingMLAOperation, members prevOut / prevLse and calcType), which makes
+ * successive KV chunks on one device a ring, and a top-k sparse variant that
+ * gathers the selected latent-cache rows (NKI mla_sparse_attention_cte_kernel,
+ * "Parameters").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Memory: every data pointer is a DEVICE pointer on the current HIP device.
+ *   The library never allocates, frees or synchronises; it only enqueues work
+ *   on `stream` (0 = the null stream).  The caller keeps every buffer alive
+ *   until that work completes.
+ * - Element types: activations and outputs are bfloat16 (passed as uint16_t
+ *   bit patterns), LSE values are float32, indices and lengths int32.
+ * - Layout: a tensor argument is an mla_rows view: element (b, h, t, d) lives
+ *   at data[b*stride_b + h*stride_h + t*stride_t + d], strides in elements,
+ *   the innermost (feature) dimension contiguous.  Both the [B, H, N, D]
+ *   layout of the TT-NN page and the [tokens, heads, D] layout of the Ascend
+ *   page are such views.  Data pointers and the b/h/t strides of bf16 views
+ *   must be multiples of 8 elements (16 bytes).  LSE views use the same
+ *   struct with d absent (D = 1, any strides).
+ * - Errors: every function validates all arguments before enqueuing anything.
+ *   On failure it enqueues nothing, returns a non-zero mla_status and
+ *   mla_last_error() describes the first problem found.  A HIP launch error
+ *   is returned as MLA_ERR_HIP.  Nothing aborts or throws across the ABI.
+ * - Shapes without a kernel return MLA_ERR_UNSUPPORTED; there is no slow or
+ *   host fallback.
+ */
+#ifndef MLA355_H
+#define MLA355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,   /* a shape, stride, alignment or option is invalid */
+  MLA_ERR_UNSUPPORTED = 2,   /* valid, but no kernel is built for it */
+  MLA_ERR_HIP = 3            /* the HIP runtime reported an error */
+} mla_status;
+
+/* A view of bf16 (or fp32 for LSE) rows; see "Layout" above. */
+typedef struct {
+  void* data;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_t;
+} mla_rows;
+
+/* flags for mla_fwd */
+#define MLA_CAUSAL 1u        /* key j visible to query i iff kv_offset + j <= q_offset + i */
+#define MLA_OUT_F32 2u       /* out holds float32 instead of bf16 */
+#define MLA_PREV_OUT_F32 4u  /* prev_out holds float32 instead of bf16 */
+
+/*
+ * mla_fwd -- one attention call (one ring step).
+ *
+ * Query rows: q [B, Hq, Nq, dq] plus, optionally, q_rope [B, Hq, Nq, dr]; the
+ * query vector is their concatenation (dq + dr columns).  Key rows: kv
+ * [B, Hkv, Nkv, dq] plus, optionally, k_rope [B, Hkv, Nkv, dr]; same split.
+ * Query head h reads KV head h / (Hq / Hkv).  Value rows: v [B, Hkv, Nkv, dv]
+ * or, when v is NULL, the first dv columns of the kv rows (the shared-latent
+ * form: TT-NN ring_mla, head_dim_v read from the KV prefix).  The split form
+ * (q, q_rope, kv, k_rope, v all given) is the Ascend RingMLAOperation step:
+ * querySplit1/2, keySplit1/2 and value.
+ *
+ * Masking: with MLA_CAUSAL, query row i sits at global position q_offset + i
+ * and key row j at kv_offset + j, and j is visible iff its position is not
+ * after i's (TT-NN logical_n: positions are global; Ascend maskType 1 = TRIU).
+ * Without it every key is visible.
+ *
+ * Varlen (Ascend seqLen of shape [batch]): when seq_lens (device int32
+ * [n_seqs]) is given, B must be 1 and Nq == Nkv == the token count T; the
+ * sequences are packed along t, sequence s owning tokens [cu_s, cu_s + len_s)
+ * for queries and keys alike, and a query sees only keys of its own sequence
+ * (positions restart at 0 in each sequence; q_offset and kv_offset must be 0).
+ * Lengths must be >= 0 and sum to T; the device reads them, so this is not
+ * checked before launch (a negative length counts as 0, the sum is clipped to
+ * T, and tokens past the sum are left unwritten).
+ *
+ * Ring fold (Ascend calcType): prev_out [B, Hq, Nq, dv] and prev_lse
+ * [B, Hq, Nq] are both NULL (first ring step) or both given; when given the
+ * result is folded into them:  L = logaddexp(prev_lse, lse_new),
+ * out = exp(prev_lse - L) * prev_out + exp(lse_new - L) * out_new, where a
+ * side whose LSE is -inf has weight 0.  out may alias prev_out and lse may
+ * alias prev_lse (same views); any other overlap is undefined.
+ *
+ * Outputs: out [B, Hq, Nq, dv] bf16 (round to nearest even); lse [B, Hq, Nq]
+ * float32 natural-log LSE, or NULL when no LSE is wanted.  A row with no
+ * visible key (and no prev) gets out = 0 and lse = -inf.
+ *
+ * Element types of the fold: MLA_OUT_F32 makes out a float32 view and
+ * MLA_PREV_OUT_F32 makes prev_out one (16-byte aligned, strides multiples of
+ * 4 elements).  The pages' prevOut is bf16; a float32 running output lets a
+ * caller fold many ring steps without rounding the carry to bf16 each time,
+ * rounding once in the last step.
+ *
+ * scale multiplies q.k (Ascend qkScale; TensorRT-LLM softmax_scale =
+ * 1/sqrt(qk_head_dim) for q_scaling = 1); it has no default here.
+ *
+ * Kernels exist for:
+ *   - shared latent:  Hkv == 1, v == NULL, dq + dr == 576, dv == 512
+ *     (dr == 0 or 64), no seq_lens;
+ *   - split:          v != NULL, q_rope and k_rope given, dq == 128, dr == 64,
+ *     dv == 128, Hq % Hkv == 0, with or without seq_lens.
+ * Other shapes return MLA_ERR_UNSUPPORTED.
+ */
+mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope,
+                   const mla_rows* kv, const mla_rows* k_rope, const mla_rows* v,
+                   int32_t B, int32_t Hq, int32_t Hkv, int64_t Nq, int64_t Nkv,
+                   int32_t dq, int32_t dr, int32_t dv,
+                   const int32_t* seq_lens, int32_t n_seqs,
+                   float scale, uint32_t flags, int64_t q_offset, int64_t kv_offset,
+                   const mla_rows* prev_out, const mla_rows* prev_lse,
+                   const mla_rows* out, const mla_rows* lse,
+                   void* stream /* hipStream_t */);
+
+/*
+ * mla_merge_lse -- fold two partial results over disjoint key sets
+ * (TensorRT-LLM mla.py, forward_context_with_chunked_prefill: partial outputs
+ * merged with their softmax stats; Ascend RingMLAOperation prevOut/prevLse).
+ *
+ *   L = logaddexp(lse_a, lse_b)
+ *   out = exp(lse_a - L) * out_a + exp(lse_b - L) * out_b
+ * with weight exactly 0 (and no multiply) for a side whose LSE is -inf; both
+ * -inf gives out = 0, lse = -inf.
+ *
+ * out_a, out_b, out: bf16 [B, H, N, dv]; lse_a, lse_b, lse: fp32 [B, H, N].
+ * dv must be a multiple of 8.  out may alias out_a or out_b and lse may alias
+ * lse_a or lse_b (each element is read before it is written by the same
+ * thread); other overlaps are undefined.
+ */
+mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a,
+                         const mla_rows* out_b, const mla_rows* lse_b,
+                         int32_t B, int32_t H, int64_t N, int32_t dv,
+                         const mla_rows* out, const mla_rows* lse,
+                         void* stream /* hipStream_t */);
+
+/*
+ * mla_sparse_fwd -- top-k sparse latent attention (NKI
+ * mla_sparse_attention_cte_kernel, "Parameters" and "Returns").
+ *
+ * q_lift [B, S, H, L] and q_pe [B, S, H, R] (views with t = query, h = head);
+ * c_kv [B, S_kv, L] and k_pe [B, S_kv, R] (views with t = cache row, stride_h
+ * unused); topk_idx: device int32 [B, S, K] contiguous.  Query i attends
+ * exactly the K listed cache rows (a multiset: repeats count; order is
+ * irrelevant; no extra mask) with score scale * (q_lift . c_kv + q_pe . k_pe)
+ * and value c_kv.  All H heads of a query share its index list.  An index
+ * outside [0, S_kv) is not attended (the pages leave it undefined; it is
+ * treated like a padding sentinel); a query with no valid index gets out = 0.
+ *
+ * out [B, S, H*L] bf16 as a view with t = query, h = head (stride_h = L for
+ * the page's row-major h*L + l order); lse [B, S, H] fp32 (view with t =
+ * query, h = head) or NULL.  L == 512, R == 64, 1 <= K.
+ */
+mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe,
+                          const mla_rows* c_kv, const mla_rows* k_pe,
+                          const int32_t* topk_idx,
+                          int32_t B, int64_t S, int64_t S_kv, int32_t H,
+                          int32_t L, int32_t R, int32_t K, float scale,
+                          const mla_rows* out, const mla_rows* lse,
+                          void* stream /* hipStream_t */);
+
+/*
+ * mla_debug_gather -- test export.  Gathers the top-k rows of one query's
+ * index list through the same device tile loader mla_sparse_fwd uses (with
+ * its LDS swizzle undone on the way out): rows_out [K, L + R] bf16 contiguous,
+ * row k = c_kv[b, idx[k]] concatenated with k_pe[b, idx[k]] (an out-of-range
+ * index yields a row of zeros).  Backs the bit-exact gather check.
+ */
+mla_status mla_debug_gather(const mla_rows* c_kv, const mla_rows* k_pe,
+                            const int32_t* idx, int32_t b, int64_t S_kv,
+                            int32_t L, int32_t R, int32_t K,
+                            uint16_t* rows_out, void* stream /* hipStream_t */);
+
+/* Thread-local description of the last non-OK status on this thread. */
+const char* mla_last_error(void);
+
+/* Library version string. */
+const char* mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA355_H */

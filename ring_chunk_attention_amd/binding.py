@@ -1,0 +1,348 @@
+"""ctypes binding of libmla355.so.
+
+Argument marshalling only: tensors are checked for dtype/device/layout, turned
+into ``mla_rows`` views (pointer + element strides) and handed to the C ABI on
+torch's current stream.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback.  If the library is missing or cannot be
+loaded, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla355.so")
+
+MLA_CAUSAL = 1
+MLA_OUT_F32 = 2
+MLA_PREV_OUT_F32 = 4
+
+
+class MlaRows(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+        ("stride_t", ctypes.c_int64),
+    ]
+
+
+_P = ctypes.POINTER(MlaRows)
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m ring_chunk_attention_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.mla_fwd.restype = ctypes.c_int
+    lib.mla_fwd.argtypes = [
+        _P, _P, _P, _P, _P,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_int32,
+        ctypes.c_float, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64,
+        _P, _P, _P, _P, ctypes.c_void_p]
+    lib.mla_merge_lse.restype = ctypes.c_int
+    lib.mla_merge_lse.argtypes = [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_int32, _P, _P, ctypes.c_void_p]
+    lib.mla_sparse_fwd.restype = ctypes.c_int
+    lib.mla_sparse_fwd.argtypes = [_P, _P, _P, _P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_float, _P, _P, ctypes.c_void_p]
+    lib.mla_debug_gather.restype = ctypes.c_int
+    lib.mla_debug_gather.argtypes = [_P, _P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_version.restype = ctypes.c_char_p
+    lib.mla_version.argtypes = []
+    return lib
+
+
+LIB = _load()
+LIB_PATH = _LIB_PATH
+
+EXPORTS = ("mla_fwd", "mla_merge_lse", "mla_sparse_fwd", "mla_debug_gather",
+           "mla_last_error", "mla_version")
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"mla355 status {status}: {message}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MlaError(status, LIB.mla_last_error().decode())
+
+
+def version() -> str:
+    return LIB.mla_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# views
+# ---------------------------------------------------------------------------
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+
+
+def _rows_bhtd(t: torch.Tensor, name: str, dtype: torch.dtype = torch.bfloat16) -> MlaRows:
+    """[B, H, T, D] (inner dim contiguous) -> view."""
+    _need(t, name, dtype)
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name}: expected [B, H, T, D] with a contiguous last dim")
+    return MlaRows(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _rows_thd(t: torch.Tensor, name: str) -> MlaRows:
+    """[T, H, D] (tokens outermost) -> view with b = 0."""
+    _need(t, name, torch.bfloat16)
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name}: expected [T, H, D] with a contiguous last dim")
+    return MlaRows(t.data_ptr(), 0, t.stride(1), t.stride(0))
+
+
+def _lse_bht(t: torch.Tensor, name: str) -> MlaRows:
+    _need(t, name, torch.float32)
+    if t.dim() != 3:
+        raise ValueError(f"{name}: expected [B, H, T]")
+    return MlaRows(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _lse_ht(t: torch.Tensor, name: str) -> MlaRows:
+    _need(t, name, torch.float32)
+    if t.dim() != 2:
+        raise ValueError(f"{name}: expected [H, T]")
+    return MlaRows(t.data_ptr(), 0, t.stride(0), t.stride(1))
+
+
+def _ref(r: Optional[MlaRows]):
+    return ctypes.byref(r) if r is not None else None
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 512,
+        causal: bool = True, q_offset: int = 0, kv_offset: int = 0,
+        q_rope: Optional[torch.Tensor] = None, k_rope: Optional[torch.Tensor] = None,
+        v: Optional[torch.Tensor] = None,
+        prev: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention over [B, H, N, D] tensors (mla_fwd).
+
+    q [B, Hq, Nq, dq], kv [B, Hkv, Nkv, dq]; optional q_rope/k_rope
+    [.., dr] and v [B, Hkv, Nkv, dv].  With v None the value is
+    kv[..., :head_dim_v].  ``prev = (prev_out, prev_lse)`` folds the result
+    into a previous one (out/lse may be the same tensors).  Returns
+    (out [B, Hq, Nq, dv] bf16, lse [B, Hq, Nq] fp32 or None).  ``out`` and
+    ``prev_out`` may be float32 tensors (a float32 running output for ring
+    folds); their dtype selects the flag.
+    """
+    B, Hq, Nq, dq = q.shape
+    _, Hkv, Nkv, _ = kv.shape
+    dr = 0 if q_rope is None else q_rope.shape[-1]
+    dv = head_dim_v if v is None else v.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, Nq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and (want_lse or prev is not None):
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out_f32 = out.dtype == torch.float32
+    prev_f32 = prev is not None and prev[0].dtype == torch.float32
+    vq, vkv = _rows_bhtd(q, "q"), _rows_bhtd(kv, "kv")
+    vout = _rows_bhtd(out, "out", torch.float32 if out_f32 else torch.bfloat16)
+    vqr = _rows_bhtd(q_rope, "q_rope") if q_rope is not None else None
+    vkr = _rows_bhtd(k_rope, "k_rope") if k_rope is not None else None
+    vv = _rows_bhtd(v, "v") if v is not None else None
+    vpo = (_rows_bhtd(prev[0], "prev_out", torch.float32 if prev_f32 else torch.bfloat16)
+           if prev is not None else None)
+    vpl = _lse_bht(prev[1], "prev_lse") if prev is not None else None
+    vl = _lse_bht(lse, "lse") if lse is not None else None
+    flags = ((MLA_CAUSAL if causal else 0) | (MLA_OUT_F32 if out_f32 else 0)
+             | (MLA_PREV_OUT_F32 if prev_f32 else 0))
+    _check(LIB.mla_fwd(ctypes.byref(vq), _ref(vqr), ctypes.byref(vkv), _ref(vkr), _ref(vv),
+                       B, Hq, Hkv, Nq, Nkv, dq, dr, dv, None, 0, float(scale), flags,
+                       q_offset, kv_offset,
+                       _ref(vpo), _ref(vpl), ctypes.byref(vout), _ref(vl), _stream(q.device)))
+    return out, lse
+
+
+def split_fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
+              v: torch.Tensor, *, scale: float, seq_lens: Optional[torch.Tensor] = None,
+              causal: bool = True, prev: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split query/key ring step over [T, H, D] tensors (mla_fwd, Ascend
+    RingMLAOperation layout): q1 [T, H, 128], q2 [T, H, 64], k1 [T, Hkv, 128],
+    k2 [T, Hkv, 64], v [T, Hkv, 128]; seq_lens int32 [batch] on the GPU;
+    prev = (prev_out [T, H, 128], prev_lse [H, T]).  Returns out [T, H, 128]
+    and lse [H, T]."""
+    T, H, dq = q1.shape
+    Hkv = k1.shape[1]
+    dr = q2.shape[2]
+    dv = v.shape[2]
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=q1.device)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q1.device)
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", torch.int32)
+        if seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens: expected a contiguous [batch] tensor")
+    views = [_rows_thd(q1, "q1"), _rows_thd(q2, "q2"), _rows_thd(k1, "k1"), _rows_thd(k2, "k2"),
+             _rows_thd(v, "v")]
+    vpo = _rows_thd(prev[0], "prev_out") if prev is not None else None
+    vpl = _lse_ht(prev[1], "prev_lse") if prev is not None else None
+    vout, vl = _rows_thd(out, "out"), _lse_ht(lse, "lse")
+    _check(LIB.mla_fwd(ctypes.byref(views[0]), ctypes.byref(views[1]), ctypes.byref(views[2]),
+                       ctypes.byref(views[3]), ctypes.byref(views[4]),
+                       1, H, Hkv, T, T, dq, dr, dv,
+                       seq_lens.data_ptr() if seq_lens is not None else None,
+                       seq_lens.numel() if seq_lens is not None else 0,
+                       float(scale), MLA_CAUSAL if causal else 0, 0, 0,
+                       _ref(vpo), _ref(vpl), ctypes.byref(vout), ctypes.byref(vl),
+                       _stream(q1.device)))
+    return out, lse
+
+
+def merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: torch.Tensor,
+          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """LSE merge of two [B, H, N, dv] partial results (mla_merge_lse)."""
+    B, H, N, dv = out_a.shape
+    if out is None:
+        out = torch.empty_like(out_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    va, vb, vo = _rows_bhtd(out_a, "out_a"), _rows_bhtd(out_b, "out_b"), _rows_bhtd(out, "out")
+    la, lb, lo = _lse_bht(lse_a, "lse_a"), _lse_bht(lse_b, "lse_b"), _lse_bht(lse, "lse")
+    _check(LIB.mla_merge_lse(ctypes.byref(va), ctypes.byref(la), ctypes.byref(vb), ctypes.byref(lb),
+                             B, H, N, dv, ctypes.byref(vo), ctypes.byref(lo), _stream(out_a.device)))
+    return out, lse
+
+
+def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
+               topk_idx: torch.Tensor, *, scale: float, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Top-k sparse latent attention (mla_sparse_fwd): q_lift [B,S,H,L],
+    q_pe [B,S,H,R], c_kv [B,S_kv,L], k_pe [B,S_kv,R], topk_idx int32
+    [B,S,K] -> out [B, S, H*L] bf16 and lse [B, S, H] fp32."""
+    B, S, H, L = q_lift.shape
+    R = q_pe.shape[3]
+    S_kv = c_kv.shape[1]
+    K = topk_idx.shape[2]
+    for t, n in ((q_lift, "q_lift"), (q_pe, "q_pe")):
+        _need(t, n, torch.bfloat16)
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{n}: expected [B, S, H, D] with a contiguous last dim")
+    for t, n in ((c_kv, "c_kv"), (k_pe, "k_pe")):
+        _need(t, n, torch.bfloat16)
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{n}: expected [B, S_kv, D] with a contiguous last dim")
+    _need(topk_idx, "topk_idx", torch.int32)
+    if not topk_idx.is_contiguous() or topk_idx.shape[:2] != (B, S):
+        raise ValueError("topk_idx: expected a contiguous [B, S, K] tensor")
+    if out is None:
+        out = torch.empty((B, S, H * L), dtype=torch.bfloat16, device=q_lift.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, S, H), dtype=torch.float32, device=q_lift.device)
+    _need(out, "out", torch.bfloat16)
+    if out.shape != (B, S, H * L) or out.stride(2) != 1:
+        raise ValueError("out: expected [B, S, H*L] with a contiguous last dim")
+    v_ql = MlaRows(q_lift.data_ptr(), q_lift.stride(0), q_lift.stride(2), q_lift.stride(1))
+    v_qp = MlaRows(q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(2), q_pe.stride(1))
+    v_ck = MlaRows(c_kv.data_ptr(), c_kv.stride(0), 0, c_kv.stride(1))
+    v_kp = MlaRows(k_pe.data_ptr(), k_pe.stride(0), 0, k_pe.stride(1))
+    v_o = MlaRows(out.data_ptr(), out.stride(0), L * out.stride(2), out.stride(1))
+    v_l = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+        v_l = MlaRows(lse.data_ptr(), lse.stride(0), lse.stride(2), lse.stride(1))
+    _check(LIB.mla_sparse_fwd(ctypes.byref(v_ql), ctypes.byref(v_qp), ctypes.byref(v_ck),
+                              ctypes.byref(v_kp), topk_idx.data_ptr(), B, S, S_kv, H, L, R, K,
+                              float(scale), ctypes.byref(v_o), _ref(v_l), _stream(q_lift.device)))
+    return out, lse
+
+
+def debug_gather(c_kv: torch.Tensor, k_pe: torch.Tensor, idx: torch.Tensor, b: int = 0) -> torch.Tensor:
+    """Rows idx[k] of [c_kv | k_pe] of batch b, gathered by the sparse
+    kernel's device tile loader (mla_debug_gather): [K, L + R] bf16."""
+    _need(c_kv, "c_kv", torch.bfloat16)
+    _need(k_pe, "k_pe", torch.bfloat16)
+    _need(idx, "idx", torch.int32)
+    if idx.dim() != 1 or not idx.is_contiguous():
+        raise ValueError("idx: expected a contiguous 1-D int32 tensor")
+    L, R = c_kv.shape[2], k_pe.shape[2]
+    K = idx.numel()
+    rows = torch.empty((K, L + R), dtype=torch.bfloat16, device=c_kv.device)
+    v_ck = MlaRows(c_kv.data_ptr(), c_kv.stride(0), 0, c_kv.stride(1))
+    v_kp = MlaRows(k_pe.data_ptr(), k_pe.stride(0), 0, k_pe.stride(1))
+    _check(LIB.mla_debug_gather(ctypes.byref(v_ck), ctypes.byref(v_kp), idx.data_ptr(), b,
+                                c_kv.shape[1], L, R, K, rows.data_ptr(), _stream(c_kv.device)))
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# one-device ring
+# ---------------------------------------------------------------------------
+def ring_order(r: int, n_chunks: int) -> Sequence[int]:
+    """KV chunks query chunk r visits: step s brings chunk (r - s) mod P; chunks
+    after r are wholly in the causal future and are skipped."""
+    return [(r - s) % n_chunks for s in range(n_chunks) if (r - s) % n_chunks <= r]
+
+
+def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
+             head_dim_v: int = 512, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None,
+             carry: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Causal shared-latent attention of q [B,H,N,dk] over kv [B,1,N,dk]
+    processed as a ring of ``n_chunks`` contiguous chunks on one device.
+
+    Query chunk r meets each KV chunk k <= r in ring order; every call passes
+    the global offsets (r*C, k*C), so the kernel applies the causal mask on
+    the diagonal chunk and none on earlier chunks, and every call after the
+    first folds its result into the running (out, lse) through the prev
+    arguments, in place (TensorRT-LLM mla.py forward_context_with_chunked_prefill;
+    Ascend RingMLAOperation calcType).  The running output between folds is
+    kept in float32 (``carry``, [B, H, C, dv], allocated if not given) and only
+    the last step of each query chunk writes bf16 ``out``."""
+    B, H, N, dk = q.shape
+    if N % n_chunks:
+        raise ValueError("sequence length must be a multiple of the chunk count")
+    C = N // n_chunks
+    if out is None:
+        out = torch.empty((B, H, N, head_dim_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if carry is None and n_chunks > 1:
+        carry = torch.empty((B, H, C, head_dim_v), dtype=torch.float32, device=q.device)
+    for r in range(n_chunks):
+        qs = slice(r * C, (r + 1) * C)
+        o_r, l_r = out[:, :, qs], lse[:, :, qs]
+        order = ring_order(r, n_chunks)
+        for step, k in enumerate(order):
+            last = step == len(order) - 1
+            fwd(q[:, :, qs], kv[:, :, k * C:(k + 1) * C], scale=scale, head_dim_v=head_dim_v,
+                causal=True, q_offset=r * C, kv_offset=k * C,
+                prev=None if step == 0 else (carry, l_r),
+                out=o_r if last else carry, lse=l_r)
+    return out, lse

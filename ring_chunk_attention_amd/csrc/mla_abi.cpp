@@ -1,0 +1,295 @@
+// C ABI of libmla355.so: argument validation, kernel selection and launch.
+// The contract is documented in include/mla355.h.
+#include "mla355.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "mla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mla_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLA_OK;
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A bf16 row view used by a kernel: data 16-byte aligned, b/h/t strides
+// multiples of 8 elements, non-negative.
+mla_status check_rows(const mla_rows* r, const char* name, bool need_h = true) {
+  if (!r || !r->data) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+  if (!aligned16(r->data)) return fail(MLA_ERR_INVALID_ARG, "%s: data pointer must be 16-byte aligned", name);
+  if (r->stride_b < 0 || r->stride_h < 0 || r->stride_t < 0)
+    return fail(MLA_ERR_INVALID_ARG, "%s: negative stride", name);
+  if (r->stride_b % 8 || (need_h && r->stride_h % 8) || r->stride_t % 8)
+    return fail(MLA_ERR_INVALID_ARG, "%s: strides must be multiples of 8 elements", name);
+  return MLA_OK;
+}
+
+// A float32 row view: data 16-byte aligned, b/h/t strides multiples of 4.
+mla_status check_rows_f32(const mla_rows* r, const char* name) {
+  if (!r || !r->data) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+  if (!aligned16(r->data)) return fail(MLA_ERR_INVALID_ARG, "%s: data pointer must be 16-byte aligned", name);
+  if (r->stride_b < 0 || r->stride_h < 0 || r->stride_t < 0)
+    return fail(MLA_ERR_INVALID_ARG, "%s: negative stride", name);
+  if (r->stride_b % 4 || r->stride_h % 4 || r->stride_t % 4)
+    return fail(MLA_ERR_INVALID_ARG, "%s: float32 strides must be multiples of 4 elements", name);
+  return MLA_OK;
+}
+
+mla_status check_lse(const mla_rows* r, const char* name) {
+  if (!r || !r->data) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+  if (reinterpret_cast<uintptr_t>(r->data) & 3u) return fail(MLA_ERR_INVALID_ARG, "%s: data pointer must be 4-byte aligned", name);
+  if (r->stride_b < 0 || r->stride_h < 0 || r->stride_t < 0)
+    return fail(MLA_ERR_INVALID_ARG, "%s: negative stride", name);
+  return MLA_OK;
+}
+
+mla::RowsC rc(const mla_rows* r) {
+  return mla::RowsC{static_cast<const uint16_t*>(r->data), r->stride_b, r->stride_h, r->stride_t};
+}
+mla::RowsM rm(const mla_rows* r) {
+  return mla::RowsM{static_cast<uint16_t*>(r->data), r->stride_b, r->stride_h, r->stride_t};
+}
+mla::LseC lc(const mla_rows* r) {
+  if (!r) return mla::LseC{nullptr, 0, 0, 0};
+  return mla::LseC{static_cast<const float*>(r->data), r->stride_b, r->stride_h, r->stride_t};
+}
+mla::LseM lm(const mla_rows* r) {
+  if (!r) return mla::LseM{nullptr, 0, 0, 0};
+  return mla::LseM{static_cast<float*>(r->data), r->stride_b, r->stride_h, r->stride_t};
+}
+
+bool same_view(const mla_rows* a, const mla_rows* b) {
+  return a->data == b->data && a->stride_b == b->stride_b && a->stride_h == b->stride_h &&
+         a->stride_t == b->stride_t;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+const char* mla_version(void) { return "mla355 0.1 gfx950"; }
+
+mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
+                   const mla_rows* k_rope, const mla_rows* v, int32_t B, int32_t Hq,
+                   int32_t Hkv, int64_t Nq, int64_t Nkv, int32_t dq, int32_t dr, int32_t dv,
+                   const int32_t* seq_lens, int32_t n_seqs, float scale, uint32_t flags,
+                   int64_t q_offset, int64_t kv_offset, const mla_rows* prev_out,
+                   const mla_rows* prev_lse, const mla_rows* out, const mla_rows* lse,
+                   void* stream) {
+  g_last_error.clear();
+  mla_status st;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nkv < 0)
+    return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, Hq > 0, Hkv > 0, Nq >= 0, Nkv >= 0");
+  if (Hq % Hkv) return fail(MLA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (dq <= 0 || dr < 0 || dv <= 0 || dq % 8 || dr % 8 || dv % 8)
+    return fail(MLA_ERR_INVALID_ARG, "head dims must be positive multiples of 8 (dq=%d dr=%d dv=%d)", dq, dr, dv);
+  if (flags & ~(MLA_CAUSAL | MLA_OUT_F32 | MLA_PREV_OUT_F32))
+    return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+  const bool out_f32 = flags & MLA_OUT_F32, prev_f32 = flags & MLA_PREV_OUT_F32;
+  if ((st = check_rows(q, "q")) || (st = check_rows(kv, "kv"))) return st;
+  if ((st = out_f32 ? check_rows_f32(out, "out") : check_rows(out, "out"))) return st;
+  if ((q_rope == nullptr) != (k_rope == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "q_rope and k_rope must both be given or both be NULL");
+  if ((q_rope == nullptr) != (dr == 0))
+    return fail(MLA_ERR_INVALID_ARG, "dr must be 0 exactly when q_rope/k_rope are NULL");
+  if (q_rope && ((st = check_rows(q_rope, "q_rope")) || (st = check_rows(k_rope, "k_rope")))) return st;
+  if (v && (st = check_rows(v, "v"))) return st;
+  if (!v && dv > dq)
+    return fail(MLA_ERR_INVALID_ARG, "head_dim_v (%d) must not exceed the kv width (%d) when V is the KV prefix", dv, dq);
+  if ((prev_out == nullptr) != (prev_lse == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "prev_out and prev_lse must both be given or both be NULL");
+  if (prev_f32 && !prev_out) return fail(MLA_ERR_INVALID_ARG, "MLA_PREV_OUT_F32 given without prev_out");
+  if (prev_out && ((st = prev_f32 ? check_rows_f32(prev_out, "prev_out") : check_rows(prev_out, "prev_out")) ||
+                   (st = check_lse(prev_lse, "prev_lse"))))
+    return st;
+  if (prev_out && out->data == prev_out->data && out_f32 != prev_f32)
+    return fail(MLA_ERR_INVALID_ARG, "out may alias prev_out only with the same element type");
+  if (lse && (st = check_lse(lse, "lse"))) return st;
+  if (prev_out && out->data == prev_out->data && !same_view(out, prev_out))
+    return fail(MLA_ERR_INVALID_ARG, "out may alias prev_out only as the identical view");
+  if (prev_lse && lse && lse->data == prev_lse->data && !same_view(lse, prev_lse))
+    return fail(MLA_ERR_INVALID_ARG, "lse may alias prev_lse only as the identical view");
+  if (seq_lens) {
+    if (B != 1) return fail(MLA_ERR_INVALID_ARG, "seq_lens requires B == 1 (tokens packed along t)");
+    if (n_seqs <= 0) return fail(MLA_ERR_INVALID_ARG, "seq_lens given with n_seqs <= 0");
+    if (Nq != Nkv) return fail(MLA_ERR_INVALID_ARG, "seq_lens requires Nq == Nkv (same lengths for query and key)");
+    if (q_offset || kv_offset) return fail(MLA_ERR_INVALID_ARG, "seq_lens requires q_offset == kv_offset == 0");
+    if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_INVALID_ARG, "seq_lens must be 4-byte aligned");
+  }
+
+  mla::AttnParams p{};
+  p.qa = rc(q);
+  p.qb = q_rope ? rc(q_rope) : rc(q);
+  p.ka = rc(kv);
+  p.kb = k_rope ? rc(k_rope) : rc(kv);
+  p.v = v ? rc(v) : mla::RowsC{nullptr, 0, 0, 0};
+  p.out = rm(out);
+  p.prev_out = prev_out ? rc(prev_out) : mla::RowsC{nullptr, 0, 0, 0};
+  p.lse = lm(lse);
+  p.prev_lse = lc(prev_lse);
+  p.seq_lens = seq_lens;
+  p.n_seqs = seq_lens ? n_seqs : 0;
+  p.da = dq;
+  p.B = B;
+  p.Hq = Hq;
+  p.group = Hq / Hkv;
+  p.Nq = Nq;
+  p.Nkv = Nkv;
+  p.q_offset = q_offset;
+  p.kv_offset = kv_offset;
+  p.scale_log2 = scale * kLog2e;
+  p.causal = (flags & MLA_CAUSAL) ? 1 : 0;
+  p.out_f32 = out_f32 ? 1 : 0;
+  p.prev_f32 = prev_f32 ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const bool latent = !v && Hkv == 1 && dq + dr == 576 && dv == 512 && (dr == 0 || dr == 64) && !seq_lens;
+  const bool split = v && q_rope && dq == 128 && dr == 64 && dv == 128;
+  if (latent) {
+    if (dr == 0) {
+      // one 576-column tensor: the kernel reads its last 64 columns as the RoPE part
+      p.qb.p = p.qa.p + (dq - 64);
+      p.kb.p = p.ka.p + (dq - 64);
+      p.da = dq - 64;
+    }
+    const int64_t n_qblk = (Nq + 31) / 32, n_hgrp = (Hq + 3) / 4;
+    if (n_qblk * n_hgrp * B > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+    p.n_qblk = (int32_t)n_qblk;
+    p.n_hgrp = (int32_t)n_hgrp;
+    if (Nq == 0 || B == 0) return MLA_OK;
+    return hip_status(mla::launch_latent_dense(p, s), "latent attention launch");
+  }
+  if (split) {
+    const int64_t qb = seq_lens ? (Nq + 127) / 128 + n_seqs : (Nq + 127) / 128 * B;
+    if (qb * Hq > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+    if (Nq == 0 || B == 0) return MLA_OK;
+    return hip_status(mla::launch_split(p, s), "split attention launch");
+  }
+  return fail(MLA_ERR_UNSUPPORTED,
+              "no kernel for Hq=%d Hkv=%d dq=%d dr=%d dv=%d v=%s seq_lens=%s (built: shared latent "
+              "Hkv=1 dq+dr=576 dv=512 v=NULL; split dq=128 dr=64 dv=128 with v)",
+              Hq, Hkv, dq, dr, dv, v ? "given" : "NULL", seq_lens ? "given" : "NULL");
+}
+
+mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a, const mla_rows* out_b,
+                         const mla_rows* lse_b, int32_t B, int32_t H, int64_t N, int32_t dv,
+                         const mla_rows* out, const mla_rows* lse, void* stream) {
+  g_last_error.clear();
+  mla_status st;
+  if (B < 0 || H <= 0 || N < 0 || dv <= 0 || dv % 8)
+    return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, H > 0, N >= 0, dv > 0 and a multiple of 8");
+  if ((st = check_rows(out_a, "out_a")) || (st = check_rows(out_b, "out_b")) || (st = check_rows(out, "out")))
+    return st;
+  if ((st = check_lse(lse_a, "lse_a")) || (st = check_lse(lse_b, "lse_b"))) return st;
+  if (lse && (st = check_lse(lse, "lse"))) return st;
+  if ((out->data == out_a->data && !same_view(out, out_a)) || (out->data == out_b->data && !same_view(out, out_b)))
+    return fail(MLA_ERR_INVALID_ARG, "out may alias out_a/out_b only as the identical view");
+  if (lse && ((lse->data == lse_a->data && !same_view(lse, lse_a)) || (lse->data == lse_b->data && !same_view(lse, lse_b))))
+    return fail(MLA_ERR_INVALID_ARG, "lse may alias lse_a/lse_b only as the identical view");
+  const int64_t rows = (int64_t)B * H * N;
+  if ((rows + 3) / 4 > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+  mla::MergeParams p{};
+  p.oa = rc(out_a);
+  p.ob = rc(out_b);
+  p.la = lc(lse_a);
+  p.lb = lc(lse_b);
+  p.out = rm(out);
+  p.lse = lm(lse);
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.dv = dv;
+  return hip_status(mla::launch_merge(p, static_cast<hipStream_t>(stream)), "merge launch");
+}
+
+mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const mla_rows* c_kv,
+                          const mla_rows* k_pe, const int32_t* topk_idx, int32_t B, int64_t S,
+                          int64_t S_kv, int32_t H, int32_t L, int32_t R, int32_t K, float scale,
+                          const mla_rows* out, const mla_rows* lse, void* stream) {
+  g_last_error.clear();
+  mla_status st;
+  if (B < 0 || S < 0 || S_kv <= 0 || H <= 0 || K <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, S >= 0, S_kv > 0, H > 0, K > 0");
+  if (L != 512 || R != 64) return fail(MLA_ERR_UNSUPPORTED, "sparse kernel is built for L = 512, R = 64 (got %d, %d)", L, R);
+  if (H > 128) return fail(MLA_ERR_UNSUPPORTED, "sparse kernel handles up to 128 heads per query (got %d)", H);
+  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+  if ((st = check_rows(q_lift, "q_lift")) || (st = check_rows(q_pe, "q_pe")) || (st = check_rows(out, "out")))
+    return st;
+  if ((st = check_rows(c_kv, "c_kv", false)) || (st = check_rows(k_pe, "k_pe", false))) return st;
+  if (!topk_idx || (reinterpret_cast<uintptr_t>(topk_idx) & 3u))
+    return fail(MLA_ERR_INVALID_ARG, "topk_idx: missing or not 4-byte aligned");
+  if (lse && (st = check_lse(lse, "lse"))) return st;
+  if ((int64_t)B * S > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (S_kv * c_kv->stride_t * 2 > kMaxGrid || S_kv * k_pe->stride_t * 2 > kMaxGrid)
+    return fail(MLA_ERR_UNSUPPORTED, "one batch of the cache must span less than 2 GiB (row offsets are 32-bit)");
+  mla::AttnParams p{};
+  p.qa = rc(q_lift);
+  p.qb = rc(q_pe);
+  p.ka = rc(c_kv);
+  p.kb = rc(k_pe);
+  p.out = rm(out);
+  p.lse = lm(lse);
+  p.idx = topk_idx;
+  p.da = L;
+  p.B = B;
+  p.Hq = H;
+  p.group = H;
+  p.Nq = S;
+  p.Nkv = S_kv;
+  p.topk = K;
+  p.scale_log2 = scale * kLog2e;
+  if (S == 0 || B == 0) return MLA_OK;
+  return hip_status(mla::launch_latent_sparse(p, static_cast<hipStream_t>(stream)), "sparse attention launch");
+}
+
+mla_status mla_debug_gather(const mla_rows* c_kv, const mla_rows* k_pe, const int32_t* idx, int32_t b,
+                            int64_t S_kv, int32_t L, int32_t R, int32_t K, uint16_t* rows_out,
+                            void* stream) {
+  g_last_error.clear();
+  mla_status st;
+  if (L != 512 || R != 64) return fail(MLA_ERR_UNSUPPORTED, "gather is built for L = 512, R = 64");
+  if (b < 0 || S_kv <= 0 || K < 0) return fail(MLA_ERR_INVALID_ARG, "sizes: need b >= 0, S_kv > 0, K >= 0");
+  if ((st = check_rows(c_kv, "c_kv", false)) || (st = check_rows(k_pe, "k_pe", false))) return st;
+  if (!idx || (reinterpret_cast<uintptr_t>(idx) & 3u)) return fail(MLA_ERR_INVALID_ARG, "idx: missing or misaligned");
+  if (!rows_out || !aligned16(rows_out)) return fail(MLA_ERR_INVALID_ARG, "rows_out: missing or not 16-byte aligned");
+  if (S_kv * c_kv->stride_t * 2 > kMaxGrid || S_kv * k_pe->stride_t * 2 > kMaxGrid)
+    return fail(MLA_ERR_UNSUPPORTED, "one batch of the cache must span less than 2 GiB (row offsets are 32-bit)");
+  mla::GatherParams p{};
+  p.ka = rc(c_kv);
+  p.kb = rc(k_pe);
+  p.idx = idx;
+  p.b = b;
+  p.Nkv = S_kv;
+  p.K = K;
+  p.rows_out = rows_out;
+  return hip_status(mla::launch_debug_gather(p, static_cast<hipStream_t>(stream)), "gather launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal interface between the C-ABI layer and the HIP kernels of
+// libmla355.so.  Not installed; the public contract is include/mla355.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// A row view: element (b, h, t, d) at p[b*sb + h*sh + t*st + d] (strides in
+// elements; bf16 unless a flag says float32, in which case the pointer is
+// reinterpreted).
+struct RowsC {
+  const uint16_t* p;
+  int64_t sb, sh, st;
+};
+struct RowsM {
+  uint16_t* p;
+  int64_t sb, sh, st;
+};
+// A float32 per-row view (LSE): element (b, h, t) at p[b*sb + h*sh + t*st].
+struct LseC {
+  const float* p;
+  int64_t sb, sh, st;
+};
+struct LseM {
+  float* p;
+  int64_t sb, sh, st;
+};
+
+// Parameters of one attention launch.  The key (and query) vector of a row is
+// the concatenation of part A (da columns) and part B (the rest).
+struct AttnParams {
+  RowsC qa, qb;             // query parts
+  RowsC ka, kb;             // key parts (sparse: c_kv, k_pe)
+  RowsC v;                  // explicit value rows (split form only)
+  RowsM out;
+  RowsC prev_out;           // p == nullptr: no fold
+  LseM lse;                 // p == nullptr: not written
+  LseC prev_lse;
+  const int32_t* idx;       // sparse: [B, S, K] contiguous
+  const int32_t* seq_lens;  // split varlen: [n_seqs] or nullptr
+  int32_t n_seqs;
+  int32_t da;               // columns in part A
+  int32_t B, Hq, group;     // group = Hq / Hkv
+  int64_t Nq, Nkv;          // sparse: Nq = S, Nkv = S_kv
+  int32_t topk;
+  int64_t q_offset, kv_offset;
+  float scale_log2;         // scale * log2(e)
+  int32_t causal;
+  int32_t out_f32;          // out holds float32 (else bf16)
+  int32_t prev_f32;         // prev_out holds float32 (else bf16)
+  int32_t n_qblk, n_hgrp;   // grid factors (see each launcher)
+};
+
+struct MergeParams {
+  RowsC oa, ob;
+  LseC la, lb;
+  RowsM out;
+  LseM lse;
+  int32_t B, H;
+  int64_t N;
+  int32_t dv;
+};
+
+struct GatherParams {
+  RowsC ka, kb;
+  const int32_t* idx;
+  int32_t b;
+  int64_t Nkv;
+  int32_t K;
+  uint16_t* rows_out;
+};
+
+hipError_t launch_latent_dense(const AttnParams& p, hipStream_t s);
+hipError_t launch_latent_sparse(const AttnParams& p, hipStream_t s);
+hipError_t launch_split(const AttnParams& p, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_debug_gather(const GatherParams& p, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,133 @@
+"""The C ABI: every function include/mla355.h declares is exported by
+libmla355.so, and invalid arguments are rejected before anything is launched
+(these checks run on the host, so they need no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla355.h")
+LIB = os.path.join(ROOT, "ring_chunk_attention_amd", "libmla355.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("mla_fwd", "mla_merge_lse", "mla_sparse_fwd", "mla_debug_gather",
+                 "mla_last_error", "mla_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "build the library first: python -m ring_chunk_attention_amd.build"
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(mla_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_binding_exports_list_matches_header():
+    from ring_chunk_attention_amd import EXPORTS
+    assert sorted(EXPORTS) == declared_functions()
+
+
+# ---------------------------------------------------------------------------
+# validation (host only: these calls fail before touching the GPU)
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def lib():
+    from ring_chunk_attention_amd.binding import LIB as L
+    return L
+
+
+class Rows(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64)]
+
+
+FAKE = 0x10000000  # an aligned address that is never dereferenced: validation fails first
+
+
+def rows(data=FAKE, sb=128 * 8192 * 576, sh=8192 * 576, st=576):
+    return Rows(data, sb, sh, st)
+
+
+def call_fwd(lib, q=None, kv=None, out=None, lse=None, v=None, q_rope=None, k_rope=None,
+             B=1, Hq=128, Hkv=1, Nq=8192, Nkv=8192, dq=576, dr=0, dv=512, seq_lens=None, n_seqs=0,
+             scale=0.072, flags=1, q_off=0, kv_off=0, prev_out=None, prev_lse=None):
+    from ring_chunk_attention_amd.binding import MlaRows
+    def conv(r):
+        return None if r is None else ctypes.byref(MlaRows(r.data, r.stride_b, r.stride_h, r.stride_t))
+    q = rows() if q is None else q
+    kv = rows() if kv is None else kv
+    out = rows(st=512) if out is None else out
+    return lib.mla_fwd(conv(q), conv(q_rope), conv(kv), conv(k_rope), conv(v), B, Hq, Hkv, Nq, Nkv,
+                       dq, dr, dv, seq_lens, n_seqs, scale, flags, q_off, kv_off,
+                       conv(prev_out), conv(prev_lse), conv(out), conv(lse), None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(Hq=6, Hkv=4), MLA_ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(Hq=0), MLA_ERR_INVALID_ARG, "sizes"),
+    (dict(dv=500), MLA_ERR_INVALID_ARG, "multiples of 8"),
+    (dict(flags=8), MLA_ERR_INVALID_ARG, "flag"),
+    (dict(flags=5), MLA_ERR_INVALID_ARG, "without prev_out"),
+    (dict(scale=float("nan")), MLA_ERR_INVALID_ARG, "scale"),
+    (dict(q=Rows(FAKE + 2, 0, 576, 576)), MLA_ERR_INVALID_ARG, "aligned"),
+    (dict(kv=Rows(FAKE, 0, 576, 577)), MLA_ERR_INVALID_ARG, "multiples of 8"),
+    (dict(q_rope=Rows(FAKE, 0, 64, 64), dr=64, dq=512), MLA_ERR_INVALID_ARG, "both"),
+    (dict(prev_out=Rows(FAKE, 0, 512, 512)), MLA_ERR_INVALID_ARG, "prev_out and prev_lse"),
+    (dict(dv=640, dq=576), MLA_ERR_INVALID_ARG, "head_dim_v"),
+    (dict(Hkv=2, Hq=128), MLA_ERR_UNSUPPORTED, "no kernel"),
+    (dict(dq=256, dv=256), MLA_ERR_UNSUPPORTED, "no kernel"),
+    (dict(seq_lens=FAKE, n_seqs=2, B=2), MLA_ERR_INVALID_ARG, "B == 1"),
+    (dict(seq_lens=FAKE, n_seqs=2, Nkv=100), MLA_ERR_INVALID_ARG, "Nq == Nkv"),
+])
+def test_fwd_rejects_invalid_arguments(lib, kw, code, msg):
+    st = call_fwd(lib, **kw)
+    assert st == code
+    assert msg in lib.mla_last_error().decode()
+
+
+def test_fwd_rejects_partial_alias(lib):
+    o = Rows(FAKE, 0, 512, 512)
+    o2 = Rows(FAKE, 0, 512, 1024)
+    l = Rows(FAKE + 4096, 0, 8192, 1)
+    st = call_fwd(lib, out=o, prev_out=o2, prev_lse=l, lse=l)
+    assert st == MLA_ERR_INVALID_ARG and "alias" in lib.mla_last_error().decode()
+
+
+def test_merge_rejects_bad_dv(lib):
+    from ring_chunk_attention_amd.binding import MlaRows
+    r = MlaRows(FAKE, 0, 512, 512)
+    st = lib.mla_merge_lse(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r),
+                           1, 4, 16, 12, ctypes.byref(r), ctypes.byref(r), None)
+    assert st == MLA_ERR_INVALID_ARG
+
+
+def test_sparse_rejects_unsupported_dims(lib):
+    from ring_chunk_attention_amd.binding import MlaRows
+    r = MlaRows(FAKE, 0, 512, 512)
+    st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
+                            1, 16, 1024, 128, 256, 64, 128, 0.07, ctypes.byref(r), None, None)
+    assert st == MLA_ERR_UNSUPPORTED
+    st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
+                            1, 16, 1024, 256, 512, 64, 128, 0.07, ctypes.byref(r), None, None)
+    assert st == MLA_ERR_UNSUPPORTED
+
+
+def test_binding_raises_with_message(lib):
+    from ring_chunk_attention_amd.binding import MlaError, _check
+    call_fwd(lib, Hq=6, Hkv=4)
+    with pytest.raises(MlaError, match="multiple of Hkv"):
+        _check(MLA_ERR_INVALID_ARG)

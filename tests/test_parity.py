@@ -1,0 +1,336 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every case draws seeded inputs from ``workloads``, runs them through
+``ring_chunk_attention_amd`` on the GPU and compares element by element with
+the oracle: bf16 outputs to 1e-2 and fp32 LSE to 1e-3 max-abs; gathers and
+the repeated-row case bit-exact.  Small cases compare every element; the
+full-size workloads (the launch configurations the benchmark times) compare
+sampled rows that the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import LSE_TOL, O_TOL, dev, dev_bf16, host, report
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def mla():
+    import ring_chunk_attention_amd as m
+    return m
+
+
+# ---------------------------------------------------------------------------
+# shared-latent dense
+# ---------------------------------------------------------------------------
+def _dense_gpu(mla, c, **kw):
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    out, lse = mla.fwd(q, kv, scale=c.scale, head_dim_v=c.head_dim_v, causal=c.causal,
+                       q_offset=c.q_offset, kv_offset=c.kv_offset, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_tiny_config_full(mla):
+    """B=1, 4 heads, N=128, dk=576/dv=512, seed 0: every element."""
+    c = W.tiny(0)
+    out, lse = _dense_gpu(mla, c)
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
+    assert report("tiny O", host(out), o_ref) <= O_TOL
+    assert report("tiny LSE", host(lse), l_ref) <= LSE_TOL
+
+
+@pytest.mark.parametrize("B,H,N,Nkv,q_off,kv_off,causal,seed", [
+    (2, 6, 200, 200, 0, 0, True, 1),       # ragged rows and heads, two batches
+    (1, 5, 77, 150, 73, 0, True, 2),       # queries at the end of a longer key range
+    (1, 4, 64, 96, 0, 40, True, 3),        # keys start later: first rows see nothing
+    (1, 3, 45, 70, 0, 0, False, 4),        # no mask, ragged key tail
+    (1, 8, 1, 300, 299, 0, True, 5),       # a single query row (decode-like)
+])
+def test_dense_ragged(mla, B, H, N, Nkv, q_off, kv_off, causal, seed):
+    c = W.dense_case(B=B, H=H, N=N, Nkv=Nkv, seed=seed, causal=causal, q_offset=q_off,
+                     kv_offset=kv_off)
+    out, lse = _dense_gpu(mla, c)
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, causal=causal, q_offset=q_off,
+                                    kv_offset=kv_off)
+    assert report("O", host(out), o_ref) <= O_TOL
+    assert report("LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_dense_rope_split_equals_single_tensor(mla):
+    """Passing the 64 RoPE columns as separate q_rope/k_rope tensors reads the
+    same values: bitwise equal to the single 576-column call."""
+    c = W.dense_case(B=1, H=4, N=100, seed=6)
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    a, la = mla.fwd(q, kv, scale=c.scale)
+    qa, qr = q[..., :512].contiguous(), q[..., 512:].contiguous()
+    ka, kr = kv[..., :512].contiguous(), kv[..., 512:].contiguous()
+    b, lb = mla.fwd(qa, ka, q_rope=qr, k_rope=kr, scale=c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_dense_fold_prev(mla):
+    """prev_out/prev_lse folded in the epilogue equals the oracle merge of the
+    previous pair with the fresh result; rows with prev_lse = -inf keep the
+    fresh result, rows without visible keys keep prev exactly."""
+    c = W.dense_case(B=1, H=4, N=96, Nkv=96, seed=7, q_offset=0, kv_offset=32)
+    rng = np.random.default_rng(70)
+    prev_o = W.normal_bf16(rng, (1, 4, 96, 512))
+    prev_l = rng.uniform(0, 8, (1, 4, 96)).astype(np.float32)
+    prev_l[:, :, 5] = -np.inf
+    out, lse = _dense_gpu(mla, c, prev=(dev_bf16(prev_o), dev(prev_l)))
+    fresh = oracle.dense_mla(c.q, c.kv, 512, c.scale, q_offset=0, kv_offset=32)
+    o_ref, l_ref = oracle.merge(prev_o, prev_l, fresh[0], fresh[1])
+    assert report("fold O", host(out), o_ref) <= O_TOL
+    assert report("fold LSE", host(lse), l_ref) <= LSE_TOL
+    # rows 0..31 see no key (kv starts at 32): the previous values are kept bit
+    # for bit, except row 5 whose previous LSE is -inf too, which gives (0, -inf)
+    keep = [i for i in range(32) if i != 5]
+    got = out[:, :, keep].view(torch.int16).cpu().numpy()
+    assert np.array_equal(got, prev_o[:, :, keep].view(np.int16))
+    assert torch.all(out[:, :, 5] == 0) and torch.all(torch.isneginf(lse[:, :, 5]))
+
+
+def test_dense_fold_in_place(mla):
+    c = W.dense_case(B=1, H=4, N=64, seed=8)
+    rng = np.random.default_rng(80)
+    prev_o = W.normal_bf16(rng, (1, 4, 64, 512))
+    prev_l = rng.uniform(0, 8, (1, 4, 64)).astype(np.float32)
+    o_t, l_t = dev_bf16(prev_o), dev(prev_l)
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    mla.fwd(q, kv, scale=c.scale, prev=(o_t, l_t), out=o_t, lse=l_t)
+    torch.cuda.synchronize()
+    fresh = oracle.dense_mla(c.q, c.kv, 512, c.scale)
+    o_ref, l_ref = oracle.merge(prev_o, prev_l, fresh[0], fresh[1])
+    assert report("in-place O", host(o_t), o_ref) <= O_TOL
+    assert report("in-place LSE", host(l_t), l_ref) <= LSE_TOL
+
+
+def test_dense_fp32_out_and_prev(mla):
+    """float32 out and prev_out (the ring carry): the output skips the final
+    bf16 rounding, so this bounds the kernel's own arithmetic error."""
+    c = W.dense_case(B=1, H=8, N=160, seed=10)
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    out = torch.empty((1, 8, 160, 512), dtype=torch.float32, device="cuda")
+    _, lse = mla.fwd(q, kv, scale=c.scale, out=out)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
+    err = report("fp32 out O", host(out), o_ref)
+    assert err <= O_TOL
+    assert report("fp32 out LSE", host(lse), l_ref) <= LSE_TOL
+    # fold into a float32 previous result, writing bf16
+    rng = np.random.default_rng(100)
+    prev_o = rng.standard_normal((1, 8, 160, 512)).astype(np.float32)
+    prev_l = rng.uniform(0, 8, (1, 8, 160)).astype(np.float32)
+    o2, l2 = mla.fwd(q, kv, scale=c.scale, prev=(dev(prev_o), dev(prev_l)))
+    torch.cuda.synchronize()
+    m_o, m_l = oracle.merge(prev_o, prev_l, o_ref, l_ref)
+    assert report("fp32 prev O", host(o2), m_o) <= O_TOL
+    assert report("fp32 prev LSE", host(l2), m_l) <= LSE_TOL
+
+
+def test_dense_deterministic(mla):
+    c = W.dense_case(B=1, H=8, N=256, seed=9)
+    a = _dense_gpu(mla, c)
+    b = _dense_gpu(mla, c)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_dsv3_full_size_sampled(mla):
+    """128 heads x 8192 causal rows (the benchmark's launch): sampled rows of
+    four heads against the oracle, plus whole-output sanity."""
+    c = W.dsv3_prefill(0)
+    out, lse = _dense_gpu(mla, c)
+    heads = [0, 37, 90, 127]
+    rows = np.unique(np.concatenate([[0, 1, 2, 31, 32, 33, 127, 128, 4095, 4096, 8190, 8191],
+                                     np.random.default_rng(1).integers(0, 8192, 52)]))
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, rows=rows, heads=heads)
+    o_got = host(out[:, heads][:, :, rows])
+    l_got = host(lse[:, heads][:, :, rows])
+    assert report("dsv3 O", o_got, o_ref) <= O_TOL
+    assert report("dsv3 LSE", l_got, l_ref) <= LSE_TOL
+    assert not torch.isnan(out).any() and torch.isfinite(lse).all()
+
+
+# ---------------------------------------------------------------------------
+# merge and one-device ring
+# ---------------------------------------------------------------------------
+def test_merge_kernel(mla):
+    rng = np.random.default_rng(20)
+    oa = W.normal_bf16(rng, (2, 3, 50, 512))
+    ob = W.normal_bf16(rng, (2, 3, 50, 512))
+    la = rng.uniform(-5, 5, (2, 3, 50)).astype(np.float32)
+    lb = rng.uniform(-5, 5, (2, 3, 50)).astype(np.float32)
+    la[0, 0, :3] = -np.inf
+    lb[0, 0, 2:5] = -np.inf
+    out, lse = mla.merge(dev_bf16(oa), dev(la), dev_bf16(ob), dev(lb))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.merge(oa, la, ob, lb)
+    assert report("merge O", host(out), o_ref) <= O_TOL
+    assert report("merge LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_merge_in_place_dv128(mla):
+    rng = np.random.default_rng(21)
+    oa = W.normal_bf16(rng, (1, 4, 33, 128))
+    ob = W.normal_bf16(rng, (1, 4, 33, 128))
+    la = rng.uniform(-5, 5, (1, 4, 33)).astype(np.float32)
+    lb = rng.uniform(-5, 5, (1, 4, 33)).astype(np.float32)
+    ta, tl = dev_bf16(oa), dev(la)
+    mla.merge(ta, tl, dev_bf16(ob), dev(lb), out=ta, lse=tl)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.merge(oa, la, ob, lb)
+    assert report("merge in place O", host(ta), o_ref) <= O_TOL
+    assert report("merge in place LSE", host(tl), l_ref) <= LSE_TOL
+
+
+@pytest.mark.parametrize("H,N,P", [(4, 256, 4), (3, 192, 3), (2, 96, 1)])
+def test_ring_small_equals_unchunked_oracle(mla, H, N, P):
+    c = W.dense_case(B=1, H=H, N=N, seed=30 + P)
+    out, lse = mla.ring_fwd(dev_bf16(c.q), dev_bf16(c.kv), P, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
+    assert report("ring O", host(out), o_ref) <= O_TOL
+    assert report("ring LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_ring4_config_sampled(mla):
+    """16 heads, N = 4096 in 4 chunks of 1024 in ring order: sampled rows of
+    four heads against the unchunked oracle."""
+    c = W.ring4(0)
+    out, lse = mla.ring_fwd(dev_bf16(c.q), dev_bf16(c.kv), 4, scale=c.scale)
+    torch.cuda.synchronize()
+    heads = [0, 5, 10, 15]
+    rows = np.array([0, 1, 511, 1023, 1024, 1025, 2047, 2048, 3071, 3072, 3073, 4094, 4095])
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, rows=rows, heads=heads)
+    assert report("ring4 O", host(out[:, heads][:, :, rows]), o_ref) <= O_TOL
+    assert report("ring4 LSE", host(lse[:, heads][:, :, rows]), l_ref) <= LSE_TOL
+
+
+# ---------------------------------------------------------------------------
+# split q/k varlen ring step
+# ---------------------------------------------------------------------------
+def _split_gpu(mla, c, with_prev=True):
+    args = [dev_bf16(x) for x in (c.q1, c.q2, c.k1, c.k2, c.v)]
+    prev = (dev_bf16(c.prev_out), dev(c.prev_lse)) if (with_prev and c.prev_out is not None) else None
+    out, lse = mla.split_fwd(*args, scale=c.scale, seq_lens=dev(c.seq_lens), prev=prev)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("lens,H,Hkv,with_prev", [
+    ([5, 130, 1, 257, 64], 4, 2, True),
+    ([300, 200], 2, 2, False),
+    ([129], 3, 1, True),
+])
+def test_split_small(mla, lens, H, Hkv, with_prev):
+    c = W.split_case(seq_lens=lens, H=H, Hkv=Hkv, seed=sum(lens), with_prev=with_prev)
+    out, lse = _split_gpu(mla, c, with_prev)
+    o_ref, l_ref = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale,
+                                    prev_out=c.prev_out if with_prev else None,
+                                    prev_lse=c.prev_lse if with_prev else None)
+    assert report("split O", host(out), o_ref) <= O_TOL
+    assert report("split LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_split_config_sampled(mla):
+    """8 sequences (seed-0 lengths, T = 27610), 32 heads, prev fold: sampled
+    tokens of each sequence for four heads against the oracle."""
+    c = W.split_ring_step(0)
+    out, lse = _split_gpu(mla, c)
+    cu = np.concatenate([[0], np.cumsum(c.seq_lens)])
+    f = W.bf16_bits_to_f64
+    worst_o = worst_l = 0.0
+    for s in range(len(c.seq_lens)):
+        t0, L = int(cu[s]), int(c.seq_lens[s])
+        rows = np.unique(np.array([0, 1, 127, 128, L // 2, L - 2, L - 1]).clip(0, L - 1))
+        for h in (0, 9, 22, 31):
+            q = np.concatenate([f(c.q1[t0 + rows, h]), f(c.q2[t0 + rows, h])], 1)
+            k = np.concatenate([f(c.k1[t0:t0 + L, h]), f(c.k2[t0:t0 + L, h])], 1)
+            o, l = oracle.attention(q, k, f(c.v[t0:t0 + L, h]), c.scale, True, rows, np.arange(L))
+            o, l = oracle.merge(c.prev_out[t0 + rows, h], c.prev_lse[h, t0 + rows], o, l)
+            worst_o = max(worst_o, report(f"split s{s} h{h} O", host(out[t0 + rows, h]), o))
+            worst_l = max(worst_l, report(f"split s{s} h{h} LSE", host(lse[h, t0 + rows]), l))
+    assert worst_o <= O_TOL and worst_l <= LSE_TOL
+
+
+# ---------------------------------------------------------------------------
+# sparse top-k
+# ---------------------------------------------------------------------------
+def _sparse_gpu(mla, c, idx=None):
+    idx = c.idx if idx is None else idx
+    out, lse = mla.sparse_fwd(dev_bf16(c.q_lift), dev_bf16(c.q_pe), dev_bf16(c.c_kv),
+                              dev_bf16(c.k_pe), dev(idx), scale=c.scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("H,K,seed", [(128, 96, 40), (20, 2048, 41), (128, 40, 42)])
+def test_sparse_small(mla, H, K, seed):
+    c = W.sparse_case(S=24, S_kv=3000, pos0=2900, H=H, K=K, seed=seed)
+    out, lse = _sparse_gpu(mla, c)
+    o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale)
+    assert report("sparse O", host(out), o_ref) <= O_TOL
+    assert report("sparse LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_sparse_duplicates_and_invalid_indices(mla):
+    c = W.sparse_case(S=8, S_kv=500, pos0=300, H=128, K=64, seed=43)
+    idx = c.idx.copy()
+    idx[0, 0, 10:20] = idx[0, 0, 3]          # repeats count with multiplicity
+    idx[0, 1, 5] = -1                        # skipped
+    idx[0, 2, 7] = 500                       # past the cache: skipped
+    idx[0, 3, :] = -1                        # nothing valid: O = 0, LSE = -inf
+    out, lse = _sparse_gpu(mla, c, idx)
+    o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, idx, c.scale)
+    assert report("sparse dup O", host(out), o_ref) <= O_TOL
+    assert report("sparse dup LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_sparse_repeated_row_bit_exact(mla):
+    """K copies of one row: every weight is 1, so out = c_kv[r] exactly and
+    LSE = s_r + ln K."""
+    c = W.sparse_case(S=6, S_kv=400, pos0=300, H=128, K=256, seed=44)
+    r = 123
+    idx = np.full_like(c.idx, r)
+    out, lse = _sparse_gpu(mla, c, idx)
+    got = out.view(torch.int16).cpu().numpy().reshape(6, 128, 512)
+    want = np.broadcast_to(c.c_kv[0, r].view(np.int16), (6, 128, 512))
+    assert np.array_equal(got, want)
+    _, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, idx, c.scale)
+    assert report("repeated LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_debug_gather_bit_exact(mla):
+    c = W.sparse_case(S=2, S_kv=1000, pos0=900, H=4, K=200, seed=45)
+    ck, kp = dev_bf16(c.c_kv), dev_bf16(c.k_pe)
+    idx = c.idx[0, 1].copy()
+    idx[7] = -3
+    idx[8] = 1000
+    rows = mla.debug_gather(ck, kp, dev(idx))
+    torch.cuda.synchronize()
+    cat = torch.cat([ck[0], kp[0]], dim=1)
+    safe = torch.from_numpy(np.where((idx >= 0) & (idx < 1000), idx, 0).astype(np.int64)).cuda()
+    want = cat.index_select(0, safe)
+    want[7] = 0
+    want[8] = 0
+    assert torch.equal(rows.view(torch.int16), want.view(torch.int16))
+
+
+def test_sparse_config_sampled(mla):
+    """S = 4096 queries at positions 12288.., 16384 cache rows, 128 heads,
+    K = 2048: sampled queries (all heads) against the oracle."""
+    c = W.sparse_topk(0)
+    out, lse = _sparse_gpu(mla, c)
+    rows = [0, 1, 1000, 2047, 4094, 4095]
+    o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale, rows=rows)
+    assert report("sparse cfg O", host(out[:, rows]), o_ref) <= O_TOL
+    assert report("sparse cfg LSE", host(lse[:, rows]), l_ref) <= LSE_TOL
