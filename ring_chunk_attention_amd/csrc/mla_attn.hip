@@ -87,17 +87,28 @@ struct SplitCfg {
 __device__ __forceinline__ int swz_f(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 __device__ __forceinline__ int swz(int c, int r) { return c ^ swz_f(r); }
 
-template <class C>
+constexpr int NBUF = 3;          // key-tile buffers in flight
+constexpr int KMAX_IDX = 4096;   // sparse: longest index list staged in LDS
+
+// Sub-tile layout.  A sub-tile with NG 64-column groups per row is stored as
+// blocks of 8 rows x 8 chunks (16 bytes each) = 1 KB: block (r/8, g) at byte
+// ((r/8)*NG + g)*1024, row r%8 at +128*(r%8), and logical chunk q of group g
+// at position (q%8) ^ f(r%8).  One wave instruction of a global->LDS copy
+// fills one block, so every lane's source offset is the same for all groups
+// and tiles, and the instruction offset selects the group.
+__device__ __forceinline__ int tile_off(int NG, int r, int q) {
+  return (((r >> 3) * NG + (q >> 3)) << 10) + ((r & 7) << 7) + (((q & 7) ^ swz_f(r & 7)) << 4);
+}
+
+template <class C, bool SP>
 struct Smem {
-  static constexpr int AROWB = C::DA * 2;          // bytes per row, first part
-  static constexpr int BROWB = DB * 2;             // bytes per row, RoPE part
-  static constexpr int VROWB = C::DV * 2;
-  static constexpr int ATILE = BN * AROWB, BTILE = BN * BROWB;
-  static constexpr int VTILE = C::VLAT ? 16 : BN * VROWB;
-  alignas(16) unsigned char a[2][ATILE];
-  alignas(16) unsigned char b[2][BTILE];
-  alignas(16) unsigned char v[2][VTILE];
-  alignas(16) unsigned char p[WAVES][2][64 * 16];  // P^T fragments per wave, per 16-key half
+  static constexpr int ATILE = BN * C::DA * 2, BTILE = BN * DB * 2;
+  static constexpr int VTILE = C::VLAT ? 16 : BN * C::DV * 2;
+  alignas(16) unsigned char a[NBUF][ATILE];
+  alignas(16) unsigned char b[NBUF][BTILE];
+  alignas(16) unsigned char v[NBUF][VTILE];
+  alignas(16) unsigned char p[2][WAVES][2][64 * 16];  // P^T fragments: buffer, wave, 16-key half
+  alignas(16) int idx[SP ? KMAX_IDX : 4];            // sparse: the query's index list
   alignas(16) float wprev[ROWS];
   alignas(16) float wcur[ROWS];
   int redo;
@@ -121,55 +132,58 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcFlags);
 }
 
-// One wave-wide 16-byte-per-lane copy into LDS: lane l's 16 bytes at
-// rsrc + voffset + soffset land at lds_base + 16*l.
-__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base, uint32_t voffset,
-                                            uint32_t soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, (int)voffset, (int)soffset, 0, 0);
+// One wave-wide copy into LDS: lane l's 16 bytes at rsrc + voffset + IMM land
+// at lds_base + 16*l.  The instruction's immediate offset is added to the LDS
+// address as well as to the memory address, so the LDS base handed to the
+// instruction is lowered by it.  The whole memory offset is in voffset (plus
+// the immediate), which the buffer range check covers: offsets past the
+// record read zeros.
+template <int IMM>
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_base - IMM), 16, (int)voffset, 0, IMM, 0);
+}
+
+template <int NG>
+__device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t r, unsigned char* tile, int w, uint32_t voffset) {
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    unsigned char* dst = tile + (w * NG + g) * 1024;
+    switch (g) {  // the group offset is an instruction immediate
+      case 0: copy_to_lds<0>(r, dst, voffset); break;
+      case 1: copy_to_lds<128>(r, dst, voffset); break;
+      case 2: copy_to_lds<256>(r, dst, voffset); break;
+      case 3: copy_to_lds<384>(r, dst, voffset); break;
+      case 4: copy_to_lds<512>(r, dst, voffset); break;
+      case 5: copy_to_lds<640>(r, dst, voffset); break;
+      case 6: copy_to_lds<768>(r, dst, voffset); break;
+      default: copy_to_lds<896>(r, dst, voffset); break;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // V^T fragment (MFMA A operand, 32 value columns x 16 keys) for value-column
-// block `db` (32 columns) and key half `c` (keys 16c..16c+15) of a tile whose
-// rows are `rowb` bytes apart.  Lane l receives column 32*db + l%32 for the
-// keys 16c + (j/4)*8 + 4*(l/32) + j%4, j = 0..7, which is the key order the
-// S^T accumulator leaves in lane l.
-__device__ __forceinline__ bf16x8 read_vt(const unsigned char* tile, int rowb, int db, int c, int lane) {
+// block `db` (32 columns) and key half `c` (keys 16c..16c+15) of a sub-tile
+// with NG column groups.  Lane l receives column 32*db + l%32 for the keys
+// 16c + (j/4)*8 + 4*(l/32) + j%4, j = 0..7, the key order the S^T
+// accumulator leaves in lane l.
+template <int NG>
+__device__ __forceinline__ bf16x8 read_vt(const unsigned char* tile, int db, int c, int lane) {
   const int g16 = lane >> 4, i = lane & 15;
   const int hh = g16 >> 1, dvh = g16 & 1, jr = i >> 2, cq = i & 3;
   const int col = 32 * db + 16 * dvh + 4 * cq;
-  const int lc = col >> 3, within = (col & 7) * 2;
   const int key0 = 16 * c + 4 * hh + jr;
-  const int key1 = key0 + 8;
-  const unsigned char* a0 = tile + key0 * rowb + swz(lc, key0) * 16 + within;
-  const unsigned char* a1 = tile + key1 * rowb + swz(lc, key1) * 16 + within;
+  const unsigned char* a0 = tile + tile_off(NG, key0, col >> 3) + (col & 7) * 2;
+  const unsigned char* a1 = tile + tile_off(NG, key0 + 8, col >> 3) + (col & 7) * 2;
   s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a0);
   s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a1);
   s16x8 x = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   return __builtin_bit_cast(bf16x8, x);
-}
-
-// Tile loader.  Wave w copies rows 8w..8w+7 of each sub-tile.  A sub-tile of
-// `ch` 16-byte chunks per row is copied in 64-chunk wave instructions, so one
-// instruction covers 64/ch rows; lane l handles chunk l % ch of row
-// (64/ch)*i + l/ch and fetches the logical chunk that the swizzle places
-// there.  `roff(r)` gives the byte offset of tile row r in its source buffer
-// (kOob for a row that must read as zeros).
-template <int CH, class RowOff>
-__device__ __forceinline__ void load_subtile(__amdgpu_buffer_rsrc_t rs, unsigned char* tile, int w, int lane,
-                                             RowOff roff) {
-  constexpr int RPI = 64 / CH;       // rows per instruction
-  constexpr int NI = 8 / RPI;        // instructions per wave (8 rows)
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = 8 * w + RPI * i + lane / CH;
-    const int pc = lane % CH;
-    const int lcn = swz(pc, r);
-    const uint32_t ro = roff(r);
-    const uint32_t off = ro == kOob ? kOob : ro + (uint32_t)lcn * 16u;
-    copy_to_lds(rs, tile + (8 * w + RPI * i) * CH * 16, off, 0);
-  }
 }
 
 // Per-workgroup context: which rows it owns and where keys come from.
@@ -186,15 +200,17 @@ struct Ctx {
 template <class C, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_kernel(const AttnParams p) {
+  constexpr bool SP = MODE == SPARSE;
   constexpr int DA = C::DA, DV = C::DV;
   constexpr int DK = DA + DB;
-  constexpr int KS = DK / 16;          // MFMA k-steps of Q.K
-  constexpr int KSA = DA / 16;         // k-steps served by the first sub-tile
+  constexpr int KS = DK / 16;            // MFMA k-steps of Q.K
+  constexpr int KSA = DA / 16;           // k-steps served by the first sub-tile
+  constexpr int NGA = DA / 64;           // column groups of the first sub-tile
+  constexpr int NGV = C::VLAT ? NGA : DV / 64;
   constexpr int NDVB = DV / 32 / WAVES;  // 32-column value blocks per wave
-  constexpr int AROWB = Smem<C>::AROWB, BROWB = Smem<C>::BROWB;
   static_assert(KS - KSA == 4, "second part is 64 columns");
 
-  __shared__ Smem<C> sm;
+  __shared__ Smem<C, SP> sm;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -283,70 +299,319 @@ void attn_fwd_kernel(const AttnParams p) {
   }
 
   // ---------------------------------------------------------- key sources
-  const int kvh = (MODE == SPARSE) ? 0 : row_head(0) / p.group;
+  const int kvh = SP ? 0 : row_head(0) / p.group;
   const uint16_t* kA = p.ka.p + cx.b * p.ka.sb + (int64_t)kvh * p.ka.sh + cx.t0 * p.ka.st;
   const uint16_t* kB = p.kb.p + cx.b * p.kb.sb + (int64_t)kvh * p.kb.sh + cx.t0 * p.kb.st;
   const uint16_t* vS = C::VLAT ? kA : p.v.p + cx.b * p.v.sb + (int64_t)kvh * p.v.sh + cx.t0 * p.v.st;
   const uint32_t stA = (uint32_t)(p.ka.st * 2), stB = (uint32_t)(p.kb.st * 2), stV = (uint32_t)(p.v.st * 2);
-  const int32_t* idx_row = (MODE == SPARSE) ? p.idx + ((int64_t)cx.b * p.Nq + cx.q0) * p.topk : nullptr;
 
-  // sparse: this lane's entry (row lr) of the index list of tile t
-  auto load_idx = [&](int t) -> int {
-    const int64_t k = (int64_t)t * BN + lr;
-    return k < p.topk ? idx_row[k] : -1;
-  };
+  if constexpr (SP) {  // stage the query's index list in LDS
+    const int32_t* idx_row = p.idx + ((int64_t)cx.b * p.Nq + cx.q0) * p.topk;
+    for (int k = tid; k < p.topk; k += 256) sm.idx[k] = idx_row[k];
+    __syncthreads();
+  }
   auto idx_ok = [&](int r) -> bool { return r >= 0 && r < p.Nkv; };
 
-  auto issue_tile = [&](int t, int buf, int idx_lane) {
+  // loader: wave w copies rows 8w..8w+7 of every sub-tile; lane l handles
+  // row 8w + l/8, chunk position l%8
+  const int lrow = 8 * w + (lane >> 3);
+  const uint32_t lchunk = (uint32_t)(((lane & 7) ^ swz_f(lane >> 3)) << 4);
+  const uint32_t voA = (uint32_t)lrow * stA + lchunk;
+  const uint32_t voB = (uint32_t)lrow * stB + lchunk;
+  const uint32_t voV = (uint32_t)lrow * stV + lchunk;
+
+  auto issue_tile = [&](int t, int buf) {
     const int64_t k0 = (int64_t)t * BN;
-    if constexpr (MODE == SPARSE) {
-      // the whole cache is the buffer; a row's offset comes from its index
+    if constexpr (SP) {
+      const int r = (int)k0 + lrow;
+      const int ix = r < p.topk ? sm.idx[r] : -1;
+      const bool ok = idx_ok(ix);
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(kA, (uint32_t)(p.Nkv * stA));
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(kB, (uint32_t)(p.Nkv * stB));
-      auto roffA = [&](int r) -> uint32_t {
-        const int ix = __builtin_amdgcn_readlane(idx_lane, r);
-        return idx_ok(ix) ? (uint32_t)ix * stA : kOob;
-      };
-      auto roffB = [&](int r) -> uint32_t {
-        const int ix = __shfl(idx_lane, r);
-        return idx_ok(ix) ? (uint32_t)ix * stB : kOob;
-      };
-      load_subtile<DA / 8>(ra, sm.a[buf], w, lane, roffA);
-      load_subtile<DB / 8>(rb, sm.b[buf], w, lane, roffB);
+      copy_rows<NGA>(ra, sm.a[buf], w, ok ? (uint32_t)ix * stA + lchunk : kOob);
+      copy_rows<1>(rb, sm.b[buf], w, ok ? (uint32_t)ix * stB + lchunk : kOob);
     } else {
       // the buffer is the tile's rows [k0, min(k0 + BN, kv_len)); rows past it read zeros
-      const int64_t nrows = min<int64_t>(BN, cx.kv_len - k0);
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(kA + k0 * p.ka.st, (uint32_t)(nrows * stA));
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(kB + k0 * p.kb.st, (uint32_t)(nrows * stB));
-      load_subtile<DA / 8>(ra, sm.a[buf], w, lane, [&](int r) -> uint32_t { return (uint32_t)r * stA; });
-      load_subtile<DB / 8>(rb, sm.b[buf], w, lane, [&](int r) -> uint32_t { return (uint32_t)r * stB; });
-      if constexpr (!C::VLAT) {
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vS + k0 * p.v.st, (uint32_t)(nrows * stV));
-        load_subtile<DV / 8>(rv, sm.v[buf], w, lane, [&](int r) -> uint32_t { return (uint32_t)r * stV; });
-      }
+      const uint32_t nrows = (uint32_t)min<int64_t>(BN, cx.kv_len - k0);
+      copy_rows<NGA>(make_rsrc(kA + k0 * p.ka.st, nrows * stA), sm.a[buf], w, voA);
+      copy_rows<1>(make_rsrc(kB + k0 * p.kb.st, nrows * stB), sm.b[buf], w, voB);
+      if constexpr (!C::VLAT) copy_rows<NGV>(make_rsrc(vS + k0 * p.v.st, nrows * stV), sm.v[buf], w, voV);
     }
   };
 
-  // LDS byte offsets of this lane's K fragments
-  const int f_lr = swz_f(lr);
+  // LDS byte offsets of this lane's K fragments (k-step c: + (c/4) KB)
   int koffA[4], koffB[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    koffA[j] = lr * AROWB + (((2 * j + h) ^ f_lr) * 16);
-    koffB[j] = lr * BROWB + (((2 * j + h) ^ f_lr) * 16);
+    koffA[j] = tile_off(NGA, lr, 2 * j + h);
+    koffB[j] = tile_off(1, lr, 2 * j + h);
   }
 
   const int n_tiles = (int)((cx.kv_end + BN - 1) / BN);
-  const int64_t my_qpos = p.q_offset + row_query(w);          // causal position of this lane's row
-  const int64_t wave_min_qpos = p.q_offset + row_query(w) - lr;  // smallest position of the wave's rows
+  // key rows visible to this lane's row: [0, vis_end), relative to the
+  // workgroup's key range (a key's position is kv_offset + its index)
+  int32_t vis_end, wave_vis_end;
+  {
+    const int64_t row_pos = p.q_offset + row_query(w);
+    const int64_t wave_pos = row_pos - lr;                // first row of the wave
+    int64_t ve = cx.kv_len, we = cx.kv_len;
+    if (p.causal && !SP) {
+      ve = min<int64_t>(ve, max<int64_t>(0, row_pos - p.kv_offset + 1));
+      we = min<int64_t>(we, max<int64_t>(0, wave_pos - p.kv_offset + 1));
+    }
+    vis_end = (int32_t)ve;        // <= kv_len, which fits 32 bits
+    wave_vis_end = (int32_t)we;   // visible to every row of the wave
+  }
 
   f32x16 O[WAVES][NDVB];
   float m_ref = -INFINITY;  // reference max of this lane's row (log2 units)
   float m_run = -INFINITY;  // running exact max
   float l_part = 0.f;       // this lane's share of the row sum, relative to m_ref
   float l_rnd = 0.f;        // the same over the bf16-rounded weights
+  bool over = false;
   if (tid == 0) sm.redo = 0;
 
+  // S^T = K Q^T for one tile (lane: query row lr; keys (r/4)*8 + 4h + r%4)
+  auto qk = [&](int buf) -> f32x16 {
+    f32x16 s;
+    if constexpr (KS == 36) {
+      // The 576-wide contraction as one MFMA chain written out by hand: the
+      // accumulator stays in VGPRs (the O accumulators own the AGPRs) and
+      // the K fragments stream through four registers, read from LDS three
+      // k-steps ahead of the MFMA that uses them.  lgkmcnt(n) waits until
+      // at most n of the reads issued so far are outstanding (LDS reads
+      // complete in order).  The trailing nops cover the MFMA result ->
+      // VALU read hazard that the compiler cannot see through the asm.
+      const uint32_t ta = lds_addr(sm.a[buf]), tb = lds_addr(sm.b[buf]);
+      const uint32_t a0 = ta + koffA[0], a1 = ta + koffA[1], a2 = ta + koffA[2], a3 = ta + koffA[3];
+      const uint32_t b0 = tb + koffB[0], b1 = tb + koffB[1], b2 = tb + koffB[2], b3 = tb + koffB[3];
+      u32x4 t0, t1, t2, t3;
+    asm volatile(
+      "s_waitcnt lgkmcnt(0)\n"
+      "ds_read_b128 %[t0], %[a0] offset:0\n"
+      "ds_read_b128 %[t1], %[a1] offset:0\n"
+      "ds_read_b128 %[t2], %[a2] offset:0\n"
+      "ds_read_b128 %[t3], %[a3] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], 0\n"
+      "ds_read_b128 %[t0], %[a0] offset:1024\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
+      "ds_read_b128 %[t1], %[a1] offset:1024\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
+      "ds_read_b128 %[t2], %[a2] offset:1024\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
+      "ds_read_b128 %[t3], %[a3] offset:1024\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q4], %[s]\n"
+      "ds_read_b128 %[t0], %[a0] offset:2048\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q5], %[s]\n"
+      "ds_read_b128 %[t1], %[a1] offset:2048\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q6], %[s]\n"
+      "ds_read_b128 %[t2], %[a2] offset:2048\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q7], %[s]\n"
+      "ds_read_b128 %[t3], %[a3] offset:2048\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q8], %[s]\n"
+      "ds_read_b128 %[t0], %[a0] offset:3072\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q9], %[s]\n"
+      "ds_read_b128 %[t1], %[a1] offset:3072\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q10], %[s]\n"
+      "ds_read_b128 %[t2], %[a2] offset:3072\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q11], %[s]\n"
+      "ds_read_b128 %[t3], %[a3] offset:3072\n"
+      : [s] "=&v"(s), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
+      : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
+      : "memory");
+    asm volatile(
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], %[s]\n"
+      "ds_read_b128 %[t0], %[a0] offset:4096\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
+      "ds_read_b128 %[t1], %[a1] offset:4096\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
+      "ds_read_b128 %[t2], %[a2] offset:4096\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
+      "ds_read_b128 %[t3], %[a3] offset:4096\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q4], %[s]\n"
+      "ds_read_b128 %[t0], %[a0] offset:5120\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q5], %[s]\n"
+      "ds_read_b128 %[t1], %[a1] offset:5120\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q6], %[s]\n"
+      "ds_read_b128 %[t2], %[a2] offset:5120\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q7], %[s]\n"
+      "ds_read_b128 %[t3], %[a3] offset:5120\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q8], %[s]\n"
+      "ds_read_b128 %[t0], %[a0] offset:6144\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q9], %[s]\n"
+      "ds_read_b128 %[t1], %[a1] offset:6144\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q10], %[s]\n"
+      "ds_read_b128 %[t2], %[a2] offset:6144\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q11], %[s]\n"
+      "ds_read_b128 %[t3], %[a3] offset:6144\n"
+      : [s] "+v"(s), [t0] "+v"(t0), [t1] "+v"(t1), [t2] "+v"(t2), [t3] "+v"(t3)
+      : [q0] "v"(qf[12]), [q1] "v"(qf[13]), [q2] "v"(qf[14]), [q3] "v"(qf[15]), [q4] "v"(qf[16]), [q5] "v"(qf[17]), [q6] "v"(qf[18]), [q7] "v"(qf[19]), [q8] "v"(qf[20]), [q9] "v"(qf[21]), [q10] "v"(qf[22]), [q11] "v"(qf[23]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
+      : "memory");
+    asm volatile(
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], %[s]\n"
+      "ds_read_b128 %[t0], %[a0] offset:7168\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
+      "ds_read_b128 %[t1], %[a1] offset:7168\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
+      "ds_read_b128 %[t2], %[a2] offset:7168\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
+      "ds_read_b128 %[t3], %[a3] offset:7168\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q4], %[s]\n"
+      "ds_read_b128 %[t0], %[b0] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q5], %[s]\n"
+      "ds_read_b128 %[t1], %[b1] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q6], %[s]\n"
+      "ds_read_b128 %[t2], %[b2] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q7], %[s]\n"
+      "ds_read_b128 %[t3], %[b3] offset:0\n"
+      "s_waitcnt lgkmcnt(3)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q8], %[s]\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q9], %[s]\n"
+      "s_waitcnt lgkmcnt(1)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q10], %[s]\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q11], %[s]\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      "s_nop 7\n"
+      : [s] "+v"(s), [t0] "+v"(t0), [t1] "+v"(t1), [t2] "+v"(t2), [t3] "+v"(t3)
+      : [q0] "v"(qf[24]), [q1] "v"(qf[25]), [q2] "v"(qf[26]), [q3] "v"(qf[27]), [q4] "v"(qf[28]), [q5] "v"(qf[29]), [q6] "v"(qf[30]), [q7] "v"(qf[31]), [q8] "v"(qf[32]), [q9] "v"(qf[33]), [q10] "v"(qf[34]), [q11] "v"(qf[35]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3), [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3)
+      : "memory");
+
+    } else {
+      s = f32x16{};
+      const unsigned char* ta = sm.a[buf];
+      const unsigned char* tb = sm.b[buf];
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        const bf16x8 kf = c < KSA ? *reinterpret_cast<const bf16x8*>(ta + koffA[c & 3] + (c >> 2) * 1024)
+                                  : *reinterpret_cast<const bf16x8*>(tb + koffB[c - KSA]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s, 0, 0, 0);
+      }
+    }
+    return s;
+  };
+
+  // softmax, first half: scale to log2 units, mask, row max, reference max.
+  // `live` false: no tile (all scores masked).
+  auto scores = [&](const f32x16& s, int t, bool live, float* x) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = s[r] * p.scale_log2;
+    bool need_mask;
+    unsigned vbits = 0xffffffffu;
+    if constexpr (SP) {
+      const int k = k0 + lr;
+      vbits = (unsigned)__ballot(live && k < p.topk && idx_ok(sm.idx[k < p.topk ? k : 0]));
+      need_mask = vbits != 0xffffffffu;
+    } else {
+      need_mask = !live || k0 + BN > wave_vis_end;
+    }
+    if (need_mask) {
+      // key kk of the tile (kk = (r/4)*8 + 4h + r%4) is visible iff
+      // k0 + kk < vis_end, i.e. (r/4)*8 + r%4 < vis_end - k0 - 4h
+      const int bound = live ? vis_end - k0 - 4 * h : -1000;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bool ok;
+        if constexpr (SP) {
+          ok = (vbits >> ((r >> 2) * 8 + 4 * h + (r & 3))) & 1u;
+        } else {
+          ok = (r >> 2) * 8 + (r & 3) < bound;
+        }
+        x[r] = ok ? x[r] : -INFINITY;
+      }
+    }
+    float mt = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
+    mt = xhalf_max(mt);
+    m_run = fmaxf(m_run, mt);
+    if (m_ref == -INFINITY) m_ref = mt;  // the row's first visible tile (pass 0)
+    over |= m_run > m_ref + TAU;
+  };
+
+  // softmax, second half: weights, row sums, bf16 P^T fragments to LDS
+  auto weights = [&](const float* x, int pb) {
+    const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+    f32x8 p0, p1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      p0[r] = __builtin_amdgcn_exp2f(x[r] - mu);
+      p1[r] = __builtin_amdgcn_exp2f(x[r + 8] - mu);
+    }
+    const bf16x8 b0 = __builtin_convertvector(p0, bf16x8);
+    const bf16x8 b1 = __builtin_convertvector(p1, bf16x8);
+    // the exact row sum gives the LSE; the sum of the weights as the P.V
+    // product sees them (rounded to bf16) normalises O, so its weights sum to one
+    float ps = 0.f, pr = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      ps += p0[r] + p1[r];
+      pr += (float)b0[r] + (float)b1[r];
+    }
+    l_part += ps;
+    l_rnd += pr;
+    *reinterpret_cast<bf16x8*>(sm.p[pb][w][0] + lane * 16) = b0;
+    *reinterpret_cast<bf16x8*>(sm.p[pb][w][1] + lane * 16) = b1;
+  };
+
+  // O^T += V^T P^T over this wave's value columns for all 128 rows
+  auto pv = [&](int buf, int pb) {
+    const unsigned char* vt = C::VLAT ? sm.a[buf] : sm.v[buf];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 pf[WAVES];
+#pragma unroll
+      for (int rb = 0; rb < WAVES; ++rb) pf[rb] = *reinterpret_cast<const bf16x8*>(sm.p[pb][rb][c] + lane * 16);
+#pragma unroll
+      for (int j = 0; j < NDVB; ++j) {
+        const bf16x8 vf = read_vt<NGV>(vt, w * NDVB + j, c, lane);
+#pragma unroll
+        for (int rb = 0; rb < WAVES; ++rb)
+          O[rb][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], O[rb][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // ------------------------------------------------------------ main loop
+  // Iteration t computes S(t+1) = K(t+1) Q^T, then P(t) V(t) with the
+  // softmax of S(t+1) in between, and ends on the one barrier of the
+  // iteration.  Tiles t, t+1 are resident and t+2 is in flight (3 buffers);
+  // P is double buffered.
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
       if (!sm.redo) break;   // workgroup-uniform: read after a barrier
@@ -359,119 +624,33 @@ void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int j = 0; j < NDVB; ++j) O[rb][j] = f32x16{};
 
-    int idx_cur = -1, idx_nxt = -1;
     if (n_tiles > 0) {
-      if constexpr (MODE == SPARSE) {
-        idx_cur = load_idx(0);
-        idx_nxt = n_tiles > 1 ? load_idx(1) : -1;
+      issue_tile(0, 0);
+      if (n_tiles > 1) issue_tile(1, 1);
+      wait_vmem();
+      __syncthreads();
+      {
+        float x[16];
+        scores(qk(0), 0, true, x);
+        weights(x, 0);
+      }
+      if (n_tiles > 2) issue_tile(2, 2);
+      __syncthreads();
+      int buf = 0;
+      for (int t = 0; t < n_tiles; ++t) {
+        const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+        const bool live = t + 1 < n_tiles;
+        f32x16 s = f32x16{};
+        if (live) s = qk(nbuf);
+        float x[16];
+        scores(s, t + 1, live, x);
+        pv(buf, t & 1);
+        weights(x, (t + 1) & 1);
         wait_vmem();
+        __syncthreads();
+        if (t + 3 < n_tiles) issue_tile(t + 3, buf);
+        buf = nbuf;
       }
-      issue_tile(0, 0, idx_cur);
-      wait_vmem();
-    }
-    __syncthreads();
-
-    bool over = false;
-    for (int t = 0; t < n_tiles; ++t) {
-      const int buf = t & 1;
-      int idx_nn = -1;
-      if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1, idx_nxt);
-      if constexpr (MODE == SPARSE) {
-        if (t + 2 < n_tiles) idx_nn = load_idx(t + 2);
-      }
-      const int64_t k0 = (int64_t)t * BN;
-
-      // S^T = K Q^T  (lane: query row lr; keys (r/4)*8 + 4h + r%4)
-      f32x16 s = f32x16{};
-      const unsigned char* ta = sm.a[buf];
-      const unsigned char* tb = sm.b[buf];
-#pragma unroll
-      for (int c = 0; c < KS; ++c) {
-        const bf16x8 kf = c < KSA
-            ? *reinterpret_cast<const bf16x8*>(ta + koffA[c & 3] + (c >> 2) * 128)
-            : *reinterpret_cast<const bf16x8*>(tb + koffB[c - KSA]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s, 0, 0, 0);
-      }
-
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = s[r] * p.scale_log2;
-
-      bool need_mask;
-      unsigned vbits = 0xffffffffu;
-      if constexpr (MODE == SPARSE) {
-        vbits = (unsigned)__ballot(idx_ok(idx_cur));
-        need_mask = vbits != 0xffffffffu;
-      } else {
-        need_mask = (k0 + BN > cx.kv_len) || (p.causal && p.kv_offset + k0 + BN - 1 > wave_min_qpos);
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = (r >> 2) * 8 + 4 * h + (r & 3);
-          bool ok;
-          if constexpr (MODE == SPARSE) {
-            ok = (vbits >> kk) & 1u;
-          } else {
-            const int64_t key = k0 + kk;
-            ok = key < cx.kv_len && (!p.causal || p.kv_offset + key <= my_qpos);
-          }
-          x[r] = ok ? x[r] : -INFINITY;
-        }
-      }
-
-      float mt = x[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-      mt = xhalf_max(mt);
-      m_run = fmaxf(m_run, mt);
-      if (m_ref == -INFINITY) m_ref = mt;        // the row's first visible tile (pass 0)
-      over |= m_run > m_ref + TAU;
-      const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-      f32x8 p0, p1;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        p0[r] = __builtin_amdgcn_exp2f(x[r] - mu);
-        p1[r] = __builtin_amdgcn_exp2f(x[r + 8] - mu);
-      }
-      const bf16x8 b0 = __builtin_convertvector(p0, bf16x8);
-      const bf16x8 b1 = __builtin_convertvector(p1, bf16x8);
-      // two row sums: the exact one gives the LSE; the one of the weights as
-      // the P.V product sees them (rounded to bf16) normalises O, so that its
-      // weights sum to one
-      float ps = 0.f, pr = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        ps += p0[r] + p1[r];
-        pr += (float)b0[r] + (float)b1[r];
-      }
-      l_part += ps;
-      l_rnd += pr;
-
-      *reinterpret_cast<bf16x8*>(sm.p[w][0] + lane * 16) = b0;
-      *reinterpret_cast<bf16x8*>(sm.p[w][1] + lane * 16) = b1;
-      __syncthreads();
-
-      // O^T += V^T P^T over this wave's value columns for all 128 rows
-      const unsigned char* vt = C::VLAT ? sm.a[buf] : sm.v[buf];
-      constexpr int VROWB = C::VLAT ? AROWB : Smem<C>::VROWB;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 pb[WAVES];
-#pragma unroll
-        for (int rb = 0; rb < WAVES; ++rb) pb[rb] = *reinterpret_cast<const bf16x8*>(sm.p[rb][c] + lane * 16);
-#pragma unroll
-        for (int j = 0; j < NDVB; ++j) {
-          const bf16x8 vf = read_vt(vt, VROWB, w * NDVB + j, c, lane);
-#pragma unroll
-          for (int rb = 0; rb < WAVES; ++rb)
-            O[rb][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[rb], O[rb][j], 0, 0, 0);
-        }
-      }
-      wait_vmem();
-      __syncthreads();
-      idx_cur = idx_nxt;
-      idx_nxt = idx_nn;
     }
     if (pass == 0) {
       if (__ballot(over) != 0ull && lane == 0) sm.redo = 1;
@@ -531,15 +710,15 @@ void attn_fwd_kernel(const AttnParams p) {
         for (int e = 0; e < 4; ++e) y[e] = wc * O[rb][j][4 * g + e];
         if (fold) {
           if (p.prev_f32) {
-            const f32x4 pv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.prev_out.p) + pel + d);
+            const f32x4 pv4 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.prev_out.p) + pel + d);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] += wp * pv[e];
+            for (int e = 0; e < 4; ++e) y[e] += wp * pv4[e];
           } else {
-            const u32x2 pv = *reinterpret_cast<const u32x2*>(p.prev_out.p + pel + d);
-            y[0] += wp * __uint_as_float(pv[0] << 16);
-            y[1] += wp * __uint_as_float(pv[0] & 0xffff0000u);
-            y[2] += wp * __uint_as_float(pv[1] << 16);
-            y[3] += wp * __uint_as_float(pv[1] & 0xffff0000u);
+            const u32x2 pv2 = *reinterpret_cast<const u32x2*>(p.prev_out.p + pel + d);
+            y[0] += wp * __uint_as_float(pv2[0] << 16);
+            y[1] += wp * __uint_as_float(pv2[0] & 0xffff0000u);
+            y[2] += wp * __uint_as_float(pv2[1] << 16);
+            y[3] += wp * __uint_as_float(pv2[1] & 0xffff0000u);
           }
         }
         if (p.out_f32) {
@@ -559,37 +738,33 @@ void attn_fwd_kernel(const AttnParams p) {
 // natural order.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void debug_gather_kernel(const GatherParams p) {
-  constexpr int DA = 512;
+  constexpr int DA = 512, NGA = DA / 64;
   __shared__ alignas(16) unsigned char ta[BN * DA * 2];
   __shared__ alignas(16) unsigned char tb[BN * DB * 2];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, lr = lane & 31;
+  const int lane = tid & 63;
   const uint16_t* kA = p.ka.p + p.b * p.ka.sb;
   const uint16_t* kB = p.kb.p + p.b * p.kb.sb;
   const uint32_t stA = (uint32_t)(p.ka.st * 2), stB = (uint32_t)(p.kb.st * 2);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(kA, (uint32_t)(p.Nkv * stA));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(kB, (uint32_t)(p.Nkv * stB));
+  const int lrow = 8 * w + (lane >> 3);
+  const uint32_t lchunk = (uint32_t)(((lane & 7) ^ swz_f(lane >> 3)) << 4);
+  auto ok = [&](int r) { return r >= 0 && r < p.Nkv; };
   const int n_tiles = (p.K + BN - 1) / BN;
   for (int t = 0; t < n_tiles; ++t) {
     const int k0 = t * BN;
-    const int ix = (k0 + lr < p.K) ? p.idx[k0 + lr] : -1;
-    auto ok = [&](int r) { return r >= 0 && r < p.Nkv; };
-    load_subtile<DA / 8>(ra, ta, w, lane, [&](int r) -> uint32_t {
-      const int v = __builtin_amdgcn_readlane(ix, r);
-      return ok(v) ? (uint32_t)v * stA : kOob;
-    });
-    load_subtile<DB / 8>(rb, tb, w, lane, [&](int r) -> uint32_t {
-      const int v = __shfl(ix, r);
-      return ok(v) ? (uint32_t)v * stB : kOob;
-    });
+    const int ix = (k0 + lrow < p.K) ? p.idx[k0 + lrow] : -1;
+    copy_rows<NGA>(ra, ta, w, ok(ix) ? (uint32_t)ix * stA + lchunk : kOob);
+    copy_rows<1>(rb, tb, w, ok(ix) ? (uint32_t)ix * stB + lchunk : kOob);
     wait_vmem();
     __syncthreads();
     for (int e = tid; e < BN * (DA + DB) / 8; e += 256) {
       const int r = e / ((DA + DB) / 8), c = e % ((DA + DB) / 8);
       if (k0 + r >= p.K) continue;
-      const u32x4 val = c < DA / 8 ? *reinterpret_cast<const u32x4*>(ta + r * DA * 2 + swz(c, r) * 16)
-                                   : *reinterpret_cast<const u32x4*>(tb + r * DB * 2 + swz(c - DA / 8, r) * 16);
+      const u32x4 val = c < DA / 8 ? *reinterpret_cast<const u32x4*>(ta + tile_off(NGA, r, c))
+                                   : *reinterpret_cast<const u32x4*>(tb + tile_off(1, r, c - DA / 8));
       *reinterpret_cast<u32x4*>(p.rows_out + (int64_t)(k0 + r) * (DA + DB) + c * 8) = val;
     }
     __syncthreads();
