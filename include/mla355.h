@@ -171,7 +171,8 @@ mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a,
  *
  * out [B, S, H*L] bf16 as a view with t = query, h = head (stride_h = L for
  * the page's row-major h*L + l order); lse [B, S, H] fp32 (view with t =
- * query, h = head) or NULL.  L == 512, R == 64, 1 <= K.
+ * query, h = head) or NULL.  L == 512, R == 64, H <= 128, 1 <= K <= 4096
+ * (larger K returns MLA_ERR_UNSUPPORTED).
  */
 mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe,
                           const mla_rows* c_kv, const mla_rows* k_pe,

@@ -239,6 +239,8 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
     return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, S >= 0, S_kv > 0, H > 0, K > 0");
   if (L != 512 || R != 64) return fail(MLA_ERR_UNSUPPORTED, "sparse kernel is built for L = 512, R = 64 (got %d, %d)", L, R);
   if (H > 128) return fail(MLA_ERR_UNSUPPORTED, "sparse kernel handles up to 128 heads per query (got %d)", H);
+  if (K > mla::kSparseMaxTopk)
+    return fail(MLA_ERR_UNSUPPORTED, "sparse kernel handles up to %d indices per query (got %d)", mla::kSparseMaxTopk, K);
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
   if ((st = check_rows(q_lift, "q_lift")) || (st = check_rows(q_pe, "q_pe")) || (st = check_rows(out, "out")))
     return st;

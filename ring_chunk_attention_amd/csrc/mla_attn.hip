@@ -79,16 +79,18 @@ struct SplitCfg {
   static constexpr bool VLAT = false;  // separate V tile
 };
 
-// Physical 16-byte chunk of logical chunk `c` in tile row `r`: the low three
-// bits are XORed with f(r) = 2*(r%4) + (r/4)%2, a permutation of 0..7 over
-// any 8 aligned rows (conflict-free 16-byte reads of 8 rows at one column)
-// whose values over 4 aligned rows are all even or all odd (conflict-free
-// 8-byte transposed reads of 4 rows x 32 bytes).
-__device__ __forceinline__ int swz_f(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ int swz(int c, int r) { return c ^ swz_f(r); }
+// Row swizzle of the LDS tiles: logical 16-byte chunk c of tile row r sits at
+// position c ^ g(r) within its 128-byte group, with g(r) = 4*((r/2)%2) +
+// (r/4)%4.  The LDS has 64 four-byte banks and serves 16 lanes of a 16-byte
+// read per cycle.  Over any 16 aligned rows, g is a permutation of 0..7 on the
+// even rows and on the odd rows, so 16 rows read at one column fall on 16
+// distinct 16-byte bank groups (rows of a block are 128 bytes apart, so even
+// and odd rows use opposite halves of the 256-byte bank window); and within 4
+// aligned rows the two rows of equal parity differ in bit 2, so the 8-byte
+// transposed reads of 4 rows x 32 bytes are conflict-free as well.
+__device__ __forceinline__ int swz_f(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
-constexpr int NBUF = 3;          // key-tile buffers in flight
-constexpr int KMAX_IDX = 4096;   // sparse: longest index list staged in LDS
+constexpr int KMAX_IDX = kSparseMaxTopk;  // sparse: longest index list staged in LDS
 
 // Sub-tile layout.  A sub-tile with NG 64-column groups per row is stored as
 // blocks of 8 rows x 8 chunks (16 bytes each) = 1 KB: block (r/8, g) at byte
@@ -97,25 +99,38 @@ constexpr int KMAX_IDX = 4096;   // sparse: longest index list staged in LDS
 // fills one block, so every lane's source offset is the same for all groups
 // and tiles, and the instruction offset selects the group.
 __device__ __forceinline__ int tile_off(int NG, int r, int q) {
-  return (((r >> 3) * NG + (q >> 3)) << 10) + ((r & 7) << 7) + (((q & 7) ^ swz_f(r & 7)) << 4);
+  return (((r >> 3) * NG + (q >> 3)) << 10) + ((r & 7) << 7) + (((q & 7) ^ swz_f(r & 15)) << 4);
 }
 
-template <class C, bool SP>
+template <class C, bool SP, int NB>
 struct Smem {
   static constexpr int ATILE = BN * C::DA * 2, BTILE = BN * DB * 2;
-  static constexpr int VTILE = C::VLAT ? 16 : BN * C::DV * 2;
-  alignas(16) unsigned char a[NBUF][ATILE];
-  alignas(16) unsigned char b[NBUF][BTILE];
-  alignas(16) unsigned char v[NBUF][VTILE];
-  alignas(16) unsigned char p[2][WAVES][2][64 * 16];  // P^T fragments: buffer, wave, 16-key half
-  alignas(16) int idx[SP ? KMAX_IDX : 4];            // sparse: the query's index list
-  alignas(16) float wprev[ROWS];
-  alignas(16) float wcur[ROWS];
-  int redo;
+  static constexpr int VTILE = C::VLAT ? 0 : BN * C::DV * 2;
+  alignas(16) unsigned char a[NB][ATILE];
+  alignas(16) unsigned char b[NB][BTILE];
+  alignas(16) unsigned char v[NB][VTILE];
+  alignas(16) int idx[SP ? KMAX_IDX : 0];            // sparse: the query's index list
+  union {
+    alignas(16) unsigned char p[2][WAVES][2][64 * 16];  // P^T fragments: buffer, wave, 16-key half
+    struct {                                            // after the key loop
+      float wprev[ROWS];
+      float wcur[ROWS];
+      int flag[WAVES];
+    } epi;
+  };
 };
 
-__device__ __forceinline__ float xhalf_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float xhalf_sum(float x) { return x + __shfl_xor(x, 32); }
+// Combine lane l with lane l^32: v_permlane32_swap exchanges the upper half
+// of one register with the lower half of another; with both operands equal
+// to x the two results hold x and its partner value in either order.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ bf16x8 load16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
@@ -128,26 +143,51 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcFlags);
+// Raw buffer resource (4 scalar words) over `bytes` bytes at `base`: stride
+// 0, so an offset at or past `bytes` is out of range and reads zeros.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kRsrcFlags;
+  return r;
 }
 
-// One wave-wide copy into LDS: lane l's 16 bytes at rsrc + voffset + IMM land
-// at lds_base + 16*l.  The instruction's immediate offset is added to the LDS
-// address as well as to the memory address, so the LDS base handed to the
-// instruction is lowered by it.  The whole memory offset is in voffset (plus
-// the immediate), which the buffer range check covers: offsets past the
-// record read zeros.
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
+// One wave-wide copy into LDS (buffer_load_dwordx4 ... lds): lane l's 16 bytes
+// at rsrc + voffset + IMM land at lds_base + 16*l.  The LDS address is M0 +
+// IMM + 16*l (the immediate offset applies to both sides), so M0 is set to
+// lds_base - IMM; the nop covers the M0 write -> LDS-DMA read hazard.  The
+// copy is issued from asm so that the compiler does not make later LDS reads
+// of the other tile buffers wait for it: the kernel waits for its copies
+// itself (vmcnt) before the barrier that publishes a tile.  M0 is a reserved
+// register, so the asm restores it.
 template <int IMM>
-__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base, uint32_t voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_base - IMM), 16, (int)voffset, 0, IMM, 0);
+__device__ __forceinline__ void copy_to_lds(const u32x4& r, uint32_t lds, uint32_t voffset) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n"
+      "s_mov_b32 m0, %[m0]\n"
+      "s_nop 0\n"
+      "buffer_load_dwordx4 %[vo], %[rs], 0 offen offset:%[imm] lds\n"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [m0] "s"(lds - IMM), [vo] "v"(voffset), [rs] "s"(r), [imm] "n"(IMM)
+      : "memory");
 }
 
-template <int NG>
-__device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t r, unsigned char* tile, int w, uint32_t voffset) {
+// Copy column groups [G0, G1) of a block row (8 rows x NG column groups) of a
+// sub-tile at LDS byte address `tile`: one instruction per column group.
+template <int NG, int G0 = 0, int G1 = NG>
+__device__ __forceinline__ void copy_rows(const u32x4& r, uint32_t tile, int w, uint32_t voffset) {
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    unsigned char* dst = tile + (w * NG + g) * 1024;
+  for (int g = G0; g < G1; ++g) {
+    const uint32_t dst = tile + (uint32_t)(w * NG + g) * 1024u;
     switch (g) {  // the group offset is an instruction immediate
       case 0: copy_to_lds<0>(r, dst, voffset); break;
       case 1: copy_to_lds<128>(r, dst, voffset); break;
@@ -161,11 +201,19 @@ __device__ __forceinline__ void copy_rows(__amdgpu_buffer_rsrc_t r, unsigned cha
   }
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
-}
-
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Wait until at most `tiles` tiles' copies (KI copy instructions each, issued
+// by this wave) are in flight; loads complete in order.
+template <int KI>
+__device__ __forceinline__ void wait_tiles(int tiles) {
+  if (tiles <= 0) wait_vmem_n<0>();
+  else if (tiles == 1) wait_vmem_n<KI>();
+  else wait_vmem_n<2 * KI>();
+}
 
 // V^T fragment (MFMA A operand, 32 value columns x 16 keys) for value-column
 // block `db` (32 columns) and key half `c` (keys 16c..16c+15) of a sub-tile
@@ -208,9 +256,14 @@ void attn_fwd_kernel(const AttnParams p) {
   constexpr int NGA = DA / 64;           // column groups of the first sub-tile
   constexpr int NGV = C::VLAT ? NGA : DV / 64;
   constexpr int NDVB = DV / 32 / WAVES;  // 32-column value blocks per wave
+  constexpr int KI = NGA + 1 + (C::VLAT ? 0 : NGV);  // copy instructions per wave per tile
+  // key-tile buffers: four let a tile's copy run two iterations ahead of its
+  // use (the sparse form keeps the index list in LDS instead of a fourth)
+  constexpr int NB = SP ? 3 : 4;
   static_assert(KS - KSA == 4, "second part is 64 columns");
+  static_assert(NB - 2 <= 2, "wait_tiles covers at most two tiles in flight");
 
-  __shared__ Smem<C, SP> sm;
+  __shared__ Smem<C, SP, NB> sm;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -315,27 +368,56 @@ void attn_fwd_kernel(const AttnParams p) {
   // loader: wave w copies rows 8w..8w+7 of every sub-tile; lane l handles
   // row 8w + l/8, chunk position l%8
   const int lrow = 8 * w + (lane >> 3);
-  const uint32_t lchunk = (uint32_t)(((lane & 7) ^ swz_f(lane >> 3)) << 4);
+  const uint32_t lchunk = (uint32_t)(((lane & 7) ^ swz_f(lrow & 15)) << 4);
   const uint32_t voA = (uint32_t)lrow * stA + lchunk;
   const uint32_t voB = (uint32_t)lrow * stB + lchunk;
   const uint32_t voV = (uint32_t)lrow * stV + lchunk;
 
-  auto issue_tile = [&](int t, int buf) {
+  // LDS byte addresses of the tile buffers (buffer i at + i * tile size)
+  const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]);
+  const uint32_t lds_v = C::VLAT ? lds_a : lds_addr(&sm.v[0][0]);
+
+  // Issue the copies of tile t into buffer buf.  part < 0: all of them;
+  // part 0, 1, 2 (the 576-wide form): about a third each, so that the copies
+  // can be spread over the Q.K chain instead of queueing up at once.
+  auto issue_tile = [&](int t, int buf, int part) {
     const int64_t k0 = (int64_t)t * BN;
+    const uint32_t la = lds_a + buf * Smem<C, SP, NB>::ATILE;
+    const uint32_t lb = lds_b + buf * Smem<C, SP, NB>::BTILE;
+    u32x4 ra, rb;
+    uint32_t oa, ob;
     if constexpr (SP) {
       const int r = (int)k0 + lrow;
       const int ix = r < p.topk ? sm.idx[r] : -1;
       const bool ok = idx_ok(ix);
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(kA, (uint32_t)(p.Nkv * stA));
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(kB, (uint32_t)(p.Nkv * stB));
-      copy_rows<NGA>(ra, sm.a[buf], w, ok ? (uint32_t)ix * stA + lchunk : kOob);
-      copy_rows<1>(rb, sm.b[buf], w, ok ? (uint32_t)ix * stB + lchunk : kOob);
+      ra = make_rsrc(kA, (uint32_t)(p.Nkv * stA));
+      rb = make_rsrc(kB, (uint32_t)(p.Nkv * stB));
+      oa = ok ? (uint32_t)ix * stA + lchunk : kOob;
+      ob = ok ? (uint32_t)ix * stB + lchunk : kOob;
     } else {
       // the buffer is the tile's rows [k0, min(k0 + BN, kv_len)); rows past it read zeros
       const uint32_t nrows = (uint32_t)min<int64_t>(BN, cx.kv_len - k0);
-      copy_rows<NGA>(make_rsrc(kA + k0 * p.ka.st, nrows * stA), sm.a[buf], w, voA);
-      copy_rows<1>(make_rsrc(kB + k0 * p.kb.st, nrows * stB), sm.b[buf], w, voB);
-      if constexpr (!C::VLAT) copy_rows<NGV>(make_rsrc(vS + k0 * p.v.st, nrows * stV), sm.v[buf], w, voV);
+      ra = make_rsrc(kA + k0 * p.ka.st, nrows * stA);
+      rb = make_rsrc(kB + k0 * p.kb.st, nrows * stB);
+      oa = voA;
+      ob = voB;
+      if constexpr (!C::VLAT) {
+        if (part <= 0)
+          copy_rows<NGV>(make_rsrc(vS + k0 * p.v.st, nrows * stV), lds_v + buf * Smem<C, SP, NB>::VTILE, w, voV);
+      }
+    }
+    if constexpr (NGA == 8) {
+      if (part < 0 || part == 0) copy_rows<NGA, 0, 3>(ra, la, w, oa);
+      if (part < 0 || part == 1) copy_rows<NGA, 3, 6>(ra, la, w, oa);
+      if (part < 0 || part == 2) {
+        copy_rows<NGA, 6, 8>(ra, la, w, oa);
+        copy_rows<1>(rb, lb, w, ob);
+      }
+    } else {
+      if (part <= 0) {
+        copy_rows<NGA>(ra, la, w, oa);
+        copy_rows<1>(rb, lb, w, ob);
+      }
     }
   };
 
@@ -369,149 +451,155 @@ void attn_fwd_kernel(const AttnParams p) {
   float l_part = 0.f;       // this lane's share of the row sum, relative to m_ref
   float l_rnd = 0.f;        // the same over the bf16-rounded weights
   bool over = false;
-  if (tid == 0) sm.redo = 0;
 
   // S^T = K Q^T for one tile (lane: query row lr; keys (r/4)*8 + 4h + r%4)
-  auto qk = [&](int buf) -> f32x16 {
+  // pend_t >= 0: copies of tile pend_t into buffer pend_buf to issue along
+  // the way
+  auto qk = [&](int buf, int pend_t, int pend_buf) -> f32x16 {
     f32x16 s;
     if constexpr (KS == 36) {
       // The 576-wide contraction as one MFMA chain written out by hand: the
       // accumulator stays in VGPRs (the O accumulators own the AGPRs) and
-      // the K fragments stream through four registers, read from LDS three
-      // k-steps ahead of the MFMA that uses them.  lgkmcnt(n) waits until
+      // the K fragments stream through six registers, read from LDS five
+      // k-steps ahead of the MFMA that uses them (LDS latency under load is
+      // well above three MFMA issue intervals).  lgkmcnt(n) waits until
       // at most n of the reads issued so far are outstanding (LDS reads
       // complete in order).  The trailing nops cover the MFMA result ->
       // VALU read hazard that the compiler cannot see through the asm.
-      const uint32_t ta = lds_addr(sm.a[buf]), tb = lds_addr(sm.b[buf]);
+      const uint32_t ta = lds_a + buf * Smem<C, SP, NB>::ATILE, tb = lds_b + buf * Smem<C, SP, NB>::BTILE;
       const uint32_t a0 = ta + koffA[0], a1 = ta + koffA[1], a2 = ta + koffA[2], a3 = ta + koffA[3];
       const uint32_t b0 = tb + koffB[0], b1 = tb + koffB[1], b2 = tb + koffB[2], b3 = tb + koffB[3];
-      u32x4 t0, t1, t2, t3;
-    asm volatile(
+      u32x4 t0, t1, t2, t3, t4, t5;
+      if (pend_t >= 0) issue_tile(pend_t, pend_buf, 0);
+      asm volatile(
       "s_waitcnt lgkmcnt(0)\n"
       "ds_read_b128 %[t0], %[a0] offset:0\n"
       "ds_read_b128 %[t1], %[a1] offset:0\n"
       "ds_read_b128 %[t2], %[a2] offset:0\n"
       "ds_read_b128 %[t3], %[a3] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t4], %[a0] offset:1024\n"
+      "ds_read_b128 %[t5], %[a1] offset:1024\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], 0\n"
-      "ds_read_b128 %[t0], %[a0] offset:1024\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t0], %[a2] offset:1024\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
-      "ds_read_b128 %[t1], %[a1] offset:1024\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t1], %[a3] offset:1024\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
-      "ds_read_b128 %[t2], %[a2] offset:1024\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t2], %[a0] offset:2048\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
-      "ds_read_b128 %[t3], %[a3] offset:1024\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q4], %[s]\n"
-      "ds_read_b128 %[t0], %[a0] offset:2048\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q5], %[s]\n"
-      "ds_read_b128 %[t1], %[a1] offset:2048\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q6], %[s]\n"
-      "ds_read_b128 %[t2], %[a2] offset:2048\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q7], %[s]\n"
-      "ds_read_b128 %[t3], %[a3] offset:2048\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q8], %[s]\n"
+      "ds_read_b128 %[t3], %[a1] offset:2048\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q4], %[s]\n"
+      "ds_read_b128 %[t4], %[a2] offset:2048\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q5], %[s]\n"
+      "ds_read_b128 %[t5], %[a3] offset:2048\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q6], %[s]\n"
       "ds_read_b128 %[t0], %[a0] offset:3072\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q9], %[s]\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q7], %[s]\n"
       "ds_read_b128 %[t1], %[a1] offset:3072\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q10], %[s]\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q8], %[s]\n"
       "ds_read_b128 %[t2], %[a2] offset:3072\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q11], %[s]\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q9], %[s]\n"
       "ds_read_b128 %[t3], %[a3] offset:3072\n"
-      : [s] "=&v"(s), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3)
-      : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
-      : "memory");
-    asm volatile(
-      "s_waitcnt lgkmcnt(3)\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q10], %[s]\n"
+      "ds_read_b128 %[t4], %[a0] offset:4096\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q11], %[s]\n"
+      "ds_read_b128 %[t5], %[a1] offset:4096\n"
+          : [s] "=&v"(s), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [t4] "=&v"(t4), [t5] "=&v"(t5)
+          : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
+          : "memory");
+      if (pend_t >= 0) issue_tile(pend_t, pend_buf, 1);
+      asm volatile(
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], %[s]\n"
-      "ds_read_b128 %[t0], %[a0] offset:4096\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t0], %[a2] offset:4096\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
-      "ds_read_b128 %[t1], %[a1] offset:4096\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t1], %[a3] offset:4096\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
-      "ds_read_b128 %[t2], %[a2] offset:4096\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t2], %[a0] offset:5120\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
-      "ds_read_b128 %[t3], %[a3] offset:4096\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q4], %[s]\n"
-      "ds_read_b128 %[t0], %[a0] offset:5120\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q5], %[s]\n"
-      "ds_read_b128 %[t1], %[a1] offset:5120\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q6], %[s]\n"
-      "ds_read_b128 %[t2], %[a2] offset:5120\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q7], %[s]\n"
-      "ds_read_b128 %[t3], %[a3] offset:5120\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q8], %[s]\n"
+      "ds_read_b128 %[t3], %[a1] offset:5120\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q4], %[s]\n"
+      "ds_read_b128 %[t4], %[a2] offset:5120\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q5], %[s]\n"
+      "ds_read_b128 %[t5], %[a3] offset:5120\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q6], %[s]\n"
       "ds_read_b128 %[t0], %[a0] offset:6144\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q9], %[s]\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q7], %[s]\n"
       "ds_read_b128 %[t1], %[a1] offset:6144\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q10], %[s]\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q8], %[s]\n"
       "ds_read_b128 %[t2], %[a2] offset:6144\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q11], %[s]\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q9], %[s]\n"
       "ds_read_b128 %[t3], %[a3] offset:6144\n"
-      : [s] "+v"(s), [t0] "+v"(t0), [t1] "+v"(t1), [t2] "+v"(t2), [t3] "+v"(t3)
-      : [q0] "v"(qf[12]), [q1] "v"(qf[13]), [q2] "v"(qf[14]), [q3] "v"(qf[15]), [q4] "v"(qf[16]), [q5] "v"(qf[17]), [q6] "v"(qf[18]), [q7] "v"(qf[19]), [q8] "v"(qf[20]), [q9] "v"(qf[21]), [q10] "v"(qf[22]), [q11] "v"(qf[23]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
-      : "memory");
-    asm volatile(
-      "s_waitcnt lgkmcnt(3)\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q10], %[s]\n"
+      "ds_read_b128 %[t4], %[a0] offset:7168\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q11], %[s]\n"
+      "ds_read_b128 %[t5], %[a1] offset:7168\n"
+          : [s] "+v"(s), [t0] "+v"(t0), [t1] "+v"(t1), [t2] "+v"(t2), [t3] "+v"(t3), [t4] "+v"(t4), [t5] "+v"(t5)
+          : [q0] "v"(qf[12]), [q1] "v"(qf[13]), [q2] "v"(qf[14]), [q3] "v"(qf[15]), [q4] "v"(qf[16]), [q5] "v"(qf[17]), [q6] "v"(qf[18]), [q7] "v"(qf[19]), [q8] "v"(qf[20]), [q9] "v"(qf[21]), [q10] "v"(qf[22]), [q11] "v"(qf[23]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
+          : "memory");
+      if (pend_t >= 0) issue_tile(pend_t, pend_buf, 2);
+      asm volatile(
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], %[s]\n"
-      "ds_read_b128 %[t0], %[a0] offset:7168\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t0], %[a2] offset:7168\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
-      "ds_read_b128 %[t1], %[a1] offset:7168\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t1], %[a3] offset:7168\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
-      "ds_read_b128 %[t2], %[a2] offset:7168\n"
-      "s_waitcnt lgkmcnt(3)\n"
+      "ds_read_b128 %[t2], %[b0] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
       "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
-      "ds_read_b128 %[t3], %[a3] offset:7168\n"
+      "ds_read_b128 %[t3], %[b1] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q4], %[s]\n"
+      "ds_read_b128 %[t4], %[b2] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q5], %[s]\n"
+      "ds_read_b128 %[t5], %[b3] offset:0\n"
+      "s_waitcnt lgkmcnt(5)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q6], %[s]\n"
+      "s_waitcnt lgkmcnt(4)\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q7], %[s]\n"
       "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q4], %[s]\n"
-      "ds_read_b128 %[t0], %[b0] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q5], %[s]\n"
-      "ds_read_b128 %[t1], %[b1] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q6], %[s]\n"
-      "ds_read_b128 %[t2], %[b2] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q7], %[s]\n"
-      "ds_read_b128 %[t3], %[b3] offset:0\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q8], %[s]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q8], %[s]\n"
       "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q9], %[s]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q9], %[s]\n"
       "s_waitcnt lgkmcnt(1)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q10], %[s]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q10], %[s]\n"
       "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q11], %[s]\n"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q11], %[s]\n"
       "s_nop 7\n"
       "s_nop 7\n"
       "s_nop 7\n"
-      : [s] "+v"(s), [t0] "+v"(t0), [t1] "+v"(t1), [t2] "+v"(t2), [t3] "+v"(t3)
-      : [q0] "v"(qf[24]), [q1] "v"(qf[25]), [q2] "v"(qf[26]), [q3] "v"(qf[27]), [q4] "v"(qf[28]), [q5] "v"(qf[29]), [q6] "v"(qf[30]), [q7] "v"(qf[31]), [q8] "v"(qf[32]), [q9] "v"(qf[33]), [q10] "v"(qf[34]), [q11] "v"(qf[35]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3), [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3)
-      : "memory");
+          : [s] "+v"(s), [t0] "+v"(t0), [t1] "+v"(t1), [t2] "+v"(t2), [t3] "+v"(t3), [t4] "+v"(t4), [t5] "+v"(t5)
+          : [q0] "v"(qf[24]), [q1] "v"(qf[25]), [q2] "v"(qf[26]), [q3] "v"(qf[27]), [q4] "v"(qf[28]), [q5] "v"(qf[29]), [q6] "v"(qf[30]), [q7] "v"(qf[31]), [q8] "v"(qf[32]), [q9] "v"(qf[33]), [q10] "v"(qf[34]), [q11] "v"(qf[35]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3), [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3)
+          : "memory");
 
     } else {
+      if (pend_t >= 0) issue_tile(pend_t, pend_buf, -1);
       s = f32x16{};
       const unsigned char* ta = sm.a[buf];
       const unsigned char* tb = sm.b[buf];
@@ -610,11 +698,12 @@ void attn_fwd_kernel(const AttnParams p) {
   // ------------------------------------------------------------ main loop
   // Iteration t computes S(t+1) = K(t+1) Q^T, then P(t) V(t) with the
   // softmax of S(t+1) in between, and ends on the one barrier of the
-  // iteration.  Tiles t, t+1 are resident and t+2 is in flight (3 buffers);
+  // iteration.  Tiles t and t+1 are resident, the next NB-2 are in flight;
   // P is double buffered.
+  bool redo = false;
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
-      if (!sm.redo) break;   // workgroup-uniform: read after a barrier
+      if (!redo) break;      // workgroup-uniform
       m_ref = m_run;         // exact row max: every weight is <= 1
       l_part = 0.f;
       l_rnd = 0.f;
@@ -625,36 +714,40 @@ void attn_fwd_kernel(const AttnParams p) {
       for (int j = 0; j < NDVB; ++j) O[rb][j] = f32x16{};
 
     if (n_tiles > 0) {
-      issue_tile(0, 0);
-      if (n_tiles > 1) issue_tile(1, 1);
-      wait_vmem();
+      const int pre = min(n_tiles, NB);
+      for (int u = 0; u < pre; ++u) issue_tile(u, u, -1);
+      wait_tiles<KI>(pre - min(pre, 2));   // tiles 0 and 1 have landed
       __syncthreads();
       {
         float x[16];
-        scores(qk(0), 0, true, x);
+        scores(qk(0, -1, 0), 0, true, x);
         weights(x, 0);
       }
-      if (n_tiles > 2) issue_tile(2, 2);
       __syncthreads();
       int buf = 0;
       for (int t = 0; t < n_tiles; ++t) {
-        const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+        const int nbuf = buf == NB - 1 ? 0 : buf + 1;
         const bool live = t + 1 < n_tiles;
         f32x16 s = f32x16{};
-        if (live) s = qk(nbuf);
+        if (live) s = qk(nbuf, -1, 0);
         float x[16];
         scores(s, t + 1, live, x);
         pv(buf, t & 1);
         weights(x, (t + 1) & 1);
-        wait_vmem();
+        // tile t+2 must have landed; copies of later tiles may stay in flight
+        wait_tiles<KI>(min(n_tiles - 1, t + NB - 1) - (t + 2));
         __syncthreads();
-        if (t + 3 < n_tiles) issue_tile(t + 3, buf);
+        // buffer `buf` is free now: copy tile t + NB into it
+        if (t + NB < n_tiles) issue_tile(t + NB, buf, -1);
         buf = nbuf;
       }
     }
     if (pass == 0) {
-      if (__ballot(over) != 0ull && lane == 0) sm.redo = 1;
+      // the P buffers are idle now: their space carries the overflow flags
+      const bool any = __ballot(over) != 0ull;
+      if (lane == 0) sm.epi.flag[w] = any;
       __syncthreads();
+      redo = (sm.epi.flag[0] | sm.epi.flag[1] | sm.epi.flag[2] | sm.epi.flag[3]) != 0;
     }
   }
 
@@ -682,8 +775,8 @@ void attn_fwd_kernel(const AttnParams p) {
       wc = eb / z * inv;
     }
     if (h == 0) {
-      sm.wprev[w * 32 + lr] = wp;
-      sm.wcur[w * 32 + lr] = wc;
+      sm.epi.wprev[w * 32 + lr] = wp;
+      sm.epi.wcur[w * 32 + lr] = wc;
       if (p.lse.p && ok) p.lse.p[cx.b * p.lse.sb + hq * p.lse.sh + tq * p.lse.st] = L;
     }
   }
@@ -692,8 +785,8 @@ void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
   for (int rb = 0; rb < WAVES; ++rb) {
     if (!row_valid(rb)) continue;
-    const float wp = sm.wprev[rb * 32 + lr];
-    const float wc = sm.wcur[rb * 32 + lr];
+    const float wp = sm.epi.wprev[rb * 32 + lr];
+    const float wc = sm.epi.wcur[rb * 32 + lr];
     const int hq = row_head(rb);
     const int64_t tq = qtok(row_query(rb));
     const int64_t oel = cx.b * p.out.sb + hq * p.out.sh + tq * p.out.st;
@@ -747,17 +840,17 @@ void debug_gather_kernel(const GatherParams p) {
   const uint16_t* kA = p.ka.p + p.b * p.ka.sb;
   const uint16_t* kB = p.kb.p + p.b * p.kb.sb;
   const uint32_t stA = (uint32_t)(p.ka.st * 2), stB = (uint32_t)(p.kb.st * 2);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(kA, (uint32_t)(p.Nkv * stA));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(kB, (uint32_t)(p.Nkv * stB));
+  const u32x4 ra = make_rsrc(kA, (uint32_t)(p.Nkv * stA));
+  const u32x4 rb = make_rsrc(kB, (uint32_t)(p.Nkv * stB));
   const int lrow = 8 * w + (lane >> 3);
-  const uint32_t lchunk = (uint32_t)(((lane & 7) ^ swz_f(lane >> 3)) << 4);
+  const uint32_t lchunk = (uint32_t)(((lane & 7) ^ swz_f(lrow & 15)) << 4);
   auto ok = [&](int r) { return r >= 0 && r < p.Nkv; };
   const int n_tiles = (p.K + BN - 1) / BN;
   for (int t = 0; t < n_tiles; ++t) {
     const int k0 = t * BN;
     const int ix = (k0 + lrow < p.K) ? p.idx[k0 + lrow] : -1;
-    copy_rows<NGA>(ra, ta, w, ok(ix) ? (uint32_t)ix * stA + lchunk : kOob);
-    copy_rows<1>(rb, tb, w, ok(ix) ? (uint32_t)ix * stB + lchunk : kOob);
+    copy_rows<NGA>(ra, lds_addr(ta), w, ok(ix) ? (uint32_t)ix * stA + lchunk : kOob);
+    copy_rows<1>(rb, lds_addr(tb), w, ok(ix) ? (uint32_t)ix * stB + lchunk : kOob);
     wait_vmem();
     __syncthreads();
     for (int e = tid; e < BN * (DA + DB) / 8; e += 256) {

@@ -7,6 +7,10 @@
 
 namespace mla {
 
+// Longest top-k index list of the sparse kernel (it stages a query's list in
+// LDS).
+constexpr int kSparseMaxTopk = 4096;
+
 // A row view: element (b, h, t, d) at p[b*sb + h*sh + t*st + d] (strides in
 // elements; bf16 unless a flag says float32, in which case the pointer is
 // reinterpreted).

@@ -124,6 +124,9 @@ def test_sparse_rejects_unsupported_dims(lib):
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
                             1, 16, 1024, 256, 512, 64, 128, 0.07, ctypes.byref(r), None, None)
     assert st == MLA_ERR_UNSUPPORTED
+    st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
+                            1, 16, 1024, 128, 512, 64, 4097, 0.07, ctypes.byref(r), None, None)
+    assert st == MLA_ERR_UNSUPPORTED and "4096" in lib.mla_last_error().decode()
 
 
 def test_binding_raises_with_message(lib):
