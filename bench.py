@@ -108,6 +108,109 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+ATTN_KERNEL = "attn_fwd_kernel<mla::(anonymous namespace)::LatentCfg"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+
+
+def _csvs(folder, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True))
+
+
+def _short_kernel(name):
+    name = name.replace("(anonymous namespace)::", "").replace("mla::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for k, ch in enumerate(name):  # drop the argument list
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            name = name[:k]
+            break
+    return name if len(name) <= 90 else name[:87] + "..."
+
+
+def summarize_stats(folder, out_path, cmd):
+    """Short markdown summary of a `rocprofv3 --kernel-trace --stats
+    --output-format csv` run: launches grouped by kernel and grid size, with the
+    mean duration over all launches and over all but the first (warm-up) one."""
+    import csv
+    files = _csvs(folder, "kernel_trace.csv")
+    if not files:
+        sys.exit(f"no *kernel_trace.csv under {folder}")
+    groups = {}
+    for r in csv.DictReader(open(files[0])):
+        key = (_short_kernel(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in groups.values())
+    lines = ["# Kernel durations: " + os.path.basename(out_path).rsplit(".", 1)[0], "",
+             "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
+             "Launches grouped by kernel and grid (workgroups); durations in microseconds "
+             "from the kernel trace; `steady` leaves out the first launch of the group.", "",
+             "| kernel | workgroups | calls | mean | steady mean | min | max | share |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for (name, wgs), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        steady = d[1:] if len(d) > 1 else d
+        lines.append(f"| `{name}` | {wgs} | {len(d)} | {sum(d) / len(d):.1f} | "
+                     f"{sum(steady) / len(steady):.1f} | {min(d):.1f} | {max(d):.1f} | "
+                     f"{100 * sum(d) / total:.1f}% |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter_means(folder, counter):
+    """Mean value of `counter` per dispatch of each kernel (rocprofv3 csv)."""
+    import csv
+    files = _csvs(folder, "counter_collection.csv")
+    if not files:
+        sys.exit(f"no *counter_collection.csv under {folder}")
+    per = {}
+    for r in csv.DictReader(open(files[0])):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    means = {}
+    for (name, _), v in per.items():
+        means.setdefault(name, []).append(v)
+    return {k: sum(v) / len(v) for k, v in means.items()}
+
+
+def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
+    """HBM bytes per launch of the attention kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) scaled by what they read for a plain 1 GiB device copy
+    in the same run; written with the hash of the kernel source it was taken
+    on, so that a later kernel change makes bench.py report null."""
+    def pick(means, key):
+        hits = [v for k, v in means.items() if key in k]
+        if not hits:
+            sys.exit(f"kernel {key!r} not found; kernels: {list(means)}")
+        return hits[0]
+    fm, wm = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    f_attn, w_attn = pick(fm, ATTN_KERNEL), pick(wm, ATTN_KERNEL)
+    f_copy, w_copy = pick(fm, COPY_KERNEL), pick(wm, COPY_KERNEL)
+    f_scale = COPY_BYTES / (f_copy * 1024.0)   # the copy reads COPY_BYTES
+    w_scale = COPY_BYTES / (w_copy * 1024.0)   # and writes COPY_BYTES
+    fetch_b = f_attn * 1024.0 * f_scale
+    write_b = w_attn * 1024.0 * w_scale
+    res = {"kernel": "attn_fwd_kernel<LatentCfg, LATENT>",
+           "workload": "DeepSeek-V3-shaped absorbed MLA prefill, causal, B=1 H=128 N=8192",
+           "kernel_sha256_16": kernel_hash(),
+           "fetch_kib_raw": round(f_attn, 1), "write_kib_raw": round(w_attn, 1),
+           "copy_1GiB_fetch_kib_raw": round(f_copy, 1), "copy_1GiB_write_kib_raw": round(w_copy, 1),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
+           "bytes_per_launch": int(fetch_b + write_b),
+           "cmd_fetch": cmd_fetch, "cmd_write": cmd_write}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,7 +220,21 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one plain device copy of 1 GiB (HBM counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="DIR",
+                    help="write a markdown summary of a rocprofv3 --stats csv run to --out, then exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM traffic summary from FETCH_SIZE / WRITE_SIZE csv runs, then exit")
+    ap.add_argument("--out", help="output file of --summarize-stats")
+    ap.add_argument("--cmd", nargs="*", default=[],
+                    help="the profiling command(s) the summary came from, recorded in it")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.out, " ".join(args.cmd))
+        return
+    if args.summarize_traffic:
+        cf, cw = (args.cmd + ["", ""])[:2]
+        summarize_traffic(*args.summarize_traffic, cf, cw)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
               f"multi-GPU path; the ring across GPUs is design-only.", file=sys.stderr)
