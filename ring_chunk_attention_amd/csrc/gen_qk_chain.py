@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Writes mla_qk_chain.inc: the 576-wide Q.K MFMA chain of the attention
+kernel as inline asm, optionally with the softmax of the previous key tile
+interleaved into it.
+
+    python3 gen_qk_chain.py            # rewrite mla_qk_chain.inc beside this file
+    python3 gen_qk_chain.py --check    # exit 1 if the file is out of date
+
+Why asm: the chain's accumulator must stay in VGPRs (the output accumulators
+own the AGPRs), the K fragments must stream from LDS a fixed distance ahead
+of the MFMA that uses them, and the softmax VALU work has to sit between the
+MFMAs.  With one wave per SIMD, an MFMA leaves room for only a few
+independent VALU instructions before the next one is due (about four adds,
+or two or three exponentials); the compiler neither keeps the accumulator in
+VGPRs nor spreads the softmax that way.
+
+The chain: 36 k-steps of v_mfma_f32_32x32x16_bf16, S^T += K_c Q_c^T, k-steps
+0..31 from the 512-column sub-tile (fragment address a[c%4] + (c/4) KB),
+32..35 from the 64-column sub-tile (b[c-32]).  NBUF fragment registers; the
+read for step c+NBUF goes out right after the MFMA of step c, and
+lgkmcnt(n) waits until at most n LDS operations are outstanding (they
+complete in order; the only others in the block are the two P writes, issued
+after every read).
+
+The softmax of the previous tile's scores x[0..15] (this lane's 16 keys of
+its query row, already masked with -inf where a key is not visible):
+  m     = max(x) over both lane halves (permlane32 swap), times sc;
+  m_run = max(m_run, m); m_ref = m if m_ref is -inf (the row's first visible
+  tile); mu = m_ref, or 0 while it is still -inf;
+  y_i   = exp2(sc * x_i - mu);  l_part += sum y_i (exact);
+  x_k   = bf16 pair (y_2k, y_2k+1) (round to nearest even), k = 0..7;
+  l_rnd += sum of the rounded weights (dot2 with the bf16 pair (1, 1));
+  the two 16-byte P fragments x[0..3] and x[4..7] are written to LDS at
+  paddr and paddr + 1 KB.
+sc > 0 is the score scale in log2 units (x raw) or 1 (x already scaled).
+The scores live in v[XR:XR+15] (a register constraint of the caller), so that
+the asm can name single registers; the last MFMA of the chain writes the new
+scores there, after the softmax has read them and the P writes have gone
+out.
+
+Placement: each softmax instruction goes to the earliest MFMA step at or
+after the steps of the instructions it depends on, within a budget of VALU
+issue time per step.  Where the pair needs wait states (a VCC write before
+v_cndmask reads it, a VGPR write before v_permlane32_swap reads it, a
+transcendental result before its first use, a permlane result before its
+first use, and, to be safe, a VALU result before a P write stores it) the
+consumer goes to a later step, so that the step's waitcnt,
+MFMA and read separate the two.  The block ends with
+24 wait states so that no VALU outside reads the MFMA result too early.
+"""
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+OUT = os.path.join(HERE, "mla_qk_chain.inc")
+
+KS, KSA, NBUF = 36, 32, 6
+XR = 200                       # first register of the score tuple
+NEG_INF = "0xff800000"
+BF16_ONE_PAIR = "0x3f803f80"
+BUDGET = 3.5                   # VALU issue time per MFMA step, in v_add_f32 units
+LAST_STEP = KS - 2             # the softmax is done before the last MFMA
+
+
+def frag(c):
+    """Address operand and byte offset of k-step c's K fragment."""
+    if c < KSA:
+        return f"%[a{c % 4}]", (c // 4) * 1024
+    return f"%[b{c - KSA}]", 0
+
+
+def x(i):
+    return f"v{XR + i}"
+
+
+def softmax_ops():
+    """(name, text, cost, deps) in program order."""
+    ops = []
+
+    def op(name, text, cost=1.0, deps=(), hazard=()):
+        """deps may share a step with the op; hazard deps may not."""
+        ops.append((name, text, cost, tuple((d, 0) for d in deps) + tuple((d, 1) for d in hazard)))
+
+    # tile max of this lane's 16 scores (before the first MFMA, while its K
+    # fragment is on the way: these carry step -1)
+    op("mx", f"v_max3_f32 %[m], {x(0)}, {x(1)}, {x(2)}\n"
+             f"v_max3_f32 %[m], %[m], {x(3)}, {x(4)}\n"
+             f"v_max3_f32 %[m], %[m], {x(5)}, {x(6)}\n"
+             f"v_max3_f32 %[m], %[m], {x(7)}, {x(8)}\n"
+             f"v_max3_f32 %[m], %[m], {x(9)}, {x(10)}\n"
+             f"v_max3_f32 %[m], %[m], {x(11)}, {x(12)}\n"
+             f"v_max3_f32 %[m], %[m], {x(13)}, {x(14)}\n"
+             f"v_max_f32 %[m], %[m], {x(15)}\n"
+             f"v_mov_b32 %[tmp], %[m]", 0.0)
+    # the other lane half (lane l +- 32 holds the row's other 16 keys)
+    op("swap", "v_permlane32_swap_b32 %[m], %[tmp]", 2.0, hazard=["mx"])
+    op("mxx", "v_max_f32 %[m], %[m], %[tmp]\n"
+              "v_mul_f32 %[m], %[sc], %[m]\n"
+              "v_max_f32 %[mrun], %[mrun], %[m]\n"
+              f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]", 3.5, hazard=["swap"])
+    op("mref", "v_cndmask_b32 %[mref], %[mref], %[m], vcc\n"
+               f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]", 2.0, hazard=["mxx"])
+    op("mu", "v_cndmask_b32_e64 %[mu], %[mref], 0, vcc", 1.0, hazard=["mref"])
+    for j in range(16):
+        op(f"fma{j}", f"v_fma_f32 {x(j)}, {x(j)}, %[sc], -%[mu]", 1.0, ["mu"])
+        op(f"exp{j}", f"v_exp_f32 {x(j)}, {x(j)}", 1.6, [f"fma{j}"])
+        op(f"add{j}", f"v_add_f32 %[lp], %[lp], {x(j)}", 1.0, [f"add{j - 1}"] if j else [], hazard=[f"exp{j}"])
+        if j % 2 == 1:
+            k = j // 2
+            # pair k -> x[k]: after both adds (they read the fp32 values), and
+            # after pair k/2, which reads x[k]
+            deps = [f"add{j - 1}", f"add{j}"] + ([f"cvt{k // 2}"] if k else [])
+            op(f"cvt{k}", f"v_cvt_pk_bf16_f32 {x(k)}, {x(j - 1)}, {x(j)}", 1.0, deps,
+               hazard=[f"exp{j - 1}", f"exp{j}"])
+            op(f"dot{k}", f"v_dot2c_f32_bf16 %[lr], {BF16_ONE_PAIR}, {x(k)}", 3.5,
+               [f"cvt{k}"] + ([f"dot{k - 1}"] if k else []))
+    op("wr", f"ds_write_b128 %[pa], v[{XR}:{XR + 3}]\n"
+             f"ds_write_b128 %[pa], v[{XR + 4}:{XR + 7}] offset:1024", 1.0,
+       hazard=[f"cvt{k}" for k in range(8)])
+    return ops
+
+
+def schedule():
+    """Step of each softmax op (see the module doc)."""
+    step, load = {}, {}
+    for name, _, cost, deps in softmax_ops():
+        if name == "mx":
+            step[name] = -1
+            continue
+        s = max(step[d] + hz for d, hz in deps)
+        while load.get(s, 0.0) + cost > BUDGET and s < LAST_STEP:
+            s += 1
+        if s > LAST_STEP:
+            raise SystemExit(f"softmax does not fit before the last MFMA ({name})")
+        step[name] = s
+        load[s] = load.get(s, 0.0) + cost
+    return step
+
+
+def chain(with_softmax):
+    slots = {}
+    if with_softmax:
+        st = schedule()
+        for name, text, _, _ in softmax_ops():
+            slots.setdefault(st[name], []).extend(text.split("\n"))
+    acc = "%[s]"
+    lines = ["s_waitcnt lgkmcnt(0)"]
+    for c in range(NBUF):
+        a, o = frag(c)
+        lines.append(f"ds_read_b128 %[t{c % NBUF}], {a} offset:{o}")
+    lines += slots.get(-1, [])
+    writes_out = 0   # P writes issued (they count in lgkmcnt after the reads)
+    for c in range(KS):
+        pending = min(NBUF - 1, KS - 1 - c)
+        lines.append(f"s_waitcnt lgkmcnt({pending + writes_out})")
+        src_c = "0" if c == 0 else acc
+        dst = f"v[{XR}:{XR + 15}]" if (with_softmax and c == KS - 1) else acc
+        lines.append(f"v_mfma_f32_32x32x16_bf16 {dst}, %[t{c % NBUF}], %[q{c}], {src_c}")
+        if c + NBUF < KS:
+            a, o = frag(c + NBUF)
+            lines.append(f"ds_read_b128 %[t{c % NBUF}], {a} offset:{o}")
+        for l in slots.get(c, []):
+            lines.append(l)
+            if l.startswith("ds_write"):
+                writes_out += 1
+    lines += ["s_nop 7", "s_nop 7", "s_nop 7"]
+    return lines
+
+
+def emit_function(name, with_softmax):
+    lines = chain(with_softmax)
+    body = "\n".join(f'      "{l}\\n"' for l in lines)
+    outs = [f'[t{k}] "=&v"(t{k})' for k in range(NBUF)]
+    ins = [f'[q{c}] "v"(qf[{c}])' for c in range(KS)]
+    ins += [f'[a{k}] "v"(a{k})' for k in range(4)] + [f'[b{k}] "v"(b{k})' for k in range(4)]
+    params = "const bf16x8* qf, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,\n" \
+             "    uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3"
+    pre = "  u32x4 t0, t1, t2, t3, t4, t5;\n"
+    if with_softmax:
+        params = "f32x16& x, " + params + \
+            ",\n    float sc, float& m_ref, float& m_run, float& l_part, float& l_rnd, uint32_t paddr"
+        outs = ['[s] "=&v"(s)', f'[x] "+{{v[{XR}:{XR + 15}]}}"(x)'] + outs
+        outs += ['[mref] "+v"(m_ref)', '[mrun] "+v"(m_run)', '[lp] "+v"(l_part)', '[lr] "+v"(l_rnd)']
+        outs += ['[m] "=&v"(m)', '[tmp] "=&v"(tmp)', '[mu] "=&v"(mu)']
+        ins += ['[sc] "s"(sc)', '[pa] "v"(paddr)']
+        clobbers = '"vcc", "memory"'
+        pre += "  f32x16 s;\n  float m, tmp, mu;\n"
+    else:
+        params = "f32x16& s, " + params
+        outs = ['[s] "=&v"(s)'] + outs
+        clobbers = '"memory"'
+    return (f"__device__ __forceinline__ void {name}({params}) {{\n{pre}"
+            f"  asm volatile(\n{body}\n"
+            f"      : {', '.join(outs)}\n"
+            f"      : {', '.join(ins)}\n"
+            f"      : {clobbers});\n}}\n")
+
+
+def render():
+    head = ("// Generated by gen_qk_chain.py from its description of the chain; do not\n"
+            "// edit by hand (rerun the script).  Included by mla_attn.hip inside its\n"
+            "// anonymous namespace, after the vector typedefs.\n\n")
+    return (head
+            + "// S^T = K Q^T over the 576 columns of one key tile.\n"
+            + emit_function("qk_chain", False) + "\n"
+            + "// The same chain with the softmax of the previous tile's scores x\n"
+            + "// interleaved (P fragments to LDS at paddr, row stats updated in\n"
+            + "// place); x returns the new scores.\n"
+            + emit_function("qk_chain_softmax", True))
+
+
+def main():
+    text = render()
+    if "--check" in sys.argv:
+        cur = open(OUT).read() if os.path.exists(OUT) else ""
+        if cur != text:
+            print(f"{OUT} is out of date; rerun {os.path.basename(__file__)}")
+            sys.exit(1)
+        return
+    with open(OUT, "w") as f:
+        f.write(text)
+
+
+if __name__ == "__main__":
+    main()

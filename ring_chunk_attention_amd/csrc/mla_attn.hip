@@ -45,6 +45,8 @@
 
 #include <math.h>
 
+#include <utility>
+
 namespace mla {
 namespace {
 
@@ -106,8 +108,10 @@ template <class C, bool SP, int NB>
 struct Smem {
   static constexpr int ATILE = BN * C::DA * 2, BTILE = BN * DB * 2;
   static constexpr int VTILE = C::VLAT ? 0 : BN * C::DV * 2;
-  alignas(16) unsigned char a[NB][ATILE];
-  alignas(16) unsigned char b[NB][BTILE];
+  // 1 KB aligned (the tiles are multiples of 1 KB): a fragment address
+  // differs from its k-step-0 neighbour only in bits 5-6 (see frag_addrs)
+  alignas(1024) unsigned char a[NB][ATILE];
+  alignas(1024) unsigned char b[NB][BTILE];
   alignas(16) unsigned char v[NB][VTILE];
   alignas(16) int idx[SP ? KMAX_IDX : 0];            // sparse: the query's index list
   union {
@@ -201,6 +205,18 @@ __device__ __forceinline__ void copy_rows(const u32x4& r, uint32_t tile, int w, 
   }
 }
 
+#include "mla_qk_chain.inc"
+
+// f(integral_constant<int, I>) for I = 0..N-1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int N>
@@ -260,6 +276,9 @@ void attn_fwd_kernel(const AttnParams p) {
   // key-tile buffers: four let a tile's copy run two iterations ahead of its
   // use (the sparse form keeps the index list in LDS instead of a fourth)
   constexpr int NB = SP ? 3 : 4;
+  // the latent form runs the softmax of tile t+1 inside the Q.K chain of
+  // tile t+2 (see the main loop), the others compute it beside P.V
+  constexpr bool SM_IN_QK = MODE == LATENT;
   static_assert(KS - KSA == 4, "second part is 64 columns");
   static_assert(NB - 2 <= 2, "wait_tiles covers at most two tiles in flight");
 
@@ -377,57 +396,54 @@ void attn_fwd_kernel(const AttnParams p) {
   const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]);
   const uint32_t lds_v = C::VLAT ? lds_a : lds_addr(&sm.v[0][0]);
 
-  // Issue the copies of tile t into buffer buf.  part < 0: all of them;
-  // part 0, 1, 2 (the 576-wide form): about a third each, so that the copies
-  // can be spread over the Q.K chain instead of queueing up at once.
-  auto issue_tile = [&](int t, int buf, int part) {
+  // Copies of one key tile: KI wave instructions, one per 64-column group of
+  // each sub-tile (A groups, then the B sub-tile, then the V groups).  The
+  // sources are worked out once per tile (tile_src); issue_copy<I> issues
+  // instruction I, so that the copies can be spread over the MFMA stream.
+  struct TileSrc {
+    u32x4 ra, rb, rv;
+    uint32_t oa, ob, la, lb, lv;
+  };
+  auto tile_src = [&](int t, int buf) __attribute__((always_inline)) -> TileSrc {
+    TileSrc c;
     const int64_t k0 = (int64_t)t * BN;
-    const uint32_t la = lds_a + buf * Smem<C, SP, NB>::ATILE;
-    const uint32_t lb = lds_b + buf * Smem<C, SP, NB>::BTILE;
-    u32x4 ra, rb;
-    uint32_t oa, ob;
+    c.la = lds_a + buf * Smem<C, SP, NB>::ATILE;
+    c.lb = lds_b + buf * Smem<C, SP, NB>::BTILE;
+    c.lv = lds_v + buf * Smem<C, SP, NB>::VTILE;
     if constexpr (SP) {
       const int r = (int)k0 + lrow;
       const int ix = r < p.topk ? sm.idx[r] : -1;
       const bool ok = idx_ok(ix);
-      ra = make_rsrc(kA, (uint32_t)(p.Nkv * stA));
-      rb = make_rsrc(kB, (uint32_t)(p.Nkv * stB));
-      oa = ok ? (uint32_t)ix * stA + lchunk : kOob;
-      ob = ok ? (uint32_t)ix * stB + lchunk : kOob;
+      c.ra = make_rsrc(kA, (uint32_t)(p.Nkv * stA));
+      c.rb = make_rsrc(kB, (uint32_t)(p.Nkv * stB));
+      c.oa = ok ? (uint32_t)ix * stA + lchunk : kOob;
+      c.ob = ok ? (uint32_t)ix * stB + lchunk : kOob;
     } else {
       // the buffer is the tile's rows [k0, min(k0 + BN, kv_len)); rows past it read zeros
       const uint32_t nrows = (uint32_t)min<int64_t>(BN, cx.kv_len - k0);
-      ra = make_rsrc(kA + k0 * p.ka.st, nrows * stA);
-      rb = make_rsrc(kB + k0 * p.kb.st, nrows * stB);
-      oa = voA;
-      ob = voB;
-      if constexpr (!C::VLAT) {
-        if (part <= 0)
-          copy_rows<NGV>(make_rsrc(vS + k0 * p.v.st, nrows * stV), lds_v + buf * Smem<C, SP, NB>::VTILE, w, voV);
-      }
+      c.ra = make_rsrc(kA + k0 * p.ka.st, nrows * stA);
+      c.rb = make_rsrc(kB + k0 * p.kb.st, nrows * stB);
+      if constexpr (!C::VLAT) c.rv = make_rsrc(vS + k0 * p.v.st, nrows * stV);
+      c.oa = voA;
+      c.ob = voB;
     }
-    if constexpr (NGA == 8) {
-      if (part < 0 || part == 0) copy_rows<NGA, 0, 3>(ra, la, w, oa);
-      if (part < 0 || part == 1) copy_rows<NGA, 3, 6>(ra, la, w, oa);
-      if (part < 0 || part == 2) {
-        copy_rows<NGA, 6, 8>(ra, la, w, oa);
-        copy_rows<1>(rb, lb, w, ob);
-      }
-    } else {
-      if (part <= 0) {
-        copy_rows<NGA>(ra, la, w, oa);
-        copy_rows<1>(rb, lb, w, ob);
-      }
-    }
+    return c;
+  };
+  auto issue_copy = [&](const TileSrc& c, auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i < NGA) copy_rows<NGA, i, i + 1>(c.ra, c.la, w, c.oa);
+    else if constexpr (i == NGA) copy_rows<1>(c.rb, c.lb, w, c.ob);
+    else copy_rows<NGV, i - NGA - 1, i - NGA>(c.rv, c.lv, w, voV);
+  };
+  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
+    const TileSrc c = tile_src(t, buf);
+    unroll<KI>([&](auto I) __attribute__((always_inline)) { issue_copy(c, I); });
   };
 
   // LDS byte offsets of this lane's K fragments (k-step c: + (c/4) KB)
-  int koffA[4], koffB[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    koffA[j] = tile_off(NGA, lr, 2 * j + h);
-    koffB[j] = tile_off(1, lr, 2 * j + h);
-  }
+  // (k-step c: chunk 2(c%4) + h of column group c/4; the chunk index is
+  // XORed with the row swizzle, so k-step c%4 = k flips bits 5-6 by k)
+  const int koffA = tile_off(NGA, lr, h), koffB = tile_off(1, lr, h);
 
   const int n_tiles = (int)((cx.kv_end + BN - 1) / BN);
   // key rows visible to this lane's row: [0, vis_end), relative to the
@@ -442,7 +458,7 @@ void attn_fwd_kernel(const AttnParams p) {
       we = min<int64_t>(we, max<int64_t>(0, wave_pos - p.kv_offset + 1));
     }
     vis_end = (int32_t)ve;        // <= kv_len, which fits 32 bits
-    wave_vis_end = (int32_t)we;   // visible to every row of the wave
+    wave_vis_end = __builtin_amdgcn_readfirstlane((int32_t)we);  // visible to every row of the wave
   }
 
   f32x16 O[WAVES][NDVB];
@@ -453,160 +469,29 @@ void attn_fwd_kernel(const AttnParams p) {
   bool over = false;
 
   // S^T = K Q^T for one tile (lane: query row lr; keys (r/4)*8 + 4h + r%4)
-  // pend_t >= 0: copies of tile pend_t into buffer pend_buf to issue along
-  // the way
-  auto qk = [&](int buf, int pend_t, int pend_buf) -> f32x16 {
+  // LDS byte addresses of this lane's K fragments in tile buffer `buf`
+  auto frag_addrs = [&](int buf, uint32_t* a, uint32_t* b) __attribute__((always_inline)) {
+    const uint32_t ta = lds_a + buf * Smem<C, SP, NB>::ATILE, tb = lds_b + buf * Smem<C, SP, NB>::BTILE;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[k] = (ta + koffA) ^ (uint32_t)(k << 5);
+      b[k] = (tb + koffB) ^ (uint32_t)(k << 5);
+    }
+  };
+  auto qk = [&](int buf) __attribute__((always_inline)) -> f32x16 {
     f32x16 s;
     if constexpr (KS == 36) {
-      // The 576-wide contraction as one MFMA chain written out by hand: the
-      // accumulator stays in VGPRs (the O accumulators own the AGPRs) and
-      // the K fragments stream through six registers, read from LDS five
-      // k-steps ahead of the MFMA that uses them (LDS latency under load is
-      // well above three MFMA issue intervals).  lgkmcnt(n) waits until
-      // at most n of the reads issued so far are outstanding (LDS reads
-      // complete in order).  The trailing nops cover the MFMA result ->
-      // VALU read hazard that the compiler cannot see through the asm.
-      const uint32_t ta = lds_a + buf * Smem<C, SP, NB>::ATILE, tb = lds_b + buf * Smem<C, SP, NB>::BTILE;
-      const uint32_t a0 = ta + koffA[0], a1 = ta + koffA[1], a2 = ta + koffA[2], a3 = ta + koffA[3];
-      const uint32_t b0 = tb + koffB[0], b1 = tb + koffB[1], b2 = tb + koffB[2], b3 = tb + koffB[3];
-      u32x4 t0, t1, t2, t3, t4, t5;
-      if (pend_t >= 0) issue_tile(pend_t, pend_buf, 0);
-      asm volatile(
-      "s_waitcnt lgkmcnt(0)\n"
-      "ds_read_b128 %[t0], %[a0] offset:0\n"
-      "ds_read_b128 %[t1], %[a1] offset:0\n"
-      "ds_read_b128 %[t2], %[a2] offset:0\n"
-      "ds_read_b128 %[t3], %[a3] offset:0\n"
-      "ds_read_b128 %[t4], %[a0] offset:1024\n"
-      "ds_read_b128 %[t5], %[a1] offset:1024\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], 0\n"
-      "ds_read_b128 %[t0], %[a2] offset:1024\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
-      "ds_read_b128 %[t1], %[a3] offset:1024\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
-      "ds_read_b128 %[t2], %[a0] offset:2048\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
-      "ds_read_b128 %[t3], %[a1] offset:2048\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q4], %[s]\n"
-      "ds_read_b128 %[t4], %[a2] offset:2048\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q5], %[s]\n"
-      "ds_read_b128 %[t5], %[a3] offset:2048\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q6], %[s]\n"
-      "ds_read_b128 %[t0], %[a0] offset:3072\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q7], %[s]\n"
-      "ds_read_b128 %[t1], %[a1] offset:3072\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q8], %[s]\n"
-      "ds_read_b128 %[t2], %[a2] offset:3072\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q9], %[s]\n"
-      "ds_read_b128 %[t3], %[a3] offset:3072\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q10], %[s]\n"
-      "ds_read_b128 %[t4], %[a0] offset:4096\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q11], %[s]\n"
-      "ds_read_b128 %[t5], %[a1] offset:4096\n"
-          : [s] "=&v"(s), [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [t4] "=&v"(t4), [t5] "=&v"(t5)
-          : [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
-          : "memory");
-      if (pend_t >= 0) issue_tile(pend_t, pend_buf, 1);
-      asm volatile(
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], %[s]\n"
-      "ds_read_b128 %[t0], %[a2] offset:4096\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
-      "ds_read_b128 %[t1], %[a3] offset:4096\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
-      "ds_read_b128 %[t2], %[a0] offset:5120\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
-      "ds_read_b128 %[t3], %[a1] offset:5120\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q4], %[s]\n"
-      "ds_read_b128 %[t4], %[a2] offset:5120\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q5], %[s]\n"
-      "ds_read_b128 %[t5], %[a3] offset:5120\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q6], %[s]\n"
-      "ds_read_b128 %[t0], %[a0] offset:6144\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q7], %[s]\n"
-      "ds_read_b128 %[t1], %[a1] offset:6144\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q8], %[s]\n"
-      "ds_read_b128 %[t2], %[a2] offset:6144\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q9], %[s]\n"
-      "ds_read_b128 %[t3], %[a3] offset:6144\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q10], %[s]\n"
-      "ds_read_b128 %[t4], %[a0] offset:7168\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q11], %[s]\n"
-      "ds_read_b128 %[t5], %[a1] offset:7168\n"
-          : [s] "+v"(s), [t0] "+v"(t0), [t1] "+v"(t1), [t2] "+v"(t2), [t3] "+v"(t3), [t4] "+v"(t4), [t5] "+v"(t5)
-          : [q0] "v"(qf[12]), [q1] "v"(qf[13]), [q2] "v"(qf[14]), [q3] "v"(qf[15]), [q4] "v"(qf[16]), [q5] "v"(qf[17]), [q6] "v"(qf[18]), [q7] "v"(qf[19]), [q8] "v"(qf[20]), [q9] "v"(qf[21]), [q10] "v"(qf[22]), [q11] "v"(qf[23]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3)
-          : "memory");
-      if (pend_t >= 0) issue_tile(pend_t, pend_buf, 2);
-      asm volatile(
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q0], %[s]\n"
-      "ds_read_b128 %[t0], %[a2] offset:7168\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q1], %[s]\n"
-      "ds_read_b128 %[t1], %[a3] offset:7168\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q2], %[s]\n"
-      "ds_read_b128 %[t2], %[b0] offset:0\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q3], %[s]\n"
-      "ds_read_b128 %[t3], %[b1] offset:0\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q4], %[s]\n"
-      "ds_read_b128 %[t4], %[b2] offset:0\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q5], %[s]\n"
-      "ds_read_b128 %[t5], %[b3] offset:0\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t0], %[q6], %[s]\n"
-      "s_waitcnt lgkmcnt(4)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t1], %[q7], %[s]\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t2], %[q8], %[s]\n"
-      "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t3], %[q9], %[s]\n"
-      "s_waitcnt lgkmcnt(1)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t4], %[q10], %[s]\n"
-      "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], %[t5], %[q11], %[s]\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-          : [s] "+v"(s), [t0] "+v"(t0), [t1] "+v"(t1), [t2] "+v"(t2), [t3] "+v"(t3), [t4] "+v"(t4), [t5] "+v"(t5)
-          : [q0] "v"(qf[24]), [q1] "v"(qf[25]), [q2] "v"(qf[26]), [q3] "v"(qf[27]), [q4] "v"(qf[28]), [q5] "v"(qf[29]), [q6] "v"(qf[30]), [q7] "v"(qf[31]), [q8] "v"(qf[32]), [q9] "v"(qf[33]), [q10] "v"(qf[34]), [q11] "v"(qf[35]), [a0] "v"(a0), [a1] "v"(a1), [a2] "v"(a2), [a3] "v"(a3), [b0] "v"(b0), [b1] "v"(b1), [b2] "v"(b2), [b3] "v"(b3)
-          : "memory");
-
+      uint32_t a[4], b[4];
+      frag_addrs(buf, a, b);
+      qk_chain(s, qf, a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
     } else {
-      if (pend_t >= 0) issue_tile(pend_t, pend_buf, -1);
       s = f32x16{};
       const unsigned char* ta = sm.a[buf];
       const unsigned char* tb = sm.b[buf];
 #pragma unroll
       for (int c = 0; c < KS; ++c) {
-        const bf16x8 kf = c < KSA ? *reinterpret_cast<const bf16x8*>(ta + koffA[c & 3] + (c >> 2) * 1024)
-                                  : *reinterpret_cast<const bf16x8*>(tb + koffB[c - KSA]);
+        const bf16x8 kf = c < KSA ? *reinterpret_cast<const bf16x8*>(ta + (koffA ^ ((c & 3) << 5)) + (c >> 2) * 1024)
+                                  : *reinterpret_cast<const bf16x8*>(tb + (koffB ^ ((c - KSA) << 5)));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s, 0, 0, 0);
       }
     }
@@ -615,7 +500,7 @@ void attn_fwd_kernel(const AttnParams p) {
 
   // softmax, first half: scale to log2 units, mask, row max, reference max.
   // `live` false: no tile (all scores masked).
-  auto scores = [&](const f32x16& s, int t, bool live, float* x) {
+  auto scores = [&](const f32x16& s, int t, bool live, float* x) __attribute__((always_inline)) {
     const int k0 = t * BN;
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = s[r] * p.scale_log2;
@@ -652,54 +537,95 @@ void attn_fwd_kernel(const AttnParams p) {
     over |= m_run > m_ref + TAU;
   };
 
-  // softmax, second half: weights, row sums, bf16 P^T fragments to LDS
-  auto weights = [&](const float* x, int pb) {
-    const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-    f32x8 p0, p1;
+  // softmax, second half, one quarter (4 of the lane's 16 scores) at a time,
+  // so that it can be spread over the P.V MFMAs: weights against the
+  // reference mu, row sums, and bf16 P^T fragments to LDS (a 16-key half
+  // once its two quarters are done).  The exact row sum gives the LSE; the
+  // sum of the weights as the P.V product sees them (rounded to bf16)
+  // normalises O, so its weights sum to one.
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  auto weights_q = [&](const float* x, int pb, float mu, bf16x4* bq, auto Q) __attribute__((always_inline)) {
+    constexpr int q = decltype(Q)::value;
+    f32x4 pq;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      p0[r] = __builtin_amdgcn_exp2f(x[r] - mu);
-      p1[r] = __builtin_amdgcn_exp2f(x[r + 8] - mu);
+    for (int r = 0; r < 4; ++r) pq[r] = __builtin_amdgcn_exp2f(x[4 * q + r] - mu);
+    bq[q] = __builtin_convertvector(pq, bf16x4);
+    l_part += (pq[0] + pq[1]) + (pq[2] + pq[3]);
+    l_rnd += ((float)bq[q][0] + (float)bq[q][1]) + ((float)bq[q][2] + (float)bq[q][3]);
+    if constexpr (q & 1) {
+      const bf16x8 b = {bq[q - 1][0], bq[q - 1][1], bq[q - 1][2], bq[q - 1][3], bq[q][0], bq[q][1], bq[q][2], bq[q][3]};
+      *reinterpret_cast<bf16x8*>(sm.p[pb][w][q >> 1] + lane * 16) = b;
     }
-    const bf16x8 b0 = __builtin_convertvector(p0, bf16x8);
-    const bf16x8 b1 = __builtin_convertvector(p1, bf16x8);
-    // the exact row sum gives the LSE; the sum of the weights as the P.V
-    // product sees them (rounded to bf16) normalises O, so its weights sum to one
-    float ps = 0.f, pr = 0.f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      ps += p0[r] + p1[r];
-      pr += (float)b0[r] + (float)b1[r];
-    }
-    l_part += ps;
-    l_rnd += pr;
-    *reinterpret_cast<bf16x8*>(sm.p[pb][w][0] + lane * 16) = b0;
-    *reinterpret_cast<bf16x8*>(sm.p[pb][w][1] + lane * 16) = b1;
   };
+  auto mu_of = [&]() __attribute__((always_inline)) { return m_ref == -INFINITY ? 0.f : m_ref; };
 
   // O^T += V^T P^T over this wave's value columns for all 128 rows
-  auto pv = [&](int buf, int pb) {
+  // hook(integral_constant<int, g>) runs after MFMA group g (one value-column
+  // block of one 16-key half), g = 0 .. 2*NDVB-1.  The fragments of group
+  // g+1 are read before the MFMAs of group g: the hook may hold copies into
+  // LDS, which the compiler does not move LDS reads across.
+  auto pv = [&](int buf, int pb, auto&& hook) __attribute__((always_inline)) {
     const unsigned char* vt = C::VLAT ? sm.a[buf] : sm.v[buf];
+    bf16x8 pf[WAVES];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8 pf[WAVES];
+    for (int rb = 0; rb < WAVES; ++rb) pf[rb] = *reinterpret_cast<const bf16x8*>(sm.p[pb][rb][0] + lane * 16);
+    bf16x8 vf = read_vt<NGV>(vt, w * NDVB, 0, lane);
+    unroll<2 * NDVB>([&](auto G) __attribute__((always_inline)) {
+      constexpr int g = decltype(G)::value, c = g / NDVB, j = g % NDVB;
+      bf16x8 vn = vf;
+      if constexpr (g + 1 < 2 * NDVB) vn = read_vt<NGV>(vt, w * NDVB + (g + 1) % NDVB, (g + 1) / NDVB, lane);
 #pragma unroll
-      for (int rb = 0; rb < WAVES; ++rb) pf[rb] = *reinterpret_cast<const bf16x8*>(sm.p[pb][rb][c] + lane * 16);
+      for (int rb = 0; rb < WAVES; ++rb)
+        O[rb][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], O[rb][j], 0, 0, 0);
+      // interleave the VALU work of the previous hook (softmax) with these
+      // MFMAs: the MFMA unit runs each for several VALU issue slots
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int j = 0; j < NDVB; ++j) {
-        const bf16x8 vf = read_vt<NGV>(vt, w * NDVB + j, c, lane);
-#pragma unroll
-        for (int rb = 0; rb < WAVES; ++rb)
-          O[rb][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], O[rb][j], 0, 0, 0);
+      for (int rb = 0; rb < WAVES; ++rb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
+      // and keep the row sums of that work here rather than sunk to the barrier
+      asm volatile("" ::"v"(l_part), "v"(l_rnd));
+      if constexpr (g == NDVB - 1) {
+#pragma unroll
+        for (int rb = 0; rb < WAVES; ++rb) pf[rb] = *reinterpret_cast<const bf16x8*>(sm.p[pb][rb][1] + lane * 16);
+      }
+      hook(G);
+      vf = vn;
+      (void)c;
+    });
+  };
+
+  // Softmax of S(tp) = x to P buffer tp&1 inside the Q.K chain of tile tq;
+  // x returns S(tq).  The chain neither scales nor masks: a tile that needs
+  // a mask (or a scale that is not positive) is scaled and masked here, and
+  // the chain runs with scale 1.
+  auto chain_sm = [&](f32x16& x, int tp, int tq) __attribute__((always_inline)) {
+    if constexpr (KS == 36 && !SP) {
+      const int k0 = tp * BN;
+      const bool mask = k0 + BN > wave_vis_end || !(p.scale_log2 > 0.f);  // wave-uniform
+      float sc = p.scale_log2;
+      if (mask) {
+        const int bound = vis_end - k0 - 4 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r >> 2) * 8 + (r & 3) < bound ? x[r] * p.scale_log2 : -INFINITY;
+        sc = 1.f;
+      }
+      uint32_t a[4], b[4];
+      frag_addrs(tq & (NB - 1), a, b);
+      qk_chain_softmax(x, qf, a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], sc, m_ref, m_run, l_part, l_rnd,
+                       lds_addr(sm.p[tp & 1][w][0]) + lane * 16);
     }
   };
 
   // ------------------------------------------------------------ main loop
   // Iteration t computes S(t+1) = K(t+1) Q^T, then P(t) V(t) with the
   // softmax of S(t+1) in between, and ends on the one barrier of the
-  // iteration.  Tiles t and t+1 are resident, the next NB-2 are in flight;
-  // P is double buffered.
+  // iteration.  Tiles t, t+1 and t+2 are resident (t+2 landed by the end of
+  // the iteration); the copies of tile t+NB-1 go into the buffer tile t-1
+  // left, spread over the P.V MFMAs.  P is double buffered.
+  constexpr int NPV = 2 * NDVB;  // MFMA groups of one P.V
   bool redo = false;
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
@@ -713,36 +639,96 @@ void attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int j = 0; j < NDVB; ++j) O[rb][j] = f32x16{};
 
-    if (n_tiles > 0) {
-      const int pre = min(n_tiles, NB);
-      for (int u = 0; u < pre; ++u) issue_tile(u, u, -1);
-      wait_tiles<KI>(pre - min(pre, 2));   // tiles 0 and 1 have landed
-      __syncthreads();
-      {
-        float x[16];
-        scores(qk(0, -1, 0), 0, true, x);
-        weights(x, 0);
-      }
-      __syncthreads();
-      int buf = 0;
-      for (int t = 0; t < n_tiles; ++t) {
-        const int nbuf = buf == NB - 1 ? 0 : buf + 1;
-        const bool live = t + 1 < n_tiles;
-        f32x16 s = f32x16{};
-        if (live) s = qk(nbuf, -1, 0);
-        float x[16];
-        scores(s, t + 1, live, x);
-        pv(buf, t & 1);
-        weights(x, (t + 1) & 1);
-        // tile t+2 must have landed; copies of later tiles may stay in flight
-        wait_tiles<KI>(min(n_tiles - 1, t + NB - 1) - (t + 2));
+    if constexpr (SM_IN_QK) {
+      // Iteration t: P(t) V(t) with the copies of tile t+3 (into the buffer
+      // tile t-1 left) spread over its MFMAs; then the Q.K chain of tile t+2
+      // with the softmax of S(t+1) inside it, which writes P(t+1); then the
+      // one barrier.  Tiles t..t+2 are resident, t+3 lands by the barrier.
+      // Unrolled twice so that the two score accumulators trade roles
+      // instead of being copied; the last two tiles have no chain.
+      auto pv_copy = [&](int t) __attribute__((always_inline)) {
+        const bool copy = t + NB - 1 < n_tiles;
+        const TileSrc src = tile_src(min(t + NB - 1, n_tiles - 1), (t + NB - 1) & (NB - 1));
+        pv(t & (NB - 1), t & 1, [&](auto G) __attribute__((always_inline)) {
+          constexpr int g = decltype(G)::value;
+          if (copy) {
+            unroll<(g + 1) * KI / NPV - g * KI / NPV>([&](auto I) __attribute__((always_inline)) {
+              issue_copy(src, std::integral_constant<int, g * KI / NPV + decltype(I)::value>{});
+            });
+          }
+        });
+      };
+      // Past the last tile the chain still runs: the scores of tile n_tiles
+      // are all masked (-inf), which leaves the row stats as they are, and
+      // the tile it multiplies is stale and unused.
+      if (n_tiles > 0) {
+        const int pre = min(n_tiles, NB - 1);
+        for (int u = 0; u < pre; ++u) issue_tile(u, u);
+        wait_tiles<KI>(0);
         __syncthreads();
-        // buffer `buf` is free now: copy tile t + NB into it
-        if (t + NB < n_tiles) issue_tile(t + NB, buf, -1);
-        buf = nbuf;
+        f32x16 sc = qk(0);
+        chain_sm(sc, 0, 1);
+        __syncthreads();
+        for (int t = 0; t < n_tiles; ++t) {  // sc = S(t+1)
+          pv_copy(t);
+          chain_sm(sc, t + 1, t + 2);
+          wait_tiles<KI>(0);  // tile t+3
+          __syncthreads();
+        }
+      }
+    } else {
+      if (n_tiles > 0) {
+        const int pre = min(n_tiles, NB - 1);
+        for (int u = 0; u < pre; ++u) issue_tile(u, u);
+        wait_tiles<KI>(pre - min(pre, 2));   // tiles 0 and 1 have landed
+        __syncthreads();
+        {
+          float x[16];
+          scores(qk(0), 0, true, x);
+          const float mu = mu_of();
+          bf16x4 bq[4];
+          unroll<4>([&](auto Q) __attribute__((always_inline)) { weights_q(x, 0, mu, bq, Q); });
+        }
+        __syncthreads();
+        int buf = 0;
+        for (int t = 0; t < n_tiles; ++t) {
+          const int nbuf = buf == NB - 1 ? 0 : buf + 1;
+          const int cbuf = buf == 0 ? NB - 1 : buf - 1;
+          const bool live = t + 1 < n_tiles;
+          f32x16 s = f32x16{};
+          if (live) s = qk(nbuf);
+          float x[16];
+          float mu = 0.f;
+          bf16x4 bq[4];
+          const bool copy = t + NB - 1 < n_tiles;
+          const TileSrc src = tile_src(min(t + NB - 1, n_tiles - 1), cbuf);
+          // P(t) V(t); along the way the copies of tile t+NB-1 and the softmax
+          // of S(t+1): its first half after MFMA group 0, its quarters after
+          // groups NPV/5, 2NPV/5, 3NPV/5 and 4NPV/5
+          pv(buf, t & 1, [&](auto G) __attribute__((always_inline)) {
+            constexpr int g = decltype(G)::value;
+            if (copy) {
+              unroll<(g + 1) * KI / NPV - g * KI / NPV>([&](auto I) __attribute__((always_inline)) {
+                issue_copy(src, std::integral_constant<int, g * KI / NPV + decltype(I)::value>{});
+              });
+            }
+            if constexpr (g == 0) {
+              scores(s, t + 1, live, x);
+              mu = mu_of();
+            }
+            unroll<4>([&](auto Q) __attribute__((always_inline)) {
+              if constexpr ((decltype(Q)::value + 1) * NPV / 5 == g) weights_q(x, (t + 1) & 1, mu, bq, Q);
+            });
+          });
+          // tile t+2 must have landed; the copies of tile t+NB-1 may stay in flight
+          wait_tiles<KI>(min(n_tiles - 1, t + NB - 1) - (t + 2));
+          __syncthreads();
+          buf = nbuf;
+        }
       }
     }
     if (pass == 0) {
+      over |= m_run > m_ref + TAU;  // (the softmax in the Q.K chain tracks only m_run)
       // the P buffers are idle now: their space carries the overflow flags
       const bool any = __ballot(over) != 0ull;
       if (lane == 0) sm.epi.flag[w] = any;
