@@ -29,7 +29,8 @@ its query row, already masked with -inf where a key is not visible):
   tile); mu = m_ref, or 0 while it is still -inf;
   y_i   = exp2(sc * x_i - mu);  l_part += sum y_i (exact);
   x_k   = bf16 pair (y_2k, y_2k+1) (round to nearest even), k = 0..7;
-  l_rnd += sum of the rounded weights (dot2 with the bf16 pair (1, 1));
+  l_rnd += sum of the rounded weights (each half of the pair widened to
+           fp32 by a shift or a mask: v_dot2 runs at a quarter of the rate);
   the two 16-byte P fragments x[0..3] and x[4..7] are written to LDS at
   paddr and paddr + 1 KB.
 sc > 0 is the score scale in log2 units (x raw) or 1 (x already scaled).
@@ -57,7 +58,6 @@ OUT = os.path.join(HERE, "mla_qk_chain.inc")
 KS, KSA, NBUF = 36, 32, 6
 XR = 200                       # first register of the score tuple
 NEG_INF = "0xff800000"
-BF16_ONE_PAIR = "0x3f803f80"
 BUDGET = 3.5                   # VALU issue time per MFMA step, in v_add_f32 units
 LAST_STEP = KS - 2             # the softmax is done before the last MFMA
 
@@ -112,8 +112,11 @@ def softmax_ops():
             deps = [f"add{j - 1}", f"add{j}"] + ([f"cvt{k // 2}"] if k else [])
             op(f"cvt{k}", f"v_cvt_pk_bf16_f32 {x(k)}, {x(j - 1)}, {x(j)}", 1.0, deps,
                hazard=[f"exp{j - 1}", f"exp{j}"])
-            op(f"dot{k}", f"v_dot2c_f32_bf16 %[lr], {BF16_ONE_PAIR}, {x(k)}", 3.5,
-               [f"cvt{k}"] + ([f"dot{k - 1}"] if k else []))
+            op(f"rlo{k}", f"v_lshlrev_b32 %[r0], 16, {x(k)}\n"
+                          f"v_add_f32 %[lr], %[lr], %[r0]", 2.0,
+               [f"cvt{k}"] + ([f"rhi{k - 1}"] if k else []))
+            op(f"rhi{k}", f"v_and_b32 %[r1], 0xffff0000, {x(k)}\n"
+                          f"v_add_f32 %[lr], %[lr], %[r1]", 2.0, [f"rlo{k}"])
     op("wr", f"ds_write_b128 %[pa], v[{XR}:{XR + 3}]\n"
              f"ds_write_b128 %[pa], v[{XR + 4}:{XR + 7}] offset:1024", 1.0,
        hazard=[f"cvt{k}" for k in range(8)])
@@ -128,7 +131,7 @@ def schedule():
             step[name] = -1
             continue
         s = max(step[d] + hz for d, hz in deps)
-        while load.get(s, 0.0) + cost > BUDGET and s < LAST_STEP:
+        while load.get(s, 0.0) > 0.0 and load.get(s, 0.0) + cost > BUDGET and s < LAST_STEP:
             s += 1
         if s > LAST_STEP:
             raise SystemExit(f"softmax does not fit before the last MFMA ({name})")
@@ -181,10 +184,10 @@ def emit_function(name, with_softmax):
             ",\n    float sc, float& m_ref, float& m_run, float& l_part, float& l_rnd, uint32_t paddr"
         outs = ['[s] "=&v"(s)', f'[x] "+{{v[{XR}:{XR + 15}]}}"(x)'] + outs
         outs += ['[mref] "+v"(m_ref)', '[mrun] "+v"(m_run)', '[lp] "+v"(l_part)', '[lr] "+v"(l_rnd)']
-        outs += ['[m] "=&v"(m)', '[tmp] "=&v"(tmp)', '[mu] "=&v"(mu)']
+        outs += ['[m] "=&v"(m)', '[tmp] "=&v"(tmp)', '[mu] "=&v"(mu)', '[r0] "=&v"(r0)', '[r1] "=&v"(r1)']
         ins += ['[sc] "s"(sc)', '[pa] "v"(paddr)']
         clobbers = '"vcc", "memory"'
-        pre += "  f32x16 s;\n  float m, tmp, mu;\n"
+        pre += "  f32x16 s;\n  float m, tmp, mu, r0, r1;\n"
     else:
         params = "f32x16& s, " + params
         outs = ['[s] "=&v"(s)'] + outs
