@@ -199,6 +199,174 @@ def emit_function(name, with_softmax):
             f"      : {clobbers});\n}}\n")
 
 
+
+# ---------------------------------------------------------------------------
+# One whole key-loop step of the shared-latent form in one block: the Q.K
+# chain of tile t+2 (with the softmax of S(t+1) in it) interleaved with the
+# P.V MFMAs of tile t, their LDS reads, and the copies of tile t+3.
+# ---------------------------------------------------------------------------
+TS_NBUF = 4          # K fragment registers of the chain inside the step
+TS_BUDGET = 3.0      # VALU issue time per MFMA slot
+VFA, VFB = 216, 220  # the two V fragment tuples (v[216:219], v[220:223])
+N_PV = 32            # P.V MFMAs: 2 key halves x 4 value blocks x 4 row blocks
+
+
+TS_TAIL = 4          # P.V MFMAs after the last chain step
+
+
+def ts_order():
+    """MFMA slots: P.V and chain MFMAs alternate; the chain ends TS_TAIL P.V
+    MFMAs before the block does, so that the issue of those MFMAs covers the
+    wait states between the last chain MFMA (it writes the new scores over
+    x) and the first VALU read of x after the block."""
+    seq = []
+    n_pair = N_PV - TS_TAIL
+    for i in range(n_pair):
+        seq += [("P", i), ("C", i)]
+    seq += [("C", c) for c in range(n_pair, KS)]
+    seq += [("P", i) for i in range(n_pair, N_PV)]
+    return seq
+
+
+def ts_schedule(nslots):
+    step, load = {}, {}
+    # the P write and the last pack at least two MFMAs before the chain ends
+    last = nslots - TS_TAIL - 3
+    for name, _, cost, deps in softmax_ops():
+        if name == "mx":
+            step[name] = -1
+            continue
+        s = max(step[d] + hz for d, hz in deps)
+        while load.get(s, 0.0) > 0.0 and load.get(s, 0.0) + cost > TS_BUDGET and s < last:
+            s += 1
+        if s > last:
+            raise SystemExit(f"softmax does not fit in the tile step ({name})")
+        step[name] = s
+        load[s] = load.get(s, 0.0) + cost
+    return step
+
+
+def ts_copy_slots(seq):
+    """The nine copies of a tile go out after evenly spaced P.V MFMAs."""
+    pv_slots = [k for k, (kind, _) in enumerate(seq) if kind == "P"]
+    return {pv_slots[(4 * i * N_PV) // (9 * 4) + 1]: i for i in range(9)}
+
+
+def tile_step_lines():
+    seq = ts_order()
+    st = ts_schedule(len(seq))
+    sm_slots = {}
+    for name, text, _, _ in softmax_ops():
+        sm_slots.setdefault(st[name], []).extend(text.split("\n"))
+    copies = ts_copy_slots(seq)
+
+    lines = ["s_waitcnt lgkmcnt(0)", "s_mov_b32 %[m0sv], m0"]
+    lds = []            # LDS operations in issue order
+    known = [-1]        # every LDS op up to this index has completed
+
+    def lds_op(line):
+        lines.append(line)
+        lds.append(line)
+        return len(lds) - 1
+
+    def need(ids):
+        d = max(ids)
+        if d <= known[0]:
+            return
+        n = len(lds) - 1 - d
+        n = min(n, 15)
+        lines.append(f"s_waitcnt lgkmcnt({n})")
+        known[0] = len(lds) - 1 - n
+
+    def vregs(g):
+        r = VFA if g % 2 == 0 else VFB
+        return r
+
+    def v_reads(g):
+        c, j = g // 4, g % 4
+        r = vregs(g)
+        imm = (j >> 1) * 1024 + c * 16384
+        return (lds_op(f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %[vb{j & 1}0] offset:{imm}"),
+                lds_op(f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[vb{j & 1}1] offset:{imm}"))
+
+    pf_id = [lds_op(f"ds_read_b128 %[pf{rb}], %[pr] offset:{rb * 2048}") for rb in range(4)]
+    vf_id = {0: v_reads(0)}
+    k_id = {}
+    for c in range(TS_NBUF):
+        a, o = frag(c)
+        k_id[c] = lds_op(f"ds_read_b128 %[t{c % TS_NBUF}], {a} offset:{o}")
+    lines += sm_slots.get(-1, [])
+
+    for k, (kind, i) in enumerate(seq):
+        if kind == "P":
+            g, rb = i // 4, i % 4
+            j = g % 4
+            need(list(vf_id[g]) + [pf_id[rb]])
+            r = vregs(g)
+            lines.append(f"v_mfma_f32_32x32x16_bf16 %[o{rb}{j}], v[{r}:{r + 3}], %[pf{rb}], %[o{rb}{j}]")
+            if rb == 0 and g + 1 < 8:
+                vf_id[g + 1] = v_reads(g + 1)
+            if g == 3:  # last use of pf[rb] in the first key half: load the second
+                pf_id[rb] = lds_op(f"ds_read_b128 %[pf{rb}], %[pr] offset:{rb * 2048 + 1024}")
+        else:
+            c = i
+            need([k_id[c]])
+            src_c = "0" if c == 0 else "%[s]"
+            dst = f"v[{XR}:{XR + 15}]" if c == KS - 1 else "%[s]"
+            lines.append(f"v_mfma_f32_32x32x16_bf16 {dst}, %[t{c % TS_NBUF}], %[q{c}], {src_c}")
+            if c + TS_NBUF < KS:
+                a, o = frag(c + TS_NBUF)
+                k_id[c + TS_NBUF] = lds_op(f"ds_read_b128 %[t{c % TS_NBUF}], {a} offset:{o}")
+        for l in sm_slots.get(k, []):
+            if l.startswith("ds_write"):
+                lds_op(l)
+            else:
+                lines.append(l)
+        if k in copies:
+            cp = copies[k]
+            if cp < 8:
+                lines += [f"s_add_u32 m0, %[m0a], {cp * 896}", "s_nop 0",
+                          f"buffer_load_dwordx4 %[oa], %[ra], 0 offen offset:{cp * 128} lds"]
+            else:
+                lines += ["s_mov_b32 m0, %[m0b]", "s_nop 0",
+                          "buffer_load_dwordx4 %[ob], %[rb], 0 offen offset:0 lds"]
+    # (no trailing nops: the last P.V MFMAs cover the chain result, and their
+    # own AGPR results are read only after the key loop, behind a barrier and
+    # the nops the caller places there)
+    lines += ["s_mov_b32 m0, %[m0sv]"]
+    return lines
+
+
+def emit_tile_step():
+    lines = tile_step_lines()
+    body = "\n".join(f'      "{l}\\n"' for l in lines)
+    outs = ['[s] "=&v"(s)', f'[x] "+{{v[{XR}:{XR + 15}]}}"(x)']
+    outs += [f'[t{k}] "=&v"(t{k})' for k in range(TS_NBUF)]
+    outs += [f'[pf{k}] "=&v"(pf{k})' for k in range(4)]
+    outs += [f'[vfa] "=&{{v[{VFA}:{VFA + 3}]}}"(vfa)', f'[vfb] "=&{{v[{VFB}:{VFB + 3}]}}"(vfb)']
+    outs += ['[mref] "+v"(m_ref)', '[mrun] "+v"(m_run)', '[lp] "+v"(l_part)', '[lr] "+v"(l_rnd)']
+    outs += ['[m] "=&v"(m)', '[tmp] "=&v"(tmp)', '[mu] "=&v"(mu)', '[r0] "=&v"(r0)', '[r1] "=&v"(r1)']
+    outs += [f'[o{rb}{j}] "+a"(O[{rb}][{j}])' for rb in range(4) for j in range(4)]
+    outs += ['[m0sv] "=&s"(m0sv)']
+    ins = [f'[q{c}] "v"(qf[{c}])' for c in range(KS)]
+    ins += [f'[a{k}] "v"(a{k})' for k in range(4)] + [f'[b{k}] "v"(b{k})' for k in range(4)]
+    ins += ['[sc] "s"(sc)', '[pa] "v"(pw)', '[pr] "v"(pr)']
+    ins += [f'[vb{par}{h}] "v"(vb[{2 * par + h}])' for par in range(2) for h in range(2)]
+    ins += ['[oa] "v"(oa)', '[ob] "v"(ob)', '[ra] "s"(ra)', '[rb] "s"(rb)', '[m0a] "s"(m0a)', '[m0b] "s"(m0b)']
+    params = ("f32x16& x, f32x16 (&O)[4][4], const bf16x8* qf,\n"
+              "    uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t b0, uint32_t b1, uint32_t b2,\n"
+              "    uint32_t b3, float sc, float& m_ref, float& m_run, float& l_part, float& l_rnd, uint32_t pw,\n"
+              "    uint32_t pr, const uint32_t* vb, uint32_t oa, uint32_t ob, const u32x4& ra, const u32x4& rb,\n"
+              "    uint32_t m0a, uint32_t m0b")
+    pre = ("  f32x16 s;\n  u32x4 t0, t1, t2, t3, pf0, pf1, pf2, pf3, vfa, vfb;\n"
+           "  float m, tmp, mu, r0, r1;\n  uint32_t m0sv;\n")
+    return (f"__device__ __forceinline__ void tile_step({params}) {{\n{pre}"
+            f"  asm volatile(\n{body}\n"
+            f"      : {', '.join(outs)}\n"
+            f"      : {', '.join(ins)}\n"
+            f'      : "vcc", "scc", "memory");\n}}\n')
+
+
 def render():
     head = ("// Generated by gen_qk_chain.py from its description of the chain; do not\n"
             "// edit by hand (rerun the script).  Included by mla_attn.hip inside its\n"
@@ -209,7 +377,13 @@ def render():
             + "// The same chain with the softmax of the previous tile's scores x\n"
             + "// interleaved (P fragments to LDS at paddr, row stats updated in\n"
             + "// place); x returns the new scores.\n"
-            + emit_function("qk_chain_softmax", True))
+            + emit_function("qk_chain_softmax", True) + "\n"
+            + "// One key-loop step of the shared-latent form: P V of tile t into O (P at\n"
+            + "// pr, V of the tile by the four bases vb), the Q.K chain of tile t+2 with\n"
+            + "// the softmax of S(t+1) = x in it (P to pw, new scores to x), and the nine\n"
+            + "// copies of tile t+3 (buffer resources ra/rb, offsets oa/ob, LDS bases for\n"
+            + "// M0 m0a/m0b), all interleaved.\n"
+            + emit_tile_step())
 
 
 def main():

@@ -231,6 +231,18 @@ __device__ __forceinline__ void wait_tiles(int tiles) {
   else wait_vmem_n<2 * KI>();
 }
 
+// Byte offset, within a sub-tile with NG column groups, of the first of the two
+// transposed reads read_vt makes for value block db and key half c (half 0)
+// or of the second (half 1).
+template <int NG>
+__device__ __forceinline__ uint32_t vt_off(int db, int c, int lane, int half) {
+  const int g16 = lane >> 4, i = lane & 15;
+  const int hh = g16 >> 1, dvh = g16 & 1, jr = i >> 2, cq = i & 3;
+  const int col = 32 * db + 16 * dvh + 4 * cq;
+  const int key0 = 16 * c + 4 * hh + jr + 8 * half;
+  return (uint32_t)(tile_off(NG, key0, col >> 3) + (col & 7) * 2);
+}
+
 // V^T fragment (MFMA A operand, 32 value columns x 16 keys) for value-column
 // block `db` (32 columns) and key half `c` (keys 16c..16c+15) of a sub-tile
 // with NG column groups.  Lane l receives column 32*db + l%32 for the keys
@@ -660,7 +672,8 @@ void attn_fwd_kernel(const AttnParams p) {
       };
       // Past the last tile the chain still runs: the scores of tile n_tiles
       // are all masked (-inf), which leaves the row stats as they are, and
-      // the tile it multiplies is stale and unused.
+      // the tile it multiplies is stale and unused; copies past the last
+      // tile read zeros (an empty buffer range) into a free buffer.
       if (n_tiles > 0) {
         const int pre = min(n_tiles, NB - 1);
         for (int u = 0; u < pre; ++u) issue_tile(u, u);
@@ -669,12 +682,41 @@ void attn_fwd_kernel(const AttnParams p) {
         f32x16 sc = qk(0);
         chain_sm(sc, 0, 1);
         __syncthreads();
+        // this lane's V fragment offsets for value blocks 4w and 4w+1, key
+        // half 0 (other blocks and halves are instruction offsets)
+        uint32_t vbo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vbo[k] = vt_off<NGA>(w * NDVB + (k >> 1), 0, lane, k & 1);
         for (int t = 0; t < n_tiles; ++t) {  // sc = S(t+1)
-          pv_copy(t);
-          chain_sm(sc, t + 1, t + 2);
+          // scale and mask S(t+1) where needed (see chain_sm)
+          const int k0 = (t + 1) * BN;
+          const bool mask = k0 + BN > wave_vis_end || !(p.scale_log2 > 0.f);
+          float scl = p.scale_log2;
+          if (mask) {
+            const int bound = vis_end - k0 - 4 * h;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[r] = (r >> 2) * 8 + (r & 3) < bound ? sc[r] * p.scale_log2 : -INFINITY;
+            scl = 1.f;
+          }
+          uint32_t a[4], b[4], vb[4];
+          frag_addrs((t + 2) & (NB - 1), a, b);
+          const uint32_t vtile = lds_a + (t & (NB - 1)) * Smem<C, SP, NB>::ATILE;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) vb[k] = vtile + vbo[k];
+          TileSrc src = tile_src(min(t + NB - 1, n_tiles - 1), (t + NB - 1) & (NB - 1));
+          if (t + NB - 1 >= n_tiles) {
+            src.ra[2] = 0;
+            src.rb[2] = 0;
+          }
+          tile_step(sc, O, qf, a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], scl, m_ref, m_run, l_part, l_rnd,
+                    lds_addr(sm.p[(t + 1) & 1][w][0]) + lane * 16, lds_addr(sm.p[t & 1][0][0]) + lane * 16, vb,
+                    src.oa, src.ob, src.ra, src.rb, src.la + (uint32_t)(w * NGA) * 1024u, src.lb + (uint32_t)w * 1024u);
           wait_tiles<KI>(0);  // tile t+3
           __syncthreads();
         }
+        // the step's last MFMAs write O (AGPRs) without the wait states that
+        // a following VALU access of O needs
+        asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
       }
     } else {
       if (n_tiles > 0) {
