@@ -246,10 +246,14 @@ def ts_schedule(nslots):
     return step
 
 
+TS_COPY_EVERY = 2     # slots between the copies, from the start of the block
+
+
 def ts_copy_slots(seq):
-    """The nine copies of a tile go out after evenly spaced P.V MFMAs."""
-    pv_slots = [k for k, (kind, _) in enumerate(seq) if kind == "P"]
-    return {pv_slots[(4 * i * N_PV) // (9 * 4) + 1]: i for i in range(9)}
+    """The nine copies of a tile go out one every TS_COPY_EVERY MFMA slots from
+    the start of the block (measured: early copies beat copies spread over
+    the whole block by 3-4%)."""
+    return {TS_COPY_EVERY * i: i for i in range(9)}
 
 
 def tile_step_lines():
