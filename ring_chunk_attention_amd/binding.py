@@ -310,6 +310,18 @@ def ring_order(r: int, n_chunks: int) -> Sequence[int]:
     return [(r - s) % n_chunks for s in range(n_chunks) if (r - s) % n_chunks <= r]
 
 
+_RING_STREAMS: dict = {}
+
+
+def _ring_streams(device: torch.device, n: int):
+    """A per-device pool of side streams (default priority) for the ring."""
+    key = (device.index if device.index is not None else torch.cuda.current_device())
+    pool = _RING_STREAMS.setdefault(key, [])
+    while len(pool) < n:
+        pool.append(torch.cuda.Stream(device=device))
+    return pool[:n]
+
+
 def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
              head_dim_v: int = 512, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None,
@@ -323,8 +335,13 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
     first folds its result into the running (out, lse) through the prev
     arguments, in place (TensorRT-LLM mla.py forward_context_with_chunked_prefill;
     Ascend RingMLAOperation calcType).  The running output between folds is
-    kept in float32 (``carry``, [B, H, C, dv], allocated if not given) and only
-    the last step of each query chunk writes bf16 ``out``."""
+    kept in float32 (``carry``, [n_chunks, B, H, C, dv], allocated if not
+    given) and only the last step of each query chunk writes bf16 ``out``.
+
+    The query chunks are independent of one another, so each runs its steps
+    in order on a side stream of its own, and the chunks overlap on the GPU
+    (one call covers only B*H/4 * C/32 workgroups); the caller's stream waits
+    for all of them before this returns."""
     B, H, N, dk = q.shape
     if N % n_chunks:
         raise ValueError("sequence length must be a multiple of the chunk count")
@@ -334,15 +351,25 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if carry is None and n_chunks > 1:
-        carry = torch.empty((B, H, C, head_dim_v), dtype=torch.float32, device=q.device)
-    for r in range(n_chunks):
-        qs = slice(r * C, (r + 1) * C)
-        o_r, l_r = out[:, :, qs], lse[:, :, qs]
-        order = ring_order(r, n_chunks)
-        for step, k in enumerate(order):
-            last = step == len(order) - 1
-            fwd(q[:, :, qs], kv[:, :, k * C:(k + 1) * C], scale=scale, head_dim_v=head_dim_v,
-                causal=True, q_offset=r * C, kv_offset=k * C,
-                prev=None if step == 0 else (carry, l_r),
-                out=o_r if last else carry, lse=l_r)
+        carry = torch.empty((n_chunks, B, H, C, head_dim_v), dtype=torch.float32, device=q.device)
+    main = torch.cuda.current_stream(q.device)
+    streams = _ring_streams(q.device, n_chunks)
+    for st in streams:
+        st.wait_stream(main)
+    orders = [ring_order(r, n_chunks) for r in range(n_chunks)]
+    for step in range(n_chunks):  # step-major, so that every chunk starts at once
+        for r in range(n_chunks):
+            if step >= len(orders[r]):
+                continue
+            k = orders[r][step]
+            qs = slice(r * C, (r + 1) * C)
+            o_r, l_r = out[:, :, qs], lse[:, :, qs]
+            last = step == len(orders[r]) - 1
+            with torch.cuda.stream(streams[r]):
+                fwd(q[:, :, qs], kv[:, :, k * C:(k + 1) * C], scale=scale, head_dim_v=head_dim_v,
+                    causal=True, q_offset=r * C, kv_offset=k * C,
+                    prev=None if step == 0 else (carry[r], l_r),
+                    out=o_r if last else carry[r], lse=l_r)
+    for st in streams:
+        main.wait_stream(st)
     return out, lse
