@@ -32,7 +32,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "causal MLA prefill TFLOP/s and % of bf16 MFMA peak on 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_latent_dsv3_prefill_hbm_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "ring_chunk_attention_amd", "csrc", "mla_attn.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "ring_chunk_attention_amd", "csrc", f)
+               for f in ("mla_attn.hip", "mla_qk_chain.inc")]
 
 
 def causal_pairs(n_q: int, n_kv: int, q_offset: int = 0, kv_offset: int = 0) -> int:
@@ -43,8 +44,13 @@ def causal_pairs(n_q: int, n_kv: int, q_offset: int = 0, kv_offset: int = 0) -> 
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernel's sources (the kernel file and the Q.K
+    chain it includes)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def time_launches(fn, steps: int, warmup: int):
