@@ -273,8 +273,15 @@ struct Ctx {
   int hbase;          // first head (latent), head (split)
 };
 
+// The latent and sparse forms use the whole register file and LDS of a CU
+// (one workgroup per CU); the split form needs about 200 registers and, with
+// three tile buffers, 76 KB of LDS, so two of its workgroups share a CU and
+// each hides the other's waits.
+template <int MODE>
+constexpr int kWavesPerEU = MODE == 1 ? 2 : 1;
+
 template <class C, int MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, kWavesPerEU<MODE>)))
 void attn_fwd_kernel(const AttnParams p) {
   constexpr bool SP = MODE == SPARSE;
   constexpr int DA = C::DA, DV = C::DV;
@@ -287,7 +294,7 @@ void attn_fwd_kernel(const AttnParams p) {
   constexpr int KI = NGA + 1 + (C::VLAT ? 0 : NGV);  // copy instructions per wave per tile
   // key-tile buffers: four let a tile's copy run two iterations ahead of its
   // use (the sparse form keeps the index list in LDS instead of a fourth)
-  constexpr int NB = SP ? 3 : 4;
+  constexpr int NB = MODE == LATENT ? 4 : 3;
   // the latent form runs the softmax of tile t+1 inside the Q.K chain of
   // tile t+2 (see the main loop), the others compute it beside P.V
   constexpr bool SM_IN_QK = MODE == LATENT;
