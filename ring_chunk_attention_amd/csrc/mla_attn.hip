@@ -817,6 +817,81 @@ void attn_fwd_kernel(const AttnParams p) {
   }
   __syncthreads();
 
+  if (!p.prev_out.p && !p.out_f32) {
+    // Plain bf16 output: O^T sits in the accumulators with one output row per
+    // lane, so direct stores would be 8-byte pieces of 32 rows each.  Instead
+    // the scaled bf16 rows go through LDS (the idle tile buffers; the row
+    // stride is padded by 16 bytes to spread the banks) and leave as whole
+    // rows, 16 bytes a lane.
+    constexpr int RS = DV * 2 + 16;           // LDS row stride, bytes
+    constexpr int LPR = DV * 2 / 16;          // lanes per output row
+    constexpr int RPI = 64 / LPR;             // rows per store instruction
+    // staging space: the tile buffers and what follows them up to P
+    constexpr int CAP = (int)(sizeof(sm.a) + sizeof(sm.b) + sizeof(sm.v) + sizeof(sm.idx));
+    constexpr int NPASS = ROWS * RS <= CAP ? 1 : 2;  // halves of the rows at a time
+    static_assert(ROWS * RS <= 2 * CAP, "half of the rows fits the staging space");
+    constexpr int RBP = WAVES / NPASS;        // row blocks per pass
+    const uint32_t stage = lds_addr(&sm.a[0][0]);
+#pragma unroll
+    for (int pass_ = 0; pass_ < NPASS; ++pass_) {
+#pragma unroll
+      for (int rbl = 0; rbl < RBP; ++rbl) {
+        const int rb = pass_ * RBP + rbl;
+        const float wc = sm.epi.wcur[rb * 32 + lr];
+        const uint32_t row = stage + (uint32_t)(rbl * 32 + lr) * RS;
+#pragma unroll
+        for (int j = 0; j < NDVB; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = 32 * (w * NDVB + j) + 8 * g + 4 * h;
+            const u32x2 v = {pack_bf16x2(wc * O[rb][j][4 * g], wc * O[rb][j][4 * g + 1]),
+                             pack_bf16x2(wc * O[rb][j][4 * g + 2], wc * O[rb][j][4 * g + 3])};
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)(row + d * 2)) = v;
+          }
+        }
+      }
+      __syncthreads();
+      // this wave stores staged rows w*RPI + k*WAVES*RPI (+ lane/LPR), k < NST,
+      // reading a batch of them from LDS before storing the batch
+      constexpr int NST = RBP * 32 / (WAVES * RPI);
+      constexpr int BATCH = NST < 8 ? NST : 8;
+      static_assert(NST % BATCH == 0, "store batches");
+#pragma unroll
+      for (int k0 = 0; k0 < NST; k0 += BATCH) {
+        u32x4 v[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+          const int rs = (w + (k0 + k) * WAVES) * RPI + lane / LPR;
+          v[k] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+              (uintptr_t)(stage + (uint32_t)rs * RS + (lane % LPR) * 16));
+        }
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+          const int rs = (w + (k0 + k) * WAVES) * RPI + lane / LPR;  // staged row
+          const int r = pass_ * RBP * 32 + rs;                        // row of the workgroup
+          const int rb = r >> 5, rl = r & 31;
+          int hq;
+          int64_t qq;
+          if constexpr (MODE == LATENT) {
+            hq = cx.hbase + rb;
+            qq = cx.q0 + rl;
+          } else if constexpr (MODE == SPLIT) {
+            hq = cx.hbase;
+            qq = cx.q0 + r;
+          } else {
+            hq = r;
+            qq = cx.q0;
+          }
+          if (hq < p.Hq && qq < cx.q_len)
+            *reinterpret_cast<u32x4*>(p.out.p + cx.b * p.out.sb + hq * p.out.sh + qtok(qq) * p.out.st +
+                                      (lane % LPR) * 8) = v[k];
+        }
+      }
+      if (NPASS > 1 && pass_ + 1 < NPASS) __syncthreads();
+    }
+    return;
+  }
+
 #pragma unroll
   for (int rb = 0; rb < WAVES; ++rb) {
     if (!row_valid(rb)) continue;
