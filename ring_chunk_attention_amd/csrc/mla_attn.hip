@@ -70,7 +70,10 @@ constexpr float LN2 = 0.693147180559945309f;
 constexpr unsigned kRsrcFlags = 0x00020000u;  // raw buffer resource word 3 on gfx9
 constexpr unsigned kOob = 0x80000000u;        // offset past any valid record: reads zeros
 
-enum Mode { LATENT = 0, SPLIT = 1, SPARSE = 2 };
+// SPARSE: top-k lists up to 4096 entries, beside-P.V softmax loop;
+// SPARSE_PIPE: lists up to 2048 entries, the tile-step loop of the latent form
+enum Mode { LATENT = 0, SPLIT = 1, SPARSE = 2, SPARSE_PIPE = 3 };
+constexpr int KMAX_IDX_PIPE = 2048;
 
 struct LatentCfg {
   static constexpr int DA = 512, DV = 512;
@@ -104,16 +107,18 @@ __device__ __forceinline__ int tile_off(int NG, int r, int q) {
   return (((r >> 3) * NG + (q >> 3)) << 10) + ((r & 7) << 7) + (((q & 7) ^ swz_f(r & 15)) << 4);
 }
 
-template <class C, bool SP, int NB>
+// NB buffers for the first sub-tile (and V), NBB for the 64-column one, which
+// only the Q.K chain reads; KIDX entries of the sparse index list
+template <class C, int NB, int NBB, int KIDX>
 struct Smem {
   static constexpr int ATILE = BN * C::DA * 2, BTILE = BN * DB * 2;
   static constexpr int VTILE = C::VLAT ? 0 : BN * C::DV * 2;
   // 1 KB aligned (the tiles are multiples of 1 KB): a fragment address
   // differs from its k-step-0 neighbour only in bits 5-6 (see frag_addrs)
   alignas(1024) unsigned char a[NB][ATILE];
-  alignas(1024) unsigned char b[NB][BTILE];
+  alignas(1024) unsigned char b[NBB][BTILE];
   alignas(16) unsigned char v[NB][VTILE];
-  alignas(16) int idx[SP ? KMAX_IDX : 0];            // sparse: the query's index list
+  alignas(16) int idx[KIDX];                          // sparse: the query's index list
   union {
     alignas(16) unsigned char p[2][WAVES][2][64 * 16];  // P^T fragments: buffer, wave, 16-key half
     struct {                                            // after the key loop
@@ -283,7 +288,7 @@ constexpr int kWavesPerEU = MODE == 1 ? 2 : 1;
 template <class C, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, kWavesPerEU<MODE>)))
 void attn_fwd_kernel(const AttnParams p) {
-  constexpr bool SP = MODE == SPARSE;
+  constexpr bool SP = MODE == SPARSE || MODE == SPARSE_PIPE;
   constexpr int DA = C::DA, DV = C::DV;
   constexpr int DK = DA + DB;
   constexpr int KS = DK / 16;            // MFMA k-steps of Q.K
@@ -292,16 +297,22 @@ void attn_fwd_kernel(const AttnParams p) {
   constexpr int NGV = C::VLAT ? NGA : DV / 64;
   constexpr int NDVB = DV / 32 / WAVES;  // 32-column value blocks per wave
   constexpr int KI = NGA + 1 + (C::VLAT ? 0 : NGV);  // copy instructions per wave per tile
-  // key-tile buffers: four let a tile's copy run two iterations ahead of its
-  // use (the sparse form keeps the index list in LDS instead of a fourth)
-  constexpr int NB = MODE == LATENT ? 4 : 3;
-  // the latent form runs the softmax of tile t+1 inside the Q.K chain of
-  // tile t+2 (see the main loop), the others compute it beside P.V
-  constexpr bool SM_IN_QK = MODE == LATENT;
+  // the latent form (and the sparse one for lists up to 2048) runs the
+  // softmax of tile t+1 inside the Q.K chain of tile t+2 (see the main
+  // loop) with four key-tile buffers; the others compute it beside P.V with
+  // three (the sparse form keeps its index list in LDS instead of a fourth)
+  constexpr bool SM_IN_QK = MODE == LATENT || MODE == SPARSE_PIPE;
+  constexpr int NB = SM_IN_QK ? 4 : 3;
+  // 64-column sub-tile buffers: only the Q.K chain reads them, so two are
+  // enough in the tile-step loop (the one being read and the one in flight);
+  // the pipelined sparse form needs that room for its index list
+  constexpr int NBB = MODE == SPARSE_PIPE ? 2 : NB;
+  constexpr int KIDX = MODE == SPARSE ? KMAX_IDX : MODE == SPARSE_PIPE ? KMAX_IDX_PIPE : 0;
+  using SM = Smem<C, NB, NBB, KIDX>;
   static_assert(KS - KSA == 4, "second part is 64 columns");
   static_assert(NB - 2 <= 2, "wait_tiles covers at most two tiles in flight");
 
-  __shared__ Smem<C, SP, NB> sm;
+  __shared__ SM sm;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -426,9 +437,11 @@ void attn_fwd_kernel(const AttnParams p) {
   auto tile_src = [&](int t, int buf) __attribute__((always_inline)) -> TileSrc {
     TileSrc c;
     const int64_t k0 = (int64_t)t * BN;
-    c.la = lds_a + buf * Smem<C, SP, NB>::ATILE;
-    c.lb = lds_b + buf * Smem<C, SP, NB>::BTILE;
-    c.lv = lds_v + buf * Smem<C, SP, NB>::VTILE;
+    // buf: the slot of the tile in the ring of buffers (the A buffer; the B
+    // buffer is the same slot modulo NBB)
+    c.la = lds_a + buf * SM::ATILE;
+    c.lb = lds_b + (buf % NBB) * SM::BTILE;
+    c.lv = lds_v + buf * SM::VTILE;
     if constexpr (SP) {
       const int r = (int)k0 + lrow;
       const int ix = r < p.topk ? sm.idx[r] : -1;
@@ -490,7 +503,7 @@ void attn_fwd_kernel(const AttnParams p) {
   // S^T = K Q^T for one tile (lane: query row lr; keys (r/4)*8 + 4h + r%4)
   // LDS byte addresses of this lane's K fragments in tile buffer `buf`
   auto frag_addrs = [&](int buf, uint32_t* a, uint32_t* b) __attribute__((always_inline)) {
-    const uint32_t ta = lds_a + buf * Smem<C, SP, NB>::ATILE, tb = lds_b + buf * Smem<C, SP, NB>::BTILE;
+    const uint32_t ta = lds_a + buf * SM::ATILE, tb = lds_b + (buf % NBB) * SM::BTILE;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       a[k] = (ta + koffA) ^ (uint32_t)(k << 5);
@@ -616,21 +629,46 @@ void attn_fwd_kernel(const AttnParams p) {
     });
   };
 
-  // Softmax of S(tp) = x to P buffer tp&1 inside the Q.K chain of tile tq;
-  // x returns S(tq).  The chain neither scales nor masks: a tile that needs
-  // a mask (or a scale that is not positive) is scaled and masked here, and
-  // the chain runs with scale 1.
-  auto chain_sm = [&](f32x16& x, int tp, int tq) __attribute__((always_inline)) {
-    if constexpr (KS == 36 && !SP) {
-      const int k0 = tp * BN;
-      const bool mask = k0 + BN > wave_vis_end || !(p.scale_log2 > 0.f);  // wave-uniform
-      float sc = p.scale_log2;
-      if (mask) {
-        const int bound = vis_end - k0 - 4 * h;
+  // Scores S(tp) = x ready for the chain's softmax, which neither scales nor
+  // masks: a tile that needs a mask (a key past the causal bound or the
+  // end, or an index outside the cache) or a scale that is not positive is
+  // scaled and masked here, and the chain then runs with scale 1 (returned).
+  auto prep_scores = [&](f32x16& x, int tp) __attribute__((always_inline)) -> float {
+    const int k0 = tp * BN;
+    bool mask;
+    unsigned vbits = 0xffffffffu;
+    if constexpr (SP) {
+      const int k = k0 + lr;  // key lr of the tile (lanes 32-63 repeat 0-31)
+      const int ix = sm.idx[k < p.topk ? k : 0];
+      vbits = (unsigned)__ballot((k < p.topk) & (ix >= 0) & (ix < p.Nkv));
+      mask = vbits != 0xffffffffu;
+    } else {
+      mask = k0 + BN > wave_vis_end;
+    }
+    mask = mask || !(p.scale_log2 > 0.f);  // wave-uniform
+    float sc = p.scale_log2;
+    if (mask) {
+      const int bound = vis_end - k0 - 4 * h;
+      const unsigned vb = vbits >> (4 * h);  // bit (r/4)*8 + r%4: this lane's key r
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r >> 2) * 8 + (r & 3) < bound ? x[r] * p.scale_log2 : -INFINITY;
-        sc = 1.f;
+      for (int r = 0; r < 16; ++r) {
+        bool ok;
+        if constexpr (SP) {
+          ok = (vb >> ((r >> 2) * 8 + (r & 3))) & 1u;
+        } else {
+          ok = (r >> 2) * 8 + (r & 3) < bound;
+        }
+        x[r] = ok ? x[r] * p.scale_log2 : -INFINITY;
       }
+      sc = 1.f;
+    }
+    return sc;
+  };
+  // Softmax of S(tp) = x to P buffer tp&1 inside the Q.K chain of tile tq;
+  // x returns S(tq).
+  auto chain_sm = [&](f32x16& x, int tp, int tq) __attribute__((always_inline)) {
+    if constexpr (KS == 36) {
+      const float sc = prep_scores(x, tp);
       uint32_t a[4], b[4];
       frag_addrs(tq & (NB - 1), a, b);
       qk_chain_softmax(x, qf, a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], sc, m_ref, m_run, l_part, l_rnd,
@@ -683,31 +721,39 @@ void attn_fwd_kernel(const AttnParams p) {
       // tile read zeros (an empty buffer range) into a free buffer.
       if (n_tiles > 0) {
         const int pre = min(n_tiles, NB - 1);
-        for (int u = 0; u < pre; ++u) issue_tile(u, u);
-        wait_tiles<KI>(0);
-        __syncthreads();
-        f32x16 sc = qk(0);
-        chain_sm(sc, 0, 1);
-        __syncthreads();
+        f32x16 sc;
+        if constexpr (NBB >= NB - 1) {
+          for (int u = 0; u < pre; ++u) issue_tile(u, u);
+          wait_tiles<KI>(0);
+          __syncthreads();
+          sc = qk(0);
+          chain_sm(sc, 0, 1);
+          __syncthreads();
+        } else {
+          // two 64-column buffers: tile 2's goes into tile 0's once every
+          // wave has read that in Q.K(0)
+          for (int u = 0; u < min(pre, 2); ++u) issue_tile(u, u);
+          const TileSrc c2 = tile_src(min(2, n_tiles - 1), 2);
+          if (pre > 2) unroll<NGA>([&](auto I) __attribute__((always_inline)) { issue_copy(c2, I); });
+          wait_tiles<KI>(0);
+          __syncthreads();
+          sc = qk(0);
+          __syncthreads();
+          if (pre > 2) issue_copy(c2, std::integral_constant<int, NGA>{});
+          chain_sm(sc, 0, 1);
+          wait_tiles<KI>(0);
+          __syncthreads();
+        }
         // this lane's V fragment offsets for value blocks 4w and 4w+1, key
         // half 0 (other blocks and halves are instruction offsets)
         uint32_t vbo[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) vbo[k] = vt_off<NGA>(w * NDVB + (k >> 1), 0, lane, k & 1);
         for (int t = 0; t < n_tiles; ++t) {  // sc = S(t+1)
-          // scale and mask S(t+1) where needed (see chain_sm)
-          const int k0 = (t + 1) * BN;
-          const bool mask = k0 + BN > wave_vis_end || !(p.scale_log2 > 0.f);
-          float scl = p.scale_log2;
-          if (mask) {
-            const int bound = vis_end - k0 - 4 * h;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sc[r] = (r >> 2) * 8 + (r & 3) < bound ? sc[r] * p.scale_log2 : -INFINITY;
-            scl = 1.f;
-          }
+          const float scl = prep_scores(sc, t + 1);
           uint32_t a[4], b[4], vb[4];
           frag_addrs((t + 2) & (NB - 1), a, b);
-          const uint32_t vtile = lds_a + (t & (NB - 1)) * Smem<C, SP, NB>::ATILE;
+          const uint32_t vtile = lds_a + (t & (NB - 1)) * SM::ATILE;
 #pragma unroll
           for (int k = 0; k < 4; ++k) vb[k] = vtile + vbo[k];
           TileSrc src = tile_src(min(t + NB - 1, n_tiles - 1), (t + NB - 1) & (NB - 1));
@@ -986,7 +1032,10 @@ hipError_t launch_latent_dense(const AttnParams& p, hipStream_t s) {
 hipError_t launch_latent_sparse(const AttnParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.B * p.Nq;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<LatentCfg, SPARSE>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  if (p.topk <= KMAX_IDX_PIPE)
+    hipLaunchKernelGGL((attn_fwd_kernel<LatentCfg, SPARSE_PIPE>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<LatentCfg, SPARSE>), dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -273,7 +273,8 @@ def _sparse_gpu(mla, c, idx=None):
     return out, lse
 
 
-@pytest.mark.parametrize("H,K,seed", [(128, 96, 40), (20, 2048, 41), (128, 40, 42)])
+@pytest.mark.parametrize("H,K,seed", [(128, 96, 40), (20, 2048, 41), (128, 40, 42),
+                                      (16, 2049, 46), (128, 1, 47), (8, 2900, 49)])
 def test_sparse_small(mla, H, K, seed):
     c = W.sparse_case(S=24, S_kv=3000, pos0=2900, H=H, K=K, seed=seed)
     out, lse = _sparse_gpu(mla, c)
@@ -334,3 +335,76 @@ def test_sparse_config_sampled(mla):
     o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale, rows=rows)
     assert report("sparse cfg O", host(out[:, rows]), o_ref) <= O_TOL
     assert report("sparse cfg LSE", host(lse[:, rows]), l_ref) <= LSE_TOL
+
+
+# ---------------------------------------------------------------------------
+# wide score range: the row maxima grow far past the reference max that the
+# kernels fix at a row's first key tile, so every form takes its second,
+# exact-max pass.  The 64 RoPE columns of queries and keys are scaled by 8
+# (exact in bf16), which gives scores of about 37 nats standard deviation.
+# The weights are then close to one-hot, so an output is close to one value
+# row; the value columns are halved so that outputs stay below 4 in
+# magnitude, where rounding to bf16 costs at most 2^-8 (between 4 and 8 it
+# would cost up to 2^-7, past the 1e-2 bound).
+# ---------------------------------------------------------------------------
+def _times_pow2(bits, f, cols=slice(None)):
+    """bf16 bits with the columns `cols` of the last axis times a power of two
+    (exact: only the exponent changes)."""
+    x = W.bf16_bits_to_f32(bits)
+    x[..., cols] *= np.float32(f)
+    return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _max_growth_log2(q, k, scale, vis):
+    """Largest growth, in log2 units, of a row's score max over the max of its
+    first 32 visible keys.  q [R, d], k [n, d] (fp64), vis [R, n] bool."""
+    s = (q @ k.T) * scale / math.log(2.0)
+    s = np.where(vis, s, -np.inf)
+    first = np.array([row[v][:32].max() if v.any() else -np.inf for row, v in zip(s, vis)])
+    full = s.max(axis=1)
+    ok = np.isfinite(first)
+    return float((full[ok] - first[ok]).max())
+
+
+def test_dense_wide_range_second_pass(mla):
+    c = W.dense_case(B=1, H=6, N=200, seed=8)
+    c.q = _times_pow2(c.q, 8.0, slice(512, None))
+    c.kv = _times_pow2(_times_pow2(c.kv, 8.0, slice(512, None)), 0.5, slice(0, 512))
+    q64, k64 = W.bf16_bits_to_f64(c.q[0, 0]), W.bf16_bits_to_f64(c.kv[0, 0])
+    vis = np.tril(np.ones((200, 200), dtype=bool))
+    assert _max_growth_log2(q64, k64, c.scale, vis) > 40.0
+    out, lse = _dense_gpu(mla, c)
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
+    assert report("wide O", host(out), o_ref) <= O_TOL
+    assert report("wide LSE", host(lse), l_ref) <= LSE_TOL
+
+
+@pytest.mark.parametrize("K", [300, 2400])
+def test_sparse_wide_range_second_pass(mla, K):
+    c = W.sparse_case(S=8, S_kv=3000, pos0=2900, H=32, K=K, seed=50 + K)
+    c.q_pe = _times_pow2(c.q_pe, 8.0)
+    c.k_pe = _times_pow2(c.k_pe, 8.0)
+    c.c_kv = _times_pow2(c.c_kv, 0.5)
+    q64 = np.concatenate([W.bf16_bits_to_f64(c.q_lift[0, 0]), W.bf16_bits_to_f64(c.q_pe[0, 0])], axis=1)
+    rows = np.concatenate([W.bf16_bits_to_f64(c.c_kv[0]), W.bf16_bits_to_f64(c.k_pe[0])], axis=1)
+    k64 = rows[c.idx[0, 0]]
+    assert _max_growth_log2(q64, k64, c.scale, np.ones((32, K), dtype=bool)) > 40.0
+    out, lse = _sparse_gpu(mla, c)
+    o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale)
+    assert report("wide sparse O", host(out), o_ref) <= O_TOL
+    assert report("wide sparse LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_split_wide_range_second_pass(mla):
+    c = W.split_case(seq_lens=[300, 77], H=4, Hkv=2, seed=9, with_prev=True)
+    c.q2 = _times_pow2(c.q2, 8.0)
+    c.k2 = _times_pow2(c.k2, 8.0)
+    c.v = _times_pow2(c.v, 0.5)
+    q64 = np.concatenate([W.bf16_bits_to_f64(c.q1[:300, 0]), W.bf16_bits_to_f64(c.q2[:300, 0])], axis=1)
+    k64 = np.concatenate([W.bf16_bits_to_f64(c.k1[:300, 0]), W.bf16_bits_to_f64(c.k2[:300, 0])], axis=1)
+    assert _max_growth_log2(q64, k64, c.scale, np.tril(np.ones((300, 300), dtype=bool))) > 40.0
+    out, lse = _split_gpu(mla, c, True)
+    o_ref, l_ref = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale,
+                                    prev_out=c.prev_out, prev_lse=c.prev_lse)
+    assert report("wide split O", host(out), o_ref) <= O_TOL
+    assert report("wide split LSE", host(lse), l_ref) <= LSE_TOL
