@@ -41,6 +41,18 @@
  *   is returned as MLA_ERR_HIP.  Nothing aborts or throws across the ABI.
  * - Shapes without a kernel return MLA_ERR_UNSUPPORTED; there is no slow or
  *   host fallback.
+ * - Workspace (mla_fwd, mla_sparse_fwd): optional.  When `workspace` is not
+ *   NULL it must point to at least mla_workspace_size() bytes of device
+ *   memory, 16-byte aligned, given as `workspace_bytes`; its contents need no
+ *   initialisation and are left unspecified.  With it, the workgroups of
+ *   the shared-latent kernel and of the sparse kernel (K <= 2048) take their
+ *   row blocks, longest first, from a counter in the workspace (which the
+ *   call resets on `stream` before its launch) rather than by their launch
+ *   index, so that the parts of the chip that run faster take more of the
+ *   work (TT-NN ring_mla, is_balanced; the queue is this library's reading
+ *   of "balanced").  Launches with few row blocks ignore it.  Results are
+ *   bit-identical with and without it.  Calls that may run at the same time
+ *   need distinct workspaces.
  */
 #ifndef MLA355_H
 #define MLA355_H
@@ -133,6 +145,7 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope,
                    float scale, uint32_t flags, int64_t q_offset, int64_t kv_offset,
                    const mla_rows* prev_out, const mla_rows* prev_lse,
                    const mla_rows* out, const mla_rows* lse,
+                   void* workspace, size_t workspace_bytes,
                    void* stream /* hipStream_t */);
 
 /*
@@ -180,6 +193,7 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe,
                           int32_t B, int64_t S, int64_t S_kv, int32_t H,
                           int32_t L, int32_t R, int32_t K, float scale,
                           const mla_rows* out, const mla_rows* lse,
+                          void* workspace, size_t workspace_bytes,
                           void* stream /* hipStream_t */);
 
 /*
@@ -193,6 +207,10 @@ mla_status mla_debug_gather(const mla_rows* c_kv, const mla_rows* k_pe,
                             const int32_t* idx, int32_t b, int64_t S_kv,
                             int32_t L, int32_t R, int32_t K,
                             uint16_t* rows_out, void* stream /* hipStream_t */);
+
+/* Bytes of the optional workspace of mla_fwd and mla_sparse_fwd (see
+ * "Workspace" above); the same for every shape. */
+size_t mla_workspace_size(void);
 
 /* Thread-local description of the last non-OK status on this thread. */
 const char* mla_last_error(void);

@@ -3,7 +3,7 @@
 The compute runs in libmla355.so (hand-written HIP kernels behind a C ABI,
 declared in include/mla355.h); this package is its Python binding.  Importing
 it loads the library and raises if it has not been built
-(``python -m ring_chunk_attention_amd.build``).
+(``python ring_chunk_attention_amd/build.py``).
 """
 from .binding import (EXPORTS, LIB_PATH, MlaError, debug_gather, fwd, merge, ring_fwd, ring_order,
                       sparse_fwd, split_fwd, version)

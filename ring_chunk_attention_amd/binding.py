@@ -37,7 +37,7 @@ _P = ctypes.POINTER(MlaRows)
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is missing: build it with `python -m ring_chunk_attention_amd.build`")
+            f"{_LIB_PATH} is missing: build it with `python ring_chunk_attention_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     lib.mla_fwd.restype = ctypes.c_int
     lib.mla_fwd.argtypes = [
@@ -46,14 +46,15 @@ def _load():
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_int32,
         ctypes.c_float, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64,
-        _P, _P, _P, _P, ctypes.c_void_p]
+        _P, _P, _P, _P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_merge_lse.restype = ctypes.c_int
     lib.mla_merge_lse.argtypes = [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_int32, _P, _P, ctypes.c_void_p]
     lib.mla_sparse_fwd.restype = ctypes.c_int
     lib.mla_sparse_fwd.argtypes = [_P, _P, _P, _P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                   ctypes.c_int32, ctypes.c_float, _P, _P, ctypes.c_void_p]
+                                   ctypes.c_int32, ctypes.c_float, _P, _P, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_debug_gather.restype = ctypes.c_int
     lib.mla_debug_gather.argtypes = [_P, _P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -62,6 +63,8 @@ def _load():
     lib.mla_last_error.argtypes = []
     lib.mla_version.restype = ctypes.c_char_p
     lib.mla_version.argtypes = []
+    lib.mla_workspace_size.restype = ctypes.c_size_t
+    lib.mla_workspace_size.argtypes = []
     return lib
 
 
@@ -69,7 +72,7 @@ LIB = _load()
 LIB_PATH = _LIB_PATH
 
 EXPORTS = ("mla_fwd", "mla_merge_lse", "mla_sparse_fwd", "mla_debug_gather",
-           "mla_last_error", "mla_version")
+           "mla_last_error", "mla_version", "mla_workspace_size")
 
 
 class MlaError(RuntimeError):
@@ -137,6 +140,31 @@ def _stream(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# One workspace per (device, stream): calls on one stream run one after
+# another, so they can share it; calls on different streams get their own.
+_WORKSPACES = {}
+
+
+def _workspace(device: torch.device, workspace) -> Tuple[Optional[int], int]:
+    """(pointer, bytes) of the workspace for a call on the current stream:
+    ``"auto"`` -> this stream's cached one, None -> no workspace (row blocks
+    by launch index), a uint8 GPU tensor -> that tensor."""
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace: expected 'auto', None or a uint8 tensor")
+        key = (device.index if device.index is not None else torch.cuda.current_device(),
+               torch.cuda.current_stream(device).cuda_stream)
+        ws = _WORKSPACES.get(key)
+        if ws is None:
+            ws = torch.empty(int(LIB.mla_workspace_size()), dtype=torch.uint8, device=device)
+            _WORKSPACES[key] = ws
+        workspace = ws
+    _need(workspace, "workspace", torch.uint8)
+    return workspace.data_ptr(), workspace.numel()
+
+
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
@@ -146,7 +174,7 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 51
         v: Optional[torch.Tensor] = None,
         prev: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-        want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        want_lse: bool = True, workspace="auto") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Attention over [B, H, N, D] tensors (mla_fwd).
 
     q [B, Hq, Nq, dq], kv [B, Hkv, Nkv, dq]; optional q_rope/k_rope
@@ -155,7 +183,10 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 51
     into a previous one (out/lse may be the same tensors).  Returns
     (out [B, Hq, Nq, dv] bf16, lse [B, Hq, Nq] fp32 or None).  ``out`` and
     ``prev_out`` may be float32 tensors (a float32 running output for ring
-    folds); their dtype selects the flag.
+    folds); their dtype selects the flag.  ``workspace``: "auto" (a cached
+    per-stream buffer: row blocks from a device queue), None (row blocks by
+    launch index) or a uint8 GPU tensor of at least mla_workspace_size()
+    bytes.
     """
     B, Hq, Nq, dq = q.shape
     _, Hkv, Nkv, _ = kv.shape
@@ -178,10 +209,12 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 51
     vl = _lse_bht(lse, "lse") if lse is not None else None
     flags = ((MLA_CAUSAL if causal else 0) | (MLA_OUT_F32 if out_f32 else 0)
              | (MLA_PREV_OUT_F32 if prev_f32 else 0))
+    ws, ws_bytes = _workspace(q.device, workspace)
     _check(LIB.mla_fwd(ctypes.byref(vq), _ref(vqr), ctypes.byref(vkv), _ref(vkr), _ref(vv),
                        B, Hq, Hkv, Nq, Nkv, dq, dr, dv, None, 0, float(scale), flags,
                        q_offset, kv_offset,
-                       _ref(vpo), _ref(vpl), ctypes.byref(vout), _ref(vl), _stream(q.device)))
+                       _ref(vpo), _ref(vpl), ctypes.byref(vout), _ref(vl), ws, ws_bytes,
+                       _stream(q.device)))
     return out, lse
 
 
@@ -218,7 +251,7 @@ def split_fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Te
                        seq_lens.data_ptr() if seq_lens is not None else None,
                        seq_lens.numel() if seq_lens is not None else 0,
                        float(scale), MLA_CAUSAL if causal else 0, 0, 0,
-                       _ref(vpo), _ref(vpl), ctypes.byref(vout), ctypes.byref(vl),
+                       _ref(vpo), _ref(vpl), ctypes.byref(vout), ctypes.byref(vl), None, 0,
                        _stream(q1.device)))
     return out, lse
 
@@ -241,11 +274,12 @@ def merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: 
 
 def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
                topk_idx: torch.Tensor, *, scale: float, out: Optional[torch.Tensor] = None,
-               lse: Optional[torch.Tensor] = None, want_lse: bool = True
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True, workspace="auto"
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Top-k sparse latent attention (mla_sparse_fwd): q_lift [B,S,H,L],
     q_pe [B,S,H,R], c_kv [B,S_kv,L], k_pe [B,S_kv,R], topk_idx int32
-    [B,S,K] -> out [B, S, H*L] bf16 and lse [B, S, H] fp32."""
+    [B,S,K] -> out [B, S, H*L] bf16 and lse [B, S, H] fp32.  ``workspace`` as
+    for fwd."""
     B, S, H, L = q_lift.shape
     R = q_pe.shape[3]
     S_kv = c_kv.shape[1]
@@ -279,7 +313,8 @@ def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
         v_l = MlaRows(lse.data_ptr(), lse.stride(0), lse.stride(2), lse.stride(1))
     _check(LIB.mla_sparse_fwd(ctypes.byref(v_ql), ctypes.byref(v_qp), ctypes.byref(v_ck),
                               ctypes.byref(v_kp), topk_idx.data_ptr(), B, S, S_kv, H, L, R, K,
-                              float(scale), ctypes.byref(v_o), _ref(v_l), _stream(q_lift.device)))
+                              float(scale), ctypes.byref(v_o), _ref(v_l),
+                              *_workspace(q_lift.device, workspace), _stream(q_lift.device)))
     return out, lse
 
 

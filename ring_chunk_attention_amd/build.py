@@ -1,6 +1,6 @@
 """Build libmla355.so (HIP, gfx950) in-tree.
 
-    python -m ring_chunk_attention_amd.build [--verbose]
+    python ring_chunk_attention_amd/build.py [--verbose]
 
 Compiles every source under ``csrc/`` with hipcc for gfx950 and links them
 into ``ring_chunk_attention_amd/libmla355.so``.  Objects go to ``_build/`` at

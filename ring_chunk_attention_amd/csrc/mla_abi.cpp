@@ -26,6 +26,16 @@ mla_status fail(mla_status st, const char* fmt, ...) {
   return st;
 }
 
+// The optional workspace: the item queue's counter.
+mla_status check_workspace(void* ws, size_t bytes) {
+  if (!ws) return MLA_OK;
+  if (reinterpret_cast<uintptr_t>(ws) & 15u) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (bytes < mla::kWorkspaceBytes)
+    return fail(MLA_ERR_INVALID_ARG, "workspace_bytes (%zu) is below mla_workspace_size() (%zu)", bytes,
+                (size_t)mla::kWorkspaceBytes);
+  return MLA_OK;
+}
+
 mla_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return MLA_OK;
   return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -95,13 +105,15 @@ const char* mla_last_error(void) { return g_last_error.c_str(); }
 
 const char* mla_version(void) { return "mla355 0.1 gfx950"; }
 
+size_t mla_workspace_size(void) { return mla::kWorkspaceBytes; }
+
 mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
                    const mla_rows* k_rope, const mla_rows* v, int32_t B, int32_t Hq,
                    int32_t Hkv, int64_t Nq, int64_t Nkv, int32_t dq, int32_t dr, int32_t dv,
                    const int32_t* seq_lens, int32_t n_seqs, float scale, uint32_t flags,
                    int64_t q_offset, int64_t kv_offset, const mla_rows* prev_out,
                    const mla_rows* prev_lse, const mla_rows* out, const mla_rows* lse,
-                   void* stream) {
+                   void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   mla_status st;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nkv < 0)
@@ -112,6 +124,7 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv
   if (flags & ~(MLA_CAUSAL | MLA_OUT_F32 | MLA_PREV_OUT_F32))
     return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+  if ((st = check_workspace(workspace, workspace_bytes))) return st;
   const bool out_f32 = flags & MLA_OUT_F32, prev_f32 = flags & MLA_PREV_OUT_F32;
   if ((st = check_rows(q, "q")) || (st = check_rows(kv, "kv"))) return st;
   if ((st = out_f32 ? check_rows_f32(out, "out") : check_rows(out, "out"))) return st;
@@ -168,6 +181,7 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv
   p.causal = (flags & MLA_CAUSAL) ? 1 : 0;
   p.out_f32 = out_f32 ? 1 : 0;
   p.prev_f32 = prev_f32 ? 1 : 0;
+  p.queue = static_cast<unsigned*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   const bool latent = !v && Hkv == 1 && dq + dr == 576 && dv == 512 && (dr == 0 || dr == 64) && !seq_lens;
@@ -232,7 +246,8 @@ mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a, const mla
 mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const mla_rows* c_kv,
                           const mla_rows* k_pe, const int32_t* topk_idx, int32_t B, int64_t S,
                           int64_t S_kv, int32_t H, int32_t L, int32_t R, int32_t K, float scale,
-                          const mla_rows* out, const mla_rows* lse, void* stream) {
+                          const mla_rows* out, const mla_rows* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   mla_status st;
   if (B < 0 || S < 0 || S_kv <= 0 || H <= 0 || K <= 0)
@@ -242,6 +257,7 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
   if (K > mla::kSparseMaxTopk)
     return fail(MLA_ERR_UNSUPPORTED, "sparse kernel handles up to %d indices per query (got %d)", mla::kSparseMaxTopk, K);
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+  if ((st = check_workspace(workspace, workspace_bytes))) return st;
   if ((st = check_rows(q_lift, "q_lift")) || (st = check_rows(q_pe, "q_pe")) || (st = check_rows(out, "out")))
     return st;
   if ((st = check_rows(c_kv, "c_kv", false)) || (st = check_rows(k_pe, "k_pe", false))) return st;
@@ -267,6 +283,7 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
   p.Nkv = S_kv;
   p.topk = K;
   p.scale_log2 = scale * kLog2e;
+  p.queue = static_cast<unsigned*>(workspace);
   if (S == 0 || B == 0) return MLA_OK;
   return hip_status(mla::launch_latent_sparse(p, static_cast<hipStream_t>(stream)), "sparse attention launch");
 }

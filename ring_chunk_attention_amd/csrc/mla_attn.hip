@@ -45,6 +45,7 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <utility>
 
 namespace mla {
@@ -125,6 +126,7 @@ struct Smem {
       float wprev[ROWS];
       float wcur[ROWS];
       int flag[WAVES];
+      int item;                                         // the work item (with a queue)
     } epi;
   };
 };
@@ -319,11 +321,26 @@ void attn_fwd_kernel(const AttnParams p) {
   const int lane = tid & 63, h = lane >> 5, lr = lane & 31;
 
   // ---------------------------------------------------------------- rows
+  // Work item: latent, a block of 32 query rows of WAVES heads, longest
+  // causal rows first; sparse, one query with all its heads.  With a queue
+  // the workgroup takes the next item from a device counter instead of its
+  // own index.  The hardware hands the workgroups of a launch to the XCDs in
+  // equal shares, whatever their clocks; through the counter a faster XCD
+  // also takes items sooner, and so the longer ones, and all finish
+  // together.
+  int64_t item = blockIdx.x;
+  if constexpr (MODE == LATENT || MODE == SPARSE_PIPE) {
+    if (p.queue) {
+      if (tid == 0) sm.epi.item = (int)atomicAdd(p.queue, 1u);
+      __syncthreads();
+      item = sm.epi.item;  // (P, which shares this space, is first written past a barrier)
+    }
+  }
   Ctx cx;
   cx.t0 = 0;
   if constexpr (MODE == LATENT) {
     const int per = p.n_hgrp * p.B;
-    const int id = blockIdx.x;
+    const int id = (int)item;
     const int qblk = p.n_qblk - 1 - id / per;  // longest causal rows first
     const int rem = id % per;
     cx.hbase = (rem % p.n_hgrp) * WAVES;
@@ -364,7 +381,7 @@ void attn_fwd_kernel(const AttnParams p) {
     const int64_t last_q = min(cx.q_len - 1, cx.q0 + ROWS - 1);
     cx.kv_end = p.causal ? max<int64_t>(0, min<int64_t>(cx.kv_len, p.q_offset + last_q - p.kv_offset + 1)) : cx.kv_len;
   } else {  // SPARSE
-    const int64_t id = blockIdx.x;
+    const int64_t id = item;
     cx.b = (int)(id / p.Nq);
     cx.q0 = id % p.Nq;
     cx.hbase = 0;
@@ -1020,22 +1037,49 @@ void debug_gather_kernel(const GatherParams p) {
   }
 }
 
-}  // namespace
+__global__ void queue_reset_kernel(unsigned* q) { q[0] = 0u; }
 
-hipError_t launch_latent_dense(const AttnParams& p, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.n_qblk * p.n_hgrp * p.B;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<LatentCfg, LATENT>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+// Compute units of the current device, cached per device (0 if unknown).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// One workgroup per item of a latent or sparse kernel (each fills a CU's
+// LDS).  The item queue pays off only when the items outnumber the CUs
+// several times over (a launch that fits the chip at once has no tail to
+// balance); then the counter is reset first, on the same stream.
+template <int MODE>
+hipError_t launch_items(AttnParams p, int64_t items, hipStream_t s) {
+  const int ncu = p.queue ? cu_count() : 0;
+  if (ncu > 0 && items > 4 * (int64_t)ncu) hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(1), 0, s, p.queue);
+  else p.queue = nullptr;
+  hipLaunchKernelGGL((attn_fwd_kernel<LatentCfg, MODE>), dim3((unsigned)items), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_latent_dense(const AttnParams& p, hipStream_t s) {
+  const int64_t items = (int64_t)p.n_qblk * p.n_hgrp * p.B;
+  if (items == 0) return hipSuccess;
+  return launch_items<LATENT>(p, items, s);
+}
+
 hipError_t launch_latent_sparse(const AttnParams& p, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.B * p.Nq;
-  if (blocks == 0) return hipSuccess;
-  if (p.topk <= KMAX_IDX_PIPE)
-    hipLaunchKernelGGL((attn_fwd_kernel<LatentCfg, SPARSE_PIPE>), dim3((unsigned)blocks), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<LatentCfg, SPARSE>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const int64_t items = (int64_t)p.B * p.Nq;
+  if (items == 0) return hipSuccess;
+  if (p.topk <= KMAX_IDX_PIPE) return launch_items<SPARSE_PIPE>(p, items, s);
+  AttnParams q = p;
+  q.queue = nullptr;
+  hipLaunchKernelGGL((attn_fwd_kernel<LatentCfg, SPARSE>), dim3((unsigned)items), dim3(256), 0, s, q);
   return hipGetLastError();
 }
 

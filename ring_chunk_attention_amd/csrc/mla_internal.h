@@ -11,6 +11,10 @@ namespace mla {
 // LDS).
 constexpr int kSparseMaxTopk = 4096;
 
+// Bytes of the optional workspace (word 0: the item queue's counter; the
+// rest is reserved).
+constexpr size_t kWorkspaceBytes = 256;
+
 // A row view: element (b, h, t, d) at p[b*sb + h*sh + t*st + d] (strides in
 // elements; bf16 unless a flag says float32, in which case the pointer is
 // reinterpreted).
@@ -55,6 +59,7 @@ struct AttnParams {
   int32_t out_f32;          // out holds float32 (else bf16)
   int32_t prev_f32;         // prev_out holds float32 (else bf16)
   int32_t n_qblk, n_hgrp;   // grid factors (see each launcher)
+  unsigned* queue;          // item queue's counter, or nullptr
 };
 
 struct MergeParams {

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
 
 
 def test_library_exports_every_declared_symbol():
-    assert os.path.exists(LIB), "build the library first: python -m ring_chunk_attention_amd.build"
+    assert os.path.exists(LIB), "build the library first: python ring_chunk_attention_amd/build.py"
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT\s+(mla_\w+)", out))
     missing = [n for n in declared_functions() if n not in exported]
@@ -64,7 +64,8 @@ def rows(data=FAKE, sb=128 * 8192 * 576, sh=8192 * 576, st=576):
 
 def call_fwd(lib, q=None, kv=None, out=None, lse=None, v=None, q_rope=None, k_rope=None,
              B=1, Hq=128, Hkv=1, Nq=8192, Nkv=8192, dq=576, dr=0, dv=512, seq_lens=None, n_seqs=0,
-             scale=0.072, flags=1, q_off=0, kv_off=0, prev_out=None, prev_lse=None):
+             scale=0.072, flags=1, q_off=0, kv_off=0, prev_out=None, prev_lse=None,
+             workspace=None, workspace_bytes=0):
     from ring_chunk_attention_amd.binding import MlaRows
     def conv(r):
         return None if r is None else ctypes.byref(MlaRows(r.data, r.stride_b, r.stride_h, r.stride_t))
@@ -73,7 +74,8 @@ def call_fwd(lib, q=None, kv=None, out=None, lse=None, v=None, q_rope=None, k_ro
     out = rows(st=512) if out is None else out
     return lib.mla_fwd(conv(q), conv(q_rope), conv(kv), conv(k_rope), conv(v), B, Hq, Hkv, Nq, Nkv,
                        dq, dr, dv, seq_lens, n_seqs, scale, flags, q_off, kv_off,
-                       conv(prev_out), conv(prev_lse), conv(out), conv(lse), None)
+                       conv(prev_out), conv(prev_lse), conv(out), conv(lse), workspace, workspace_bytes,
+                       None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -92,6 +94,8 @@ def call_fwd(lib, q=None, kv=None, out=None, lse=None, v=None, q_rope=None, k_ro
     (dict(dq=256, dv=256), MLA_ERR_UNSUPPORTED, "no kernel"),
     (dict(seq_lens=FAKE, n_seqs=2, B=2), MLA_ERR_INVALID_ARG, "B == 1"),
     (dict(seq_lens=FAKE, n_seqs=2, Nkv=100), MLA_ERR_INVALID_ARG, "Nq == Nkv"),
+    (dict(workspace=FAKE + 8, workspace_bytes=256), MLA_ERR_INVALID_ARG, "16-byte aligned"),
+    (dict(workspace=FAKE, workspace_bytes=255), MLA_ERR_INVALID_ARG, "mla_workspace_size"),
 ])
 def test_fwd_rejects_invalid_arguments(lib, kw, code, msg):
     st = call_fwd(lib, **kw)
@@ -119,14 +123,26 @@ def test_sparse_rejects_unsupported_dims(lib):
     from ring_chunk_attention_amd.binding import MlaRows
     r = MlaRows(FAKE, 0, 512, 512)
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
-                            1, 16, 1024, 128, 256, 64, 128, 0.07, ctypes.byref(r), None, None)
+                            1, 16, 1024, 128, 256, 64, 128, 0.07, ctypes.byref(r), None, None, 0, None)
     assert st == MLA_ERR_UNSUPPORTED
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
-                            1, 16, 1024, 256, 512, 64, 128, 0.07, ctypes.byref(r), None, None)
+                            1, 16, 1024, 256, 512, 64, 128, 0.07, ctypes.byref(r), None, None, 0, None)
     assert st == MLA_ERR_UNSUPPORTED
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
-                            1, 16, 1024, 128, 512, 64, 4097, 0.07, ctypes.byref(r), None, None)
+                            1, 16, 1024, 128, 512, 64, 4097, 0.07, ctypes.byref(r), None, None, 0, None)
     assert st == MLA_ERR_UNSUPPORTED and "4096" in lib.mla_last_error().decode()
+
+
+def test_sparse_rejects_short_workspace(lib):
+    from ring_chunk_attention_amd.binding import MlaRows
+    r = MlaRows(FAKE, 0, 512, 512)
+    st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
+                            1, 16, 1024, 128, 512, 64, 128, 0.07, ctypes.byref(r), None, FAKE, 16, None)
+    assert st == MLA_ERR_INVALID_ARG and "workspace" in lib.mla_last_error().decode()
+
+
+def test_workspace_size(lib):
+    assert lib.mla_workspace_size() == 256
 
 
 def test_binding_raises_with_message(lib):

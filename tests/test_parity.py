@@ -408,3 +408,38 @@ def test_split_wide_range_second_pass(mla):
                                     prev_out=c.prev_out, prev_lse=c.prev_lse)
     assert report("wide split O", host(out), o_ref) <= O_TOL
     assert report("wide split LSE", host(lse), l_ref) <= LSE_TOL
+
+
+# ---------------------------------------------------------------------------
+# item queue: with a workspace, workgroups take their row blocks from a
+# device counter instead of their launch index; every block is computed the
+# same way, so the results are bit-identical
+# ---------------------------------------------------------------------------
+def test_dense_queue_bit_identical_to_launch_order(mla):
+    """B = 2, 64 heads, N = 2048: 2048 row blocks, enough for the queue."""
+    c = W.dense_case(B=2, H=64, N=2048, seed=12)
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    ws = torch.empty(int(mla.binding.LIB.mla_workspace_size()), dtype=torch.uint8, device="cuda")
+    o1, l1 = mla.fwd(q, kv, scale=c.scale, workspace=None)
+    o2, l2 = mla.fwd(q, kv, scale=c.scale, workspace=ws)
+    o3, l3 = mla.fwd(q, kv, scale=c.scale, workspace=ws)   # the counter is reset per call
+    torch.cuda.synchronize()
+    for o, l in ((o2, l2), (o3, l3)):
+        assert torch.equal(o.view(torch.int16), o1.view(torch.int16))
+        assert torch.equal(l, l1)
+    # and against the oracle on a few rows of the last batch
+    b, heads, rows = 1, [0, 63], [0, 1000, 2047]
+    for hh in heads:
+        o_ref, l_ref = oracle.dense_mla(c.q[b:b + 1, hh:hh + 1], c.kv[b:b + 1], 512, c.scale, rows=rows)
+        assert report("queue O", host(o2[b:b + 1, hh:hh + 1, rows]), o_ref) <= O_TOL
+        assert report("queue LSE", host(l2[b:b + 1, hh:hh + 1, rows]), l_ref) <= LSE_TOL
+
+
+def test_sparse_queue_bit_identical_to_launch_order(mla):
+    c = W.sparse_case(S=1100, S_kv=3000, pos0=1800, H=16, K=64, seed=13)
+    args = (dev_bf16(c.q_lift), dev_bf16(c.q_pe), dev_bf16(c.c_kv), dev_bf16(c.k_pe), dev(c.idx))
+    o1, l1 = mla.sparse_fwd(*args, scale=c.scale, workspace=None)
+    o2, l2 = mla.sparse_fwd(*args, scale=c.scale, workspace="auto")
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(l2, l1)
