@@ -318,7 +318,8 @@ void attn_fwd_kernel(const AttnParams p) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, h = lane >> 5, lr = lane & 31;
+  int lane = tid & 63, h = lane >> 5, lr = lane & 31;  // (recomputed past the key loop)
+  __builtin_assume(w >= 0 && w < WAVES);
 
   // ---------------------------------------------------------------- rows
   // Work item: latent, a block of 32 query rows of WAVES heads, longest
@@ -849,6 +850,17 @@ void attn_fwd_kernel(const AttnParams p) {
     }
   }
 
+  // Lane-derived values are recomputed here rather than held across the key
+  // loop, where the register pressure would spill them to be reloaded one
+  // after another, each reload a round trip to memory.
+  {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    lane = t & 63;
+    h = lane >> 5;
+    lr = lane & 31;
+  }
+
   // ------------------------------------------------------------- epilogue
   {
     const float l_row = xhalf_sum(l_part);
@@ -895,6 +907,28 @@ void attn_fwd_kernel(const AttnParams p) {
     static_assert(ROWS * RS <= 2 * CAP, "half of the rows fits the staging space");
     constexpr int RBP = WAVES / NPASS;        // row blocks per pass
     const uint32_t stage = lds_addr(&sm.a[0][0]);
+    // output row rl of row block rb (workgroup row 32 rb + rl) is at element
+    // out_off + rb * o_srb + rl * o_srl; it exists iff rb < o_nrb and
+    // rl < o_nrl (latent) or 32 rb + rl < o_nr (split, sparse)
+    int64_t out_off, o_srb, o_srl;
+    int o_nrb = 0, o_nrl = 0, o_nr = 0;
+    if constexpr (MODE == LATENT) {
+      out_off = cx.b * p.out.sb + cx.hbase * p.out.sh + qtok(cx.q0) * p.out.st;
+      o_srb = p.out.sh;
+      o_srl = p.out.st;
+      o_nrb = p.Hq - cx.hbase;
+      o_nrl = (int)min<int64_t>(32, cx.q_len - cx.q0);
+    } else if constexpr (MODE == SPLIT) {
+      out_off = cx.b * p.out.sb + cx.hbase * p.out.sh + qtok(cx.q0) * p.out.st;
+      o_srb = 32 * p.out.st;
+      o_srl = p.out.st;
+      o_nr = (int)min<int64_t>(ROWS, cx.q_len - cx.q0);
+    } else {
+      out_off = cx.b * p.out.sb + qtok(cx.q0) * p.out.st;
+      o_srb = 32 * p.out.sh;
+      o_srl = p.out.sh;
+      o_nr = p.Hq;
+    }
 #pragma unroll
     for (int pass_ = 0; pass_ < NPASS; ++pass_) {
 #pragma unroll
@@ -915,10 +949,19 @@ void attn_fwd_kernel(const AttnParams p) {
       }
       __syncthreads();
       // this wave stores staged rows w*RPI + k*WAVES*RPI (+ lane/LPR), k < NST,
-      // reading a batch of them from LDS before storing the batch
+      // reading a batch of them from LDS before storing the batch.  Staged
+      // row k sits in row block rb0 + k/KB of the workgroup at row
+      // rl0 + (k%KB)*WAVES*RPI of the block.
       constexpr int NST = RBP * 32 / (WAVES * RPI);
       constexpr int BATCH = NST < 8 ? NST : 8;
-      static_assert(NST % BATCH == 0, "store batches");
+      constexpr int KB = 32 / (WAVES * RPI);
+      static_assert(NST % BATCH == 0 && 32 % (WAVES * RPI) == 0, "store batches");
+      const int rb0 = pass_ * RBP, rl0 = w * RPI + lane / LPR;
+      // this lane's element address in the output, stepped along the rows in
+      // vector registers (the scalar ones are all taken here)
+      int64_t orow = out_off + (int64_t)rb0 * o_srb + (int64_t)rl0 * o_srl + (lane % LPR) * 8;
+      int64_t ostep = (int64_t)(WAVES * RPI) * o_srl, oblk = o_srb - (int64_t)KB * ostep;
+      asm volatile("" : "+v"(orow), "+v"(ostep), "+v"(oblk));
 #pragma unroll
       for (int k0 = 0; k0 < NST; k0 += BATCH) {
         u32x4 v[BATCH];
@@ -930,24 +973,10 @@ void attn_fwd_kernel(const AttnParams p) {
         }
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
-          const int rs = (w + (k0 + k) * WAVES) * RPI + lane / LPR;  // staged row
-          const int r = pass_ * RBP * 32 + rs;                        // row of the workgroup
-          const int rb = r >> 5, rl = r & 31;
-          int hq;
-          int64_t qq;
-          if constexpr (MODE == LATENT) {
-            hq = cx.hbase + rb;
-            qq = cx.q0 + rl;
-          } else if constexpr (MODE == SPLIT) {
-            hq = cx.hbase;
-            qq = cx.q0 + r;
-          } else {
-            hq = r;
-            qq = cx.q0;
-          }
-          if (hq < p.Hq && qq < cx.q_len)
-            *reinterpret_cast<u32x4*>(p.out.p + cx.b * p.out.sb + hq * p.out.sh + qtok(qq) * p.out.st +
-                                      (lane % LPR) * 8) = v[k];
+          const int kk = k0 + k, rb = rb0 + kk / KB, rl = rl0 + (kk % KB) * (WAVES * RPI);
+          const bool ok = MODE == LATENT ? rb < o_nrb && rl < o_nrl : rb * 32 + rl < o_nr;
+          if (ok) *reinterpret_cast<u32x4*>(p.out.p + orow) = v[k];
+          orow += (kk + 1) % KB ? ostep : ostep + oblk;
         }
       }
       if (NPASS > 1 && pass_ + 1 < NPASS) __syncthreads();
