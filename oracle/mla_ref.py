@@ -241,3 +241,36 @@ def sparse_mla(q_lift, q_pe, c_kv, k_pe, idx, scale: float,
             out[b, ri] = ((w @ ck) / l[:, None]).reshape(-1)
             lse[b, ri] = m + np.log(l)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# token generation: one new query per sequence over its valid cache rows
+# ---------------------------------------------------------------------------
+def decode_mla(q: np.ndarray, kv: np.ndarray, kv_lens: Optional[Sequence[int]],
+               head_dim_v: int, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """q [B, H, dk] (the newest token of each sequence), kv [B, Nkv, dk],
+    kv_lens [B] (None: Nkv for every sequence) -> out [B, H, dv], lse [B, H].
+
+    Mojo mha_single_batch_pipelined (token generation, seq_len = 1, with
+    num_keys valid cache entries per sequence): the query of sequence b is
+    its newest token, so it sees its first kv_lens[b] cache rows, every one
+    of them.  The key is the whole row and the value its first head_dim_v
+    columns, as in dense_mla.  A sequence with no valid row gets out = 0 and
+    lse = -inf.  Splitting the rows into ranges and folding the partial
+    results (merge) gives the same result; that split over the keys is the
+    page's split-K with its separate reduction.
+    """
+    B, H, dk = q.shape
+    Nkv = kv.shape[1]
+    lens = [Nkv] * B if kv_lens is None else [int(x) for x in kv_lens]
+    out = np.zeros((B, H, head_dim_v))
+    lse = np.full((B, H), NEG_INF)
+    for b in range(B):
+        n = max(0, min(Nkv, lens[b]))
+        if n == 0:
+            continue
+        k = kv[b, :n]
+        o, l = attention(q[b], k, k[:, :head_dim_v], scale, causal=False,
+                         q_pos=np.zeros(H, dtype=np.int64), k_pos=np.zeros(n, dtype=np.int64))
+        out[b], lse[b] = o, l
+    return out, lse

@@ -448,6 +448,68 @@ def test_absorbed_equals_non_absorbed():
 
 
 # ---------------------------------------------------------------------------
+# token generation (decode)
+# ---------------------------------------------------------------------------
+def test_decode_matches_brute_force():
+    rng = np.random.default_rng(60)
+    B, H, N, dk, dv = 3, 2, 6, 5, 3
+    q = _rand(rng, B, H, dk)
+    kv = _rand(rng, B, N, dk)
+    lens = [6, 3, 0]
+    out, lse = oracle.decode_mla(q, kv, lens, dv, 0.7)
+    for b in range(B):
+        n = lens[b]
+        o_bf, l_bf = brute_attention(q[b].tolist(), kv[b, :n].tolist(), kv[b, :n, :dv].tolist() or [[0.0] * dv],
+                                     0.7, False, [0] * H, [0] * n)
+        if n == 0:
+            assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b]))
+        else:
+            np.testing.assert_allclose(out[b], o_bf, atol=1e-12)
+            np.testing.assert_allclose(lse[b], l_bf, atol=1e-12)
+
+
+@pytest.mark.parametrize("L", [1, 17, 40])
+def test_decode_is_last_row_of_causal_prefill(L):
+    """The newest token's decode over the first L rows equals row L-1 of the
+    causal prefill over those rows."""
+    c = W.dense_case(B=1, H=3, N=40, seed=61)
+    o_pre, l_pre = oracle.dense_mla(c.q[:, :, :L], c.kv[:, :, :L], 512, c.scale)
+    q_new = np.ascontiguousarray(c.q[:, :, L - 1])             # [1, H, dk]
+    kv_rows = np.ascontiguousarray(c.kv[:, 0])                  # [1, N, dk]
+    o_dec, l_dec = oracle.decode_mla(q_new, kv_rows, [L], 512, c.scale)
+    np.testing.assert_allclose(o_dec[0], o_pre[0, :, L - 1], atol=1e-12)
+    np.testing.assert_allclose(l_dec[0], l_pre[0, :, L - 1], atol=1e-12)
+
+
+def test_decode_zero_scale_prefix_mean():
+    """scale 0: every visible weight is 1, so out is the mean of the first
+    len value rows and lse = ln(len)."""
+    rng = np.random.default_rng(62)
+    q = _rand(rng, 2, 4, 9)
+    kv = _rand(rng, 2, 30, 9)
+    out, lse = oracle.decode_mla(q, kv, [30, 11], 6, 0.0)
+    for b, n in enumerate([30, 11]):
+        np.testing.assert_allclose(out[b], np.broadcast_to(kv[b, :n, :6].mean(axis=0), (4, 6)), atol=1e-12)
+        np.testing.assert_allclose(lse[b], np.full(4, math.log(n)), atol=1e-12)
+
+
+@pytest.mark.parametrize("cut", [0, 1, 700, 1999, 2000])
+def test_decode_split_keys_merge_to_whole(cut):
+    """Split-K: the rows [0, cut) and [cut, len) folded through their LSE
+    give the whole result (an empty side is the fold identity)."""
+    rng = np.random.default_rng(63)
+    q = W.normal_bf16(rng, (2, 4, 576))
+    kv = W.normal_bf16(rng, (2, 2000, 576))
+    scale = W.SCALE_192
+    whole = oracle.decode_mla(q, kv, [2000, 2000], 512, scale)
+    a = oracle.decode_mla(q, kv, [cut, cut], 512, scale)
+    b = oracle.decode_mla(q, np.ascontiguousarray(kv[:, cut:]), [2000 - cut] * 2, 512, scale)
+    o, l = oracle.merge(a[0], a[1], b[0], b[1])
+    np.testing.assert_allclose(o, whole[0], atol=1e-12)
+    np.testing.assert_allclose(l, whole[1], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by a pin above
 # ---------------------------------------------------------------------------
 def _mutant_attention(kind):
@@ -501,3 +563,14 @@ def test_planted_merge_sign_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "merge", mutant)
     with pytest.raises(AssertionError):
         test_golden_merge()
+
+
+def test_planted_decode_short_by_one_is_caught(monkeypatch):
+    orig = mla_ref.decode_mla
+
+    def mutant(q, kv, kv_lens, head_dim_v, scale):
+        lens = [kv.shape[1]] * q.shape[0] if kv_lens is None else list(kv_lens)
+        return orig(q, kv, [max(0, int(n) - 1) for n in lens], head_dim_v, scale)
+    monkeypatch.setattr(oracle, "decode_mla", mutant)
+    with pytest.raises(AssertionError):
+        test_decode_zero_scale_prefix_mean()

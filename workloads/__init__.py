@@ -109,6 +109,17 @@ class SparseCase:
     name: str = ""
 
 
+@dataclass
+class DecodeCase:
+    """Token generation: the newest query of each sequence over its cache rows."""
+    q: np.ndarray          # [B, H, 576] (one query per sequence)
+    kv: np.ndarray         # [B, Nkv, 576] latent cache rows (512 latent + 64 RoPE)
+    kv_lens: np.ndarray    # int32 [B] valid rows per sequence
+    head_dim_v: int
+    scale: float
+    name: str = ""
+
+
 def dense_case(B: int = 1, H: int = 4, N: int = 128, Nkv: Optional[int] = None,
                dk: int = 576, dv: int = 512, seed: int = 0, scale: float = SCALE_192,
                causal: bool = True, q_offset: int = 0, kv_offset: int = 0,
@@ -164,7 +175,26 @@ def sparse_case(S: int = 4096, S_kv: int = 16384, pos0: int = 12288, H: int = 12
     return SparseCase(q_lift, q_pe, c_kv, k_pe, idx, pos, scale, name)
 
 
-# The five workloads the method is measured and checked on.
+def decode_case(B: int = 64, H: int = 128, Nkv: int = 8192, kv_lens: Optional[List[int]] = None,
+                len_lo: Optional[int] = None, dk: int = 576, dv: int = 512, seed: int = 0,
+                scale: float = SCALE_192, name: str = "") -> DecodeCase:
+    """q then kv drawn N(0,1) -> bf16; valid lengths as given, else drawn
+    uniformly in [len_lo, Nkv] (after the tensors) when len_lo is set, else
+    Nkv for every sequence."""
+    rng = np.random.default_rng(seed)
+    q = normal_bf16(rng, (B, H, dk))
+    kv = normal_bf16(rng, (B, Nkv, dk))
+    if kv_lens is not None:
+        lens = np.asarray(kv_lens, dtype=np.int32)
+    elif len_lo is not None:
+        lens = rng.integers(len_lo, Nkv, B, endpoint=True).astype(np.int32)
+    else:
+        lens = np.full(B, Nkv, dtype=np.int32)
+    return DecodeCase(q, kv, lens, dv, scale, name)
+
+
+# The five workloads the method is measured and checked on (and decode,
+# the next step beside them).
 def tiny(seed: int = 0) -> DenseCase:
     return dense_case(B=1, H=4, N=128, seed=seed, name="tiny causal MLA H=4 N=128")
 
@@ -185,3 +215,8 @@ def split_ring_step(seed: int = 0) -> SplitCase:
 
 def sparse_topk(seed: int = 0) -> SparseCase:
     return sparse_case(seed=seed, name="sparse top-k MLA S=4096 S_kv=16384 H=128 K=2048")
+
+
+def dsv3_decode(seed: int = 0) -> DecodeCase:
+    return decode_case(B=64, H=128, Nkv=8192, seed=seed,
+                       name="DeepSeek-V3 absorbed MLA decode B=64 H=128 KV=8192")
