@@ -197,6 +197,56 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe,
                           void* stream /* hipStream_t */);
 
 /*
+ * mla_decode_fwd -- token generation: one new query per sequence over its
+ * valid cache rows, with the rows split into ranges processed in parallel
+ * and a separate reduction (Mojo mha_single_batch_pipelined: seq_len = 1,
+ * num_keys valid entries per sequence; the split over the keys "will need a
+ * separate reduction kernel at the end").
+ *
+ * q [B, H, dq] plus, optionally, q_rope [B, H, dr]: the newest token of each
+ * sequence (views with b = sequence, h = head; stride_t is ignored).
+ * kv [B, Nkv, dq] plus, optionally, k_rope [B, Nkv, dr]: the latent cache
+ * (views with t = cache row; stride_h is ignored).  kv_lens: device int32
+ * [B], the valid rows of each sequence (clamped to [0, Nkv]), or NULL for
+ * Nkv everywhere.  Sequence b's query sees its first kv_lens[b] rows, all of
+ * them; the score is scale * q.row over dq + dr columns, the value the first
+ * dv columns of the row.
+ *
+ * out [B, H, dv] bf16 and lse [B, H] fp32 natural-log LSE (or NULL), views
+ * with stride_t ignored.  A sequence with no valid row gets out = 0 and
+ * lse = -inf.
+ *
+ * n_splits: key ranges per sequence, or 0 for the library's choice; a range
+ * holds at most 2048 rows and there are at most 64 (Nkv <= 131072).  With
+ * more than one range, each writes an fp32 partial result (output and LSE)
+ * and a reduction kernel folds them through their LSE; with one, the
+ * attention kernel writes out and lse itself.  Results do not depend on
+ * the split beyond rounding.
+ *
+ * workspace: device memory of at least
+ * mla_decode_workspace_size(B, H, Nkv, n_splits) bytes, 256-byte aligned,
+ * given as workspace_bytes (required): the partial results and the item
+ * queue's counter.  It needs no initialisation; calls that may run at the
+ * same time need distinct workspaces.
+ *
+ * Kernels exist for dq + dr == 576 (dr == 0 or 64), dv == 512, H <= 128;
+ * other shapes return MLA_ERR_UNSUPPORTED.
+ */
+mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope,
+                          const mla_rows* kv, const mla_rows* k_rope,
+                          const int32_t* kv_lens,
+                          int32_t B, int32_t H, int64_t Nkv,
+                          int32_t dq, int32_t dr, int32_t dv, float scale,
+                          int32_t n_splits,
+                          const mla_rows* out, const mla_rows* lse,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream /* hipStream_t */);
+
+/* Bytes of the workspace mla_decode_fwd needs for these sizes (0 if no split
+ * fits: n_splits too small for Nkv, or Nkv > 131072). */
+size_t mla_decode_workspace_size(int32_t B, int32_t H, int64_t Nkv, int32_t n_splits);
+
+/*
  * mla_debug_gather -- test export.  Gathers the top-k rows of one query's
  * index list through the same device tile loader mla_sparse_fwd uses (with
  * its LDS swizzle undone on the way out): rows_out [K, L + R] bf16 contiguous,

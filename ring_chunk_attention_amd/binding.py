@@ -65,14 +65,22 @@ def _load():
     lib.mla_version.argtypes = []
     lib.mla_workspace_size.restype = ctypes.c_size_t
     lib.mla_workspace_size.argtypes = []
+    lib.mla_decode_fwd.restype = ctypes.c_int
+    lib.mla_decode_fwd.argtypes = [_P, _P, _P, _P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_decode_workspace_size.restype = ctypes.c_size_t
+    lib.mla_decode_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                              ctypes.c_int32]
     return lib
 
 
 LIB = _load()
 LIB_PATH = _LIB_PATH
 
-EXPORTS = ("mla_fwd", "mla_merge_lse", "mla_sparse_fwd", "mla_debug_gather",
-           "mla_last_error", "mla_version", "mla_workspace_size")
+EXPORTS = ("mla_fwd", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd", "mla_debug_gather",
+           "mla_last_error", "mla_version", "mla_workspace_size", "mla_decode_workspace_size")
 
 
 class MlaError(RuntimeError):
@@ -315,6 +323,68 @@ def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
                               ctypes.byref(v_kp), topk_idx.data_ptr(), B, S, S_kv, H, L, R, K,
                               float(scale), ctypes.byref(v_o), _ref(v_l),
                               *_workspace(q_lift.device, workspace), _stream(q_lift.device)))
+    return out, lse
+
+
+# Decode workspaces, one per (device, stream), grown to the largest call.
+_DECODE_WS = {}
+
+
+def decode_fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float,
+               kv_lens: Optional[torch.Tensor] = None, head_dim_v: int = 512,
+               q_rope: Optional[torch.Tensor] = None, k_rope: Optional[torch.Tensor] = None,
+               n_splits: int = 0, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+               workspace: Optional[torch.Tensor] = None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Token generation (mla_decode_fwd): q [B, H, dq] (the newest token of
+    each sequence), kv [B, Nkv, dq] (the latent cache), optional q_rope
+    [B, H, dr] / k_rope [B, Nkv, dr], kv_lens int32 [B] on the GPU (valid
+    rows; None = Nkv).  Returns (out [B, H, dv] bf16, lse [B, H] fp32 or
+    None).  n_splits = 0 lets the library split the keys; ``workspace`` (a
+    uint8 GPU tensor) defaults to a cached per-stream buffer."""
+    B, H, dq = q.shape
+    Nkv = kv.shape[1]
+    dr = 0 if q_rope is None else q_rope.shape[-1]
+    dv = head_dim_v
+    for t, n in ((q, "q"), (kv, "kv")) + (((q_rope, "q_rope"), (k_rope, "k_rope")) if dr else ()):
+        _need(t, n, torch.bfloat16)
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{n}: expected a 3-D tensor with a contiguous last dim")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    if kv_lens is not None:
+        _need(kv_lens, "kv_lens", torch.int32)
+        if kv_lens.shape != (B,) or not kv_lens.is_contiguous():
+            raise ValueError("kv_lens: expected a contiguous [B] tensor")
+    need = int(LIB.mla_decode_workspace_size(B, H, Nkv, n_splits))
+    if need == 0:
+        raise MlaError(2, f"no key split fits Nkv={Nkv} with n_splits={n_splits}")
+    if workspace is None:
+        key = (q.device.index if q.device.index is not None else torch.cuda.current_device(),
+               torch.cuda.current_stream(q.device).cuda_stream)
+        workspace = _DECODE_WS.get(key)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            _DECODE_WS[key] = workspace
+    _need(workspace, "workspace", torch.uint8)
+    vq = MlaRows(q.data_ptr(), q.stride(0), q.stride(1), 0)
+    vkv = MlaRows(kv.data_ptr(), kv.stride(0), 0, kv.stride(1))
+    vqr = MlaRows(q_rope.data_ptr(), q_rope.stride(0), q_rope.stride(1), 0) if dr else None
+    vkr = MlaRows(k_rope.data_ptr(), k_rope.stride(0), 0, k_rope.stride(1)) if dr else None
+    vo = MlaRows(out.data_ptr(), out.stride(0), out.stride(1), 0)
+    vl = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+        vl = MlaRows(lse.data_ptr(), lse.stride(0), lse.stride(1), 0)
+    _check(LIB.mla_decode_fwd(ctypes.byref(vq), _ref(vqr), ctypes.byref(vkv), _ref(vkr),
+                              kv_lens.data_ptr() if kv_lens is not None else None,
+                              B, H, Nkv, dq, dr, dv, float(scale), n_splits,
+                              ctypes.byref(vo), _ref(vl), workspace.data_ptr(), workspace.numel(),
+                              _stream(q.device)))
     return out, lse
 
 

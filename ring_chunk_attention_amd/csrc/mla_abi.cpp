@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -34,6 +35,47 @@ mla_status check_workspace(void* ws, size_t bytes) {
     return fail(MLA_ERR_INVALID_ARG, "workspace_bytes (%zu) is below mla_workspace_size() (%zu)", bytes,
                 (size_t)mla::kWorkspaceBytes);
   return MLA_OK;
+}
+
+// Token generation: keys per split (`chunk`, a multiple of the 32-row tile,
+// at most the sparse kernel's 2048-entry list) and splits per sequence.  The
+// library's choice (req == 0) aims at 512 work items (two per compute unit
+// of an MI355X) with at least 256 rows per split, where a split's fixed cost
+// (loading 128 query rows, writing a 256 KB fp32 partial) stays small beside
+// its key loop.  Returns false if no choice fits (more than 64 splits).
+bool decode_split(int32_t B, int64_t Nkv, int32_t req, int32_t* S, int32_t* chunk) {
+  constexpr int64_t kMaxChunk = 2048, kMinChunk = 256, kMaxSplits = 64, kTargetItems = 512;
+  const int64_t n = Nkv > 0 ? Nkv : 1;
+  int64_t s;
+  if (req > 0) {
+    s = req;
+  } else {
+    const int64_t s_min = (n + kMaxChunk - 1) / kMaxChunk;
+    const int64_t s_fill = B > 0 ? (kTargetItems + B - 1) / B : 1;
+    const int64_t s_cap = std::max<int64_t>(1, (n + kMinChunk - 1) / kMinChunk);
+    s = std::max(s_min, std::min(s_fill, s_cap));
+  }
+  int64_t c = (n + s - 1) / s;
+  c = (c + 31) / 32 * 32;
+  if (c > kMaxChunk) return false;
+  s = (n + c - 1) / c;
+  if (s > kMaxSplits) return false;
+  *S = (int32_t)s;
+  *chunk = (int32_t)c;
+  return true;
+}
+
+// Decode workspace: the queue counter, then (S > 1) the partial LSEs and
+// the fp32 partial outputs, each 256-byte aligned.
+size_t decode_ws_bytes(int32_t B, int32_t H, int32_t S, int32_t dv, size_t* off_l, size_t* off_o) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  *off_l = 256;
+  if (S <= 1) {
+    *off_o = 256;
+    return 256;
+  }
+  *off_o = *off_l + up((size_t)B * S * H * sizeof(float));
+  return *off_o + up((size_t)B * S * H * dv * sizeof(float));
 }
 
 mla_status hip_status(hipError_t e, const char* what) {
@@ -286,6 +328,104 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
   p.queue = static_cast<unsigned*>(workspace);
   if (S == 0 || B == 0) return MLA_OK;
   return hip_status(mla::launch_latent_sparse(p, static_cast<hipStream_t>(stream)), "sparse attention launch");
+}
+
+size_t mla_decode_workspace_size(int32_t B, int32_t H, int64_t Nkv, int32_t n_splits) {
+  int32_t S = 0, chunk = 0;
+  if (B < 0 || H <= 0 || Nkv < 0 || n_splits < 0 || !decode_split(B, Nkv, n_splits, &S, &chunk)) return 0;
+  size_t ol, oo;
+  return decode_ws_bytes(B, H, S, 512, &ol, &oo);
+}
+
+mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
+                          const mla_rows* k_rope, const int32_t* kv_lens, int32_t B, int32_t H,
+                          int64_t Nkv, int32_t dq, int32_t dr, int32_t dv, float scale,
+                          int32_t n_splits, const mla_rows* out, const mla_rows* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mla_status st;
+  if (B < 0 || H <= 0 || Nkv < 0 || n_splits < 0)
+    return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, H > 0, Nkv >= 0, n_splits >= 0");
+  if (dq + dr != 576 || dv != 512 || !(dr == 0 || dr == 64))
+    return fail(MLA_ERR_UNSUPPORTED, "decode is built for dq + dr = 576 (dr = 0 or 64), dv = 512 (got %d, %d, %d)",
+                dq, dr, dv);
+  if (H > 128) return fail(MLA_ERR_UNSUPPORTED, "decode handles up to 128 heads per sequence (got %d)", H);
+  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+  if ((q_rope == nullptr) != (k_rope == nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "q_rope and k_rope must both be given or both be NULL");
+  if ((q_rope == nullptr) != (dr == 0))
+    return fail(MLA_ERR_INVALID_ARG, "dr must be 0 exactly when q_rope/k_rope are NULL");
+  if ((st = check_rows(q, "q", true)) || (st = check_rows(kv, "kv", false)) || (st = check_rows(out, "out")))
+    return st;
+  if (q_rope && ((st = check_rows(q_rope, "q_rope")) || (st = check_rows(k_rope, "k_rope", false)))) return st;
+  if (lse && (st = check_lse(lse, "lse"))) return st;
+  if (kv_lens && (reinterpret_cast<uintptr_t>(kv_lens) & 3u))
+    return fail(MLA_ERR_INVALID_ARG, "kv_lens must be 4-byte aligned");
+  if (Nkv * kv->stride_t * 2 > kMaxGrid || (k_rope && Nkv * k_rope->stride_t * 2 > kMaxGrid))
+    return fail(MLA_ERR_UNSUPPORTED, "one sequence of the cache must span less than 2 GiB (row offsets are 32-bit)");
+  int32_t S = 0, chunk = 0;
+  if (!decode_split(B, Nkv, n_splits, &S, &chunk))
+    return fail(n_splits > 0 ? MLA_ERR_INVALID_ARG : MLA_ERR_UNSUPPORTED,
+                "no split of %lld rows fits (at most 64 splits of at most 2048 rows; n_splits = %d)",
+                (long long)Nkv, n_splits);
+  size_t off_l, off_o;
+  const size_t need = decode_ws_bytes(B, H, S, dv, &off_l, &off_o);
+  if (!workspace) return fail(MLA_ERR_INVALID_ARG, "decode needs a workspace of mla_decode_workspace_size() bytes");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_INVALID_ARG, "workspace_bytes (%zu) is below mla_decode_workspace_size() (%zu)",
+                workspace_bytes, need);
+  if ((int64_t)B * S > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (B == 0) return MLA_OK;
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* part_l = reinterpret_cast<float*>(ws + off_l);
+  float* part_o = reinterpret_cast<float*>(ws + off_o);
+  mla::AttnParams p{};
+  // one query per sequence: the t stride is 0, so every split of a sequence
+  // reads the same query row
+  p.qa = mla::RowsC{static_cast<const uint16_t*>(q->data), q->stride_b, q->stride_h, 0};
+  p.qb = q_rope ? mla::RowsC{static_cast<const uint16_t*>(q_rope->data), q_rope->stride_b, q_rope->stride_h, 0}
+                : mla::RowsC{p.qa.p + (dq - 64), q->stride_b, q->stride_h, 0};
+  p.ka = mla::RowsC{static_cast<const uint16_t*>(kv->data), kv->stride_b, 0, kv->stride_t};
+  p.kb = k_rope ? mla::RowsC{static_cast<const uint16_t*>(k_rope->data), k_rope->stride_b, 0, k_rope->stride_t}
+                : mla::RowsC{p.ka.p + (dq - 64), kv->stride_b, 0, kv->stride_t};
+  p.da = dr == 0 ? dq - 64 : dq;
+  p.B = B;
+  p.Hq = H;
+  p.group = H;
+  p.Nq = S;        // the items of a sequence are its splits
+  p.Nkv = Nkv;
+  p.topk = chunk;
+  p.scale_log2 = scale * kLog2e;
+  p.decode = 1;
+  p.kv_lens = kv_lens;
+  p.queue = reinterpret_cast<unsigned*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mla::RowsM o_final{static_cast<uint16_t*>(out->data), out->stride_b, out->stride_h, 0};
+  const mla::LseM l_final{lse ? static_cast<float*>(lse->data) : nullptr, lse ? lse->stride_b : 0,
+                          lse ? lse->stride_h : 0, 0};
+  if (S == 1) {
+    p.out = o_final;
+    p.lse = l_final;
+    return hip_status(mla::launch_decode(p, B, s), "decode launch");
+  }
+  // split s of sequence b writes its fp32 partial at ((b * S + s) * H + h) * dv
+  p.out = mla::RowsM{reinterpret_cast<uint16_t*>(part_o), (int64_t)S * H * dv, dv, (int64_t)H * dv};
+  p.out_f32 = 1;
+  p.lse = mla::LseM{part_l, (int64_t)S * H, 1, H};
+  if ((st = hip_status(mla::launch_decode(p, (int64_t)B * S, s), "decode launch"))) return st;
+  mla::CombineParams c{};
+  c.po = part_o;
+  c.pl = part_l;
+  c.B = B;
+  c.H = H;
+  c.S = S;
+  c.dv = dv;
+  c.out = o_final;
+  c.lse = l_final;
+  return hip_status(mla::launch_combine(c, s), "decode combine launch");
 }
 
 mla_status mla_debug_gather(const mla_rows* c_kv, const mla_rows* k_pe, const int32_t* idx, int32_t b,

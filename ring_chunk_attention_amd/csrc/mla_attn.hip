@@ -389,6 +389,11 @@ void attn_fwd_kernel(const AttnParams p) {
     cx.q_len = p.Nq;
     cx.kv_len = p.topk;
     cx.kv_end = p.topk;
+    if (p.decode) {  // the part of split q0's range inside the valid rows
+      int64_t len = p.kv_lens ? (int64_t)p.kv_lens[cx.b] : p.Nkv;
+      len = max<int64_t>(0, min<int64_t>(len, p.Nkv));
+      cx.kv_len = cx.kv_end = max<int64_t>(0, min<int64_t>(p.topk, len - cx.q0 * p.topk));
+    }
   }
 
   auto row_head = [&](int rb) -> int {
@@ -426,8 +431,13 @@ void attn_fwd_kernel(const AttnParams p) {
   const uint32_t stA = (uint32_t)(p.ka.st * 2), stB = (uint32_t)(p.kb.st * 2), stV = (uint32_t)(p.v.st * 2);
 
   if constexpr (SP) {  // stage the query's index list in LDS
-    const int32_t* idx_row = p.idx + ((int64_t)cx.b * p.Nq + cx.q0) * p.topk;
-    for (int k = tid; k < p.topk; k += 256) sm.idx[k] = idx_row[k];
+    if (p.decode) {    // token generation: the rows of split q0, -1 past the valid ones
+      const int s0 = (int)(cx.q0 * p.topk), n = (int)cx.kv_end;
+      for (int k = tid; k < p.topk; k += 256) sm.idx[k] = k < n ? s0 + k : -1;
+    } else {
+      const int32_t* idx_row = p.idx + ((int64_t)cx.b * p.Nq + cx.q0) * p.topk;
+      for (int k = tid; k < p.topk; k += 256) sm.idx[k] = idx_row[k];
+    }
     __syncthreads();
   }
   auto idx_ok = [&](int r) -> bool { return r >= 0 && r < p.Nkv; };
@@ -1110,6 +1120,11 @@ hipError_t launch_latent_sparse(const AttnParams& p, hipStream_t s) {
   q.queue = nullptr;
   hipLaunchKernelGGL((attn_fwd_kernel<LatentCfg, SPARSE>), dim3((unsigned)items), dim3(256), 0, s, q);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const AttnParams& p, int64_t items, hipStream_t s) {
+  if (items == 0) return hipSuccess;
+  return launch_items<SPARSE_PIPE>(p, items, s);
 }
 
 hipError_t launch_split(const AttnParams& p, hipStream_t s) {

@@ -60,6 +60,21 @@ struct AttnParams {
   int32_t prev_f32;         // prev_out holds float32 (else bf16)
   int32_t n_qblk, n_hgrp;   // grid factors (see each launcher)
   unsigned* queue;          // item queue's counter, or nullptr
+  // token generation (sparse kernel): each item's list is the range
+  // [q0 * topk, (q0 + 1) * topk) of its sequence's valid cache rows
+  int32_t decode;
+  const int32_t* kv_lens;   // decode: valid rows per sequence [B], or nullptr (Nkv)
+};
+
+// Decode split-K reduction: partial results of S key ranges per (b, h),
+// element (b, s, h, d) of po at ((b * S + s) * H + h) * dv + d and its LSE
+// at pl[(b * S + s) * H + h].
+struct CombineParams {
+  const float* po;
+  const float* pl;
+  int32_t B, H, S, dv;
+  RowsM out;                // [B, H, dv] bf16 (t unused)
+  LseM lse;                 // [B, H] or nullptr
 };
 
 struct MergeParams {
@@ -85,6 +100,8 @@ hipError_t launch_latent_dense(const AttnParams& p, hipStream_t s);
 hipError_t launch_latent_sparse(const AttnParams& p, hipStream_t s);
 hipError_t launch_split(const AttnParams& p, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_decode(const AttnParams& p, int64_t items, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_debug_gather(const GatherParams& p, hipStream_t s);
 
 }  // namespace mla

@@ -76,7 +76,61 @@ void merge_kernel(const MergeParams p) {
   if (lane == 0 && p.lse.p) p.lse.p[b * p.lse.sb + hh * p.lse.sh + t * p.lse.st] = L;
 }
 
+// Split-K reduction of token generation (Mojo mha_single_batch_pipelined: a
+// split over the keys needs a separate reduction kernel at the end): for
+// each (b, h), L = log sum_s exp(L_s) and out = sum_s exp(L_s - L) O_s over
+// the S partial results (a partial with L_s = -inf has weight 0 and is not
+// read).  HBM-bound: one wave per row; lane s holds split s's LSE for the
+// wave reductions, then each lane sums 8 columns over the splits (two
+// 16-byte reads per split, a coalesced 2 KB per split and row).
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void combine_kernel(const CombineParams p) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= (int64_t)p.B * p.H) return;  // whole wave
+  const int64_t b = row / p.H, hh = row % p.H;
+  const float ls = lane < p.S ? p.pl[(b * p.S + lane) * p.H + hh] : -INFINITY;
+  float mx = ls;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float e = ls == -INFINITY ? 0.f : expf(ls - mx);
+  float z = e;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+  const bool live = mx != -INFINITY;
+  const float L = live ? mx + logf(z) : -INFINITY;
+  const float wgt = live ? e / z : 0.f;  // this lane's split's weight
+  uint16_t* ro = p.out.p + b * p.out.sb + hh * p.out.sh;
+  for (int c = lane; c * 8 < p.dv; c += 64) {
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = 0.f;
+    for (int sp = 0; sp < p.S; ++sp) {
+      const float ws = __shfl(wgt, sp);
+      if (ws == 0.f) continue;  // wave-uniform
+      const f32x4* src = reinterpret_cast<const f32x4*>(p.po + ((b * p.S + sp) * p.H + hh) * p.dv + c * 8);
+      const f32x4 a = src[0], a2 = src[1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        y[k] += ws * a[k];
+        y[4 + k] += ws * a2[k];
+      }
+    }
+    u32x4 o = {pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7])};
+    *reinterpret_cast<u32x4*>(ro + c * 8) = o;
+  }
+  if (lane == 0 && p.lse.p) p.lse.p[b * p.lse.sb + hh * p.lse.sh] = L;
+}
+
 }  // namespace
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.H;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.H * p.N;

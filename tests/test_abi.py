@@ -150,3 +150,42 @@ def test_binding_raises_with_message(lib):
     call_fwd(lib, Hq=6, Hkv=4)
     with pytest.raises(MlaError, match="multiple of Hkv"):
         _check(MLA_ERR_INVALID_ARG)
+
+
+def call_decode(lib, q=None, kv=None, out=None, lse=None, kv_lens=None, B=4, H=128, Nkv=8192, dq=576,
+                dr=0, dv=512, scale=0.072, n_splits=0, workspace=0x20000000, workspace_bytes=1 << 40):
+    from ring_chunk_attention_amd.binding import MlaRows
+    def conv(r):
+        return None if r is None else ctypes.byref(MlaRows(r.data, r.stride_b, r.stride_h, r.stride_t))
+    q = rows(sb=128 * 576, sh=576, st=0) if q is None else q
+    kv = rows(sb=8192 * 576, sh=0, st=576) if kv is None else kv
+    out = rows(sb=128 * 512, sh=512, st=0) if out is None else out
+    return lib.mla_decode_fwd(conv(q), None, conv(kv), None, kv_lens, B, H, Nkv, dq, dr, dv, scale, n_splits,
+                              conv(out), conv(lse), workspace, workspace_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(H=0), MLA_ERR_INVALID_ARG, "sizes"),
+    (dict(H=129), MLA_ERR_UNSUPPORTED, "128 heads"),
+    (dict(dq=512), MLA_ERR_UNSUPPORTED, "576"),
+    (dict(dv=256), MLA_ERR_UNSUPPORTED, "576"),
+    (dict(scale=float("inf")), MLA_ERR_INVALID_ARG, "scale"),
+    (dict(workspace=None), MLA_ERR_INVALID_ARG, "needs a workspace"),
+    (dict(workspace=0x20000010), MLA_ERR_INVALID_ARG, "256-byte aligned"),
+    (dict(workspace_bytes=1024), MLA_ERR_INVALID_ARG, "mla_decode_workspace_size"),
+    (dict(n_splits=2), MLA_ERR_INVALID_ARG, "no split"),          # 4096 rows a split > 2048
+    (dict(Nkv=200000), MLA_ERR_UNSUPPORTED, "no split"),          # > 64 splits of 2048
+    (dict(kv_lens=FAKE + 2), MLA_ERR_INVALID_ARG, "kv_lens"),
+])
+def test_decode_rejects_invalid_arguments(lib, kw, code, msg):
+    assert call_decode(lib, **kw) == code
+    assert msg in lib.mla_last_error().decode()
+
+
+def test_decode_workspace_size(lib):
+    # one split: just the queue counter
+    assert lib.mla_decode_workspace_size(1, 128, 200, 1) == 256
+    # B=64, 8192 rows: 8 splits of 1024 -> LSE 64*8*128*4 B, partials 64*8*128*512*4 B
+    assert lib.mla_decode_workspace_size(64, 128, 8192, 0) == 256 + 64 * 8 * 128 * 4 + 64 * 8 * 128 * 512 * 4
+    assert lib.mla_decode_workspace_size(4, 128, 8192, 2) == 0      # a split would exceed 2048 rows
+    assert lib.mla_decode_workspace_size(4, 128, 200000, 0) == 0    # beyond 64 splits

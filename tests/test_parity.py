@@ -443,3 +443,53 @@ def test_sparse_queue_bit_identical_to_launch_order(mla):
     torch.cuda.synchronize()
     assert torch.equal(o2.view(torch.int16), o1.view(torch.int16))
     assert torch.equal(l2, l1)
+
+
+# ---------------------------------------------------------------------------
+# token generation (decode) with the keys split across workgroups
+# ---------------------------------------------------------------------------
+def _decode_gpu(mla, c, **kw):
+    out, lse = mla.decode_fwd(dev_bf16(c.q), dev_bf16(c.kv), scale=c.scale,
+                              kv_lens=dev(c.kv_lens), **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("B,H,Nkv,lens,n_splits", [
+    (5, 128, 3000, [0, 1, 33, 2049, 3000], 0),    # library's split: 12 ranges of 256
+    (5, 128, 3000, [0, 1, 33, 2049, 3000], 2),    # 2 ranges of 1504
+    (3, 128, 2000, [2000, 700, 31], 1),           # one range: the attention kernel writes out
+    (4, 16, 1100, [1100, 1, 500, 1099], 0),       # fewer heads
+    (2, 128, 9000, [9000, 4500], 0),              # more than 2048 rows: several ranges at least
+])
+def test_decode_small(mla, B, H, Nkv, lens, n_splits):
+    c = W.decode_case(B=B, H=H, Nkv=Nkv, kv_lens=lens, seed=70 + B + Nkv)
+    out, lse = _decode_gpu(mla, c, n_splits=n_splits)
+    o_ref, l_ref = oracle.decode_mla(c.q, c.kv, c.kv_lens, 512, c.scale)
+    assert report("decode O", host(out), o_ref) <= O_TOL
+    assert report("decode LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_decode_split_rope_tensors_bit_identical(mla):
+    """q/kv as one 576-column tensor or as 512 + 64 column tensors: the same
+    bits."""
+    c = W.decode_case(B=3, H=128, Nkv=1500, kv_lens=[1500, 900, 64], seed=75)
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    lens = dev(c.kv_lens)
+    o1, l1 = mla.decode_fwd(q, kv, scale=c.scale, kv_lens=lens)
+    o2, l2 = mla.decode_fwd(q[..., :512].contiguous(), kv[..., :512].contiguous(), scale=c.scale, kv_lens=lens,
+                            q_rope=q[..., 512:].contiguous(), k_rope=kv[..., 512:].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_decode_config_sampled(mla):
+    """B = 64 sequences, 128 heads, 8192 cache rows each (the benchmarked
+    launch: 8 ranges of 1024 per sequence): sampled sequences, all heads."""
+    c = W.dsv3_decode(0)
+    out, lse = _decode_gpu(mla, c)
+    seqs = [0, 31, 63]
+    o_ref, l_ref = oracle.decode_mla(c.q[seqs], c.kv[seqs], c.kv_lens[seqs], 512, c.scale)
+    assert report("decode cfg O", host(out[seqs]), o_ref) <= O_TOL
+    assert report("decode cfg LSE", host(lse[seqs]), l_ref) <= LSE_TOL
