@@ -11,7 +11,8 @@ algorithmic flops: visible (query, head, key) triples x (2*dk + 2*dv).
 Rank 0 prints ONE JSON line with the headline, its roofline against the
 dense bf16 MFMA peak, the fp64 CPU oracle timed on a bounded sample of the
 same workload, and measured lines for the other steps of the path (one-device
-ring with LSE folds, split varlen ring step, sparse top-k, standalone merge).
+ring with LSE folds, split varlen ring step, sparse top-k, standalone merge,
+token-generation decode).
 """
 from __future__ import annotations
 
@@ -370,6 +371,27 @@ def measure_rows(mla, W, to_dev, steps, warmup):
         "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
         "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
         "gather_GBps": round(gathered / ms / 1e6, 1)}
+    del t, idx, so, sL
+
+    # token generation: 64 sequences x 128 heads, 8192 cache rows each, the
+    # keys split across workgroups (4 ranges of 2048) and reduced through LSE
+    print("bench: decode workload", file=sys.stderr, flush=True)
+    c = W.dsv3_decode(0)
+    q, kv, lens = to_dev(c.q), to_dev(c.kv), torch.from_numpy(c.kv_lens).cuda()
+    B, H = c.q.shape[:2]
+    do = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+    dl = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ms, _, _ = time_launches(lambda: mla.decode_fwd(q, kv, scale=c.scale, kv_lens=lens, out=do, lse=dl),
+                             steps, warmup)
+    keys = int(c.kv_lens.astype(np.int64).sum())
+    fl = H * keys * 2176
+    # algorithmic HBM bytes: each cache row once, the queries, outputs and LSEs
+    nbytes = keys * 576 * 2 + B * H * 576 * 2 + B * H * 512 * 2 + B * H * 4
+    rows["decode_b64_kv8192_h128"] = {
+        "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+        "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+        "GBps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+        "bytes": nbytes}
     return rows
 
 

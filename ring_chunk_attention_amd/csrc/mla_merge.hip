@@ -79,8 +79,7 @@ void merge_kernel(const MergeParams p) {
 // Split-K reduction of token generation (Mojo mha_single_batch_pipelined: a
 // split over the keys needs a separate reduction kernel at the end): for
 // each (b, h), L = log sum_s exp(L_s) and out = sum_s exp(L_s - L) O_s over
-// the S partial results (a partial with L_s = -inf has weight 0 and is not
-// read).  HBM-bound: one wave per row; lane s holds split s's LSE for the
+// the S partial results (a partial with L_s = -inf has weight 0).  HBM-bound: one wave per row; lane s holds split s's LSE for the
 // wave reductions, then each lane sums 8 columns over the splits (two
 // 16-byte reads per split, a coalesced 2 KB per split and row).
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
@@ -106,11 +105,16 @@ void combine_kernel(const CombineParams p) {
     float y[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) y[k] = 0.f;
+    // every partial row is written by the attention kernel (an empty range
+    // as 0 with weight 0), so the loop reads them all, four splits' loads
+    // in flight at a time
+    const float* src = p.po + (b * p.S * p.H + hh) * p.dv + c * 8;
+    const int64_t sstep = (int64_t)p.H * p.dv;
+#pragma unroll 4
     for (int sp = 0; sp < p.S; ++sp) {
       const float ws = __shfl(wgt, sp);
-      if (ws == 0.f) continue;  // wave-uniform
-      const f32x4* src = reinterpret_cast<const f32x4*>(p.po + ((b * p.S + sp) * p.H + hh) * p.dv + c * 8);
-      const f32x4 a = src[0], a2 = src[1];
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src + sp * sstep);
+      const f32x4 a2 = *reinterpret_cast<const f32x4*>(src + sp * sstep + 4);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         y[k] += ws * a[k];

@@ -185,7 +185,7 @@ def test_decode_rejects_invalid_arguments(lib, kw, code, msg):
 def test_decode_workspace_size(lib):
     # one split: just the queue counter
     assert lib.mla_decode_workspace_size(1, 128, 200, 1) == 256
-    # B=64, 8192 rows: 8 splits of 1024 -> LSE 64*8*128*4 B, partials 64*8*128*512*4 B
-    assert lib.mla_decode_workspace_size(64, 128, 8192, 0) == 256 + 64 * 8 * 128 * 4 + 64 * 8 * 128 * 512 * 4
+    # B=64, 8192 rows: 4 splits of 2048 -> LSE 64*4*128*4 B, partials 64*4*128*512*4 B
+    assert lib.mla_decode_workspace_size(64, 128, 8192, 0) == 256 + 64 * 4 * 128 * 4 + 64 * 4 * 128 * 512 * 4
     assert lib.mla_decode_workspace_size(4, 128, 8192, 2) == 0      # a split would exceed 2048 rows
     assert lib.mla_decode_workspace_size(4, 128, 200000, 0) == 0    # beyond 64 splits

@@ -486,7 +486,7 @@ def test_decode_split_rope_tensors_bit_identical(mla):
 
 def test_decode_config_sampled(mla):
     """B = 64 sequences, 128 heads, 8192 cache rows each (the benchmarked
-    launch: 8 ranges of 1024 per sequence): sampled sequences, all heads."""
+    launch: 4 ranges of 2048 per sequence): sampled sequences, all heads."""
     c = W.dsv3_decode(0)
     out, lse = _decode_gpu(mla, c)
     seqs = [0, 31, 63]
