@@ -149,6 +149,38 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope,
                    void* stream /* hipStream_t */);
 
 /*
+ * mla_fwd_group -- up to MLA_MAX_GROUP shared-latent mla_fwd calls in one
+ * launch: one ring step for every query chunk at once (TT-NN ring_mla, the
+ * ring's steps; Ascend RingMLAOperation, one call per ring step).  Each call
+ * computes exactly what mla_fwd computes with the same arguments (the
+ * shared-latent form: v == NULL, Hkv == 1, no seq_lens; no workspace); the
+ * calls must not write memory another call of the group reads or writes.
+ * Calls are validated in order before anything is launched; the first
+ * failure returns its status, and mla_last_error() names the call.  A call
+ * with no rows is skipped; n == 0 launches nothing.
+ */
+#define MLA_MAX_GROUP 4
+
+typedef struct {
+  const mla_rows* q;            /* as mla_fwd */
+  const mla_rows* q_rope;
+  const mla_rows* kv;
+  const mla_rows* k_rope;
+  int32_t B, Hq;
+  int64_t Nq, Nkv;
+  int32_t dq, dr, dv;
+  float scale;
+  uint32_t flags;
+  int64_t q_offset, kv_offset;
+  const mla_rows* prev_out;
+  const mla_rows* prev_lse;
+  const mla_rows* out;
+  const mla_rows* lse;
+} mla_fwd_call;
+
+mla_status mla_fwd_group(int32_t n, const mla_fwd_call* calls, void* stream /* hipStream_t */);
+
+/*
  * mla_merge_lse -- fold two partial results over disjoint key sets
  * (TensorRT-LLM mla.py, forward_context_with_chunked_prefill: partial outputs
  * merged with their softmax stats; Ascend RingMLAOperation prevOut/prevLse).

@@ -34,6 +34,20 @@ class MlaRows(ctypes.Structure):
 _P = ctypes.POINTER(MlaRows)
 
 
+class MlaFwdCall(ctypes.Structure):
+    """mla_fwd_call: the arguments of one shared-latent mla_fwd call."""
+    _fields_ = [("q", _P), ("q_rope", _P), ("kv", _P), ("k_rope", _P),
+                ("B", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Nq", ctypes.c_int64), ("Nkv", ctypes.c_int64),
+                ("dq", ctypes.c_int32), ("dr", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("q_offset", ctypes.c_int64), ("kv_offset", ctypes.c_int64),
+                ("prev_out", _P), ("prev_lse", _P), ("out", _P), ("lse", _P)]
+
+
+MAX_GROUP = 4   # MLA_MAX_GROUP
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
@@ -47,6 +61,8 @@ def _load():
         ctypes.c_void_p, ctypes.c_int32,
         ctypes.c_float, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64,
         _P, _P, _P, _P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_fwd_group.restype = ctypes.c_int
+    lib.mla_fwd_group.argtypes = [ctypes.c_int32, ctypes.POINTER(MlaFwdCall), ctypes.c_void_p]
     lib.mla_merge_lse.restype = ctypes.c_int
     lib.mla_merge_lse.argtypes = [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_int32, _P, _P, ctypes.c_void_p]
@@ -79,7 +95,7 @@ def _load():
 LIB = _load()
 LIB_PATH = _LIB_PATH
 
-EXPORTS = ("mla_fwd", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd", "mla_debug_gather",
+EXPORTS = ("mla_fwd", "mla_fwd_group", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd", "mla_debug_gather",
            "mla_last_error", "mla_version", "mla_workspace_size", "mla_decode_workspace_size")
 
 
@@ -176,6 +192,36 @@ def _workspace(device: torch.device, workspace) -> Tuple[Optional[int], int]:
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
+def _fwd_args(q, kv, scale, head_dim_v, causal, q_offset, kv_offset, q_rope, k_rope, v, prev, out,
+              lse, want_lse):
+    """Views and sizes of one mla_fwd call (outputs allocated if not given)."""
+    B, Hq, Nq, dq = q.shape
+    _, Hkv, Nkv, _ = kv.shape
+    dr = 0 if q_rope is None else q_rope.shape[-1]
+    dv = head_dim_v if v is None else v.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, Nq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and (want_lse or prev is not None):
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out_f32 = out.dtype == torch.float32
+    prev_f32 = prev is not None and prev[0].dtype == torch.float32
+    a = dict(
+        q=_rows_bhtd(q, "q"), kv=_rows_bhtd(kv, "kv"),
+        out=_rows_bhtd(out, "out", torch.float32 if out_f32 else torch.bfloat16),
+        q_rope=_rows_bhtd(q_rope, "q_rope") if q_rope is not None else None,
+        k_rope=_rows_bhtd(k_rope, "k_rope") if k_rope is not None else None,
+        v=_rows_bhtd(v, "v") if v is not None else None,
+        prev_out=(_rows_bhtd(prev[0], "prev_out", torch.float32 if prev_f32 else torch.bfloat16)
+                  if prev is not None else None),
+        prev_lse=_lse_bht(prev[1], "prev_lse") if prev is not None else None,
+        lse=_lse_bht(lse, "lse") if lse is not None else None,
+        B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nkv=Nkv, dq=dq, dr=dr, dv=dv, scale=float(scale),
+        flags=((MLA_CAUSAL if causal else 0) | (MLA_OUT_F32 if out_f32 else 0)
+               | (MLA_PREV_OUT_F32 if prev_f32 else 0)),
+        q_offset=q_offset, kv_offset=kv_offset)
+    return a, out, lse
+
+
 def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 512,
         causal: bool = True, q_offset: int = 0, kv_offset: int = 0,
         q_rope: Optional[torch.Tensor] = None, k_rope: Optional[torch.Tensor] = None,
@@ -196,34 +242,48 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 51
     launch index) or a uint8 GPU tensor of at least mla_workspace_size()
     bytes.
     """
-    B, Hq, Nq, dq = q.shape
-    _, Hkv, Nkv, _ = kv.shape
-    dr = 0 if q_rope is None else q_rope.shape[-1]
-    dv = head_dim_v if v is None else v.shape[-1]
-    if out is None:
-        out = torch.empty((B, Hq, Nq, dv), dtype=torch.bfloat16, device=q.device)
-    if lse is None and (want_lse or prev is not None):
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    out_f32 = out.dtype == torch.float32
-    prev_f32 = prev is not None and prev[0].dtype == torch.float32
-    vq, vkv = _rows_bhtd(q, "q"), _rows_bhtd(kv, "kv")
-    vout = _rows_bhtd(out, "out", torch.float32 if out_f32 else torch.bfloat16)
-    vqr = _rows_bhtd(q_rope, "q_rope") if q_rope is not None else None
-    vkr = _rows_bhtd(k_rope, "k_rope") if k_rope is not None else None
-    vv = _rows_bhtd(v, "v") if v is not None else None
-    vpo = (_rows_bhtd(prev[0], "prev_out", torch.float32 if prev_f32 else torch.bfloat16)
-           if prev is not None else None)
-    vpl = _lse_bht(prev[1], "prev_lse") if prev is not None else None
-    vl = _lse_bht(lse, "lse") if lse is not None else None
-    flags = ((MLA_CAUSAL if causal else 0) | (MLA_OUT_F32 if out_f32 else 0)
-             | (MLA_PREV_OUT_F32 if prev_f32 else 0))
+    a, out, lse = _fwd_args(q, kv, scale, head_dim_v, causal, q_offset, kv_offset, q_rope, k_rope, v,
+                            prev, out, lse, want_lse)
     ws, ws_bytes = _workspace(q.device, workspace)
-    _check(LIB.mla_fwd(ctypes.byref(vq), _ref(vqr), ctypes.byref(vkv), _ref(vkr), _ref(vv),
-                       B, Hq, Hkv, Nq, Nkv, dq, dr, dv, None, 0, float(scale), flags,
-                       q_offset, kv_offset,
-                       _ref(vpo), _ref(vpl), ctypes.byref(vout), _ref(vl), ws, ws_bytes,
-                       _stream(q.device)))
+    _check(LIB.mla_fwd(ctypes.byref(a["q"]), _ref(a["q_rope"]), ctypes.byref(a["kv"]), _ref(a["k_rope"]),
+                       _ref(a["v"]), a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["dq"], a["dr"], a["dv"],
+                       None, 0, a["scale"], a["flags"], a["q_offset"], a["kv_offset"],
+                       _ref(a["prev_out"]), _ref(a["prev_lse"]), ctypes.byref(a["out"]), _ref(a["lse"]),
+                       ws, ws_bytes, _stream(q.device)))
     return out, lse
+
+
+def fwd_group(calls) -> list:
+    """Up to MAX_GROUP shared-latent fwd calls in one launch (mla_fwd_group).
+    ``calls``: a list of dicts of fwd's keyword arguments plus ``q`` and
+    ``kv`` (no ``v``, no workspace).  Returns the (out, lse) pair of each."""
+    if len(calls) > MAX_GROUP:
+        raise ValueError(f"at most {MAX_GROUP} calls per group")
+    keep, results = [], []
+    arr = (MlaFwdCall * max(1, len(calls)))()
+    device = None
+    for i, c in enumerate(calls):
+        c = dict(c)
+        q, kv = c.pop("q"), c.pop("kv")
+        device = q.device
+        a, out, lse = _fwd_args(q, kv, c.pop("scale"), c.pop("head_dim_v", 512), c.pop("causal", True),
+                                c.pop("q_offset", 0), c.pop("kv_offset", 0), c.pop("q_rope", None),
+                                c.pop("k_rope", None), None, c.pop("prev", None), c.pop("out", None),
+                                c.pop("lse", None), c.pop("want_lse", True))
+        if c:
+            raise TypeError(f"fwd_group: unexpected arguments {sorted(c)}")
+        if a["Hkv"] != 1:
+            raise ValueError("fwd_group: shared-latent calls only (one KV head)")
+        keep.append(a)
+        ref = lambda r: ctypes.pointer(r) if r is not None else None
+        arr[i] = MlaFwdCall(ref(a["q"]), ref(a["q_rope"]), ref(a["kv"]), ref(a["k_rope"]), a["B"], a["Hq"],
+                            a["Nq"], a["Nkv"], a["dq"], a["dr"], a["dv"], a["scale"], a["flags"],
+                            a["q_offset"], a["kv_offset"], ref(a["prev_out"]), ref(a["prev_lse"]),
+                            ref(a["out"]), ref(a["lse"]))
+        results.append((out, lse))
+    if calls:
+        _check(LIB.mla_fwd_group(len(calls), arr, _stream(device)))
+    return results
 
 
 def split_fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
@@ -415,18 +475,6 @@ def ring_order(r: int, n_chunks: int) -> Sequence[int]:
     return [(r - s) % n_chunks for s in range(n_chunks) if (r - s) % n_chunks <= r]
 
 
-_RING_STREAMS: dict = {}
-
-
-def _ring_streams(device: torch.device, n: int):
-    """A per-device pool of side streams (default priority) for the ring."""
-    key = (device.index if device.index is not None else torch.cuda.current_device())
-    pool = _RING_STREAMS.setdefault(key, [])
-    while len(pool) < n:
-        pool.append(torch.cuda.Stream(device=device))
-    return pool[:n]
-
-
 def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
              head_dim_v: int = 512, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None,
@@ -443,10 +491,9 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
     kept in float32 (``carry``, [n_chunks, B, H, C, dv], allocated if not
     given) and only the last step of each query chunk writes bf16 ``out``.
 
-    The query chunks are independent of one another, so each runs its steps
-    in order on a side stream of its own, and the chunks overlap on the GPU
-    (one call covers only B*H/4 * C/32 workgroups); the caller's stream waits
-    for all of them before this returns."""
+    The query chunks are independent of one another: each ring step runs as
+    one launch for all of them (mla_fwd_group, up to four chunks a launch),
+    on the caller's stream."""
     B, H, N, dk = q.shape
     if N % n_chunks:
         raise ValueError("sequence length must be a multiple of the chunk count")
@@ -457,24 +504,19 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if carry is None and n_chunks > 1:
         carry = torch.empty((n_chunks, B, H, C, head_dim_v), dtype=torch.float32, device=q.device)
-    main = torch.cuda.current_stream(q.device)
-    streams = _ring_streams(q.device, n_chunks)
-    for st in streams:
-        st.wait_stream(main)
     orders = [ring_order(r, n_chunks) for r in range(n_chunks)]
-    for step in range(n_chunks):  # step-major, so that every chunk starts at once
+    for step in range(n_chunks):
+        calls = []
         for r in range(n_chunks):
             if step >= len(orders[r]):
                 continue
             k = orders[r][step]
             qs = slice(r * C, (r + 1) * C)
-            o_r, l_r = out[:, :, qs], lse[:, :, qs]
             last = step == len(orders[r]) - 1
-            with torch.cuda.stream(streams[r]):
-                fwd(q[:, :, qs], kv[:, :, k * C:(k + 1) * C], scale=scale, head_dim_v=head_dim_v,
-                    causal=True, q_offset=r * C, kv_offset=k * C,
-                    prev=None if step == 0 else (carry[r], l_r),
-                    out=o_r if last else carry[r], lse=l_r)
-    for st in streams:
-        main.wait_stream(st)
+            calls.append(dict(q=q[:, :, qs], kv=kv[:, :, k * C:(k + 1) * C], scale=scale,
+                              head_dim_v=head_dim_v, causal=True, q_offset=r * C, kv_offset=k * C,
+                              prev=None if step == 0 else (carry[r], lse[:, :, qs]),
+                              out=out[:, :, qs] if last else carry[r], lse=lse[:, :, qs]))
+        for i in range(0, len(calls), MAX_GROUP):
+            fwd_group(calls[i:i + MAX_GROUP])
     return out, lse

@@ -142,22 +142,19 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-const char* mla_last_error(void) { return g_last_error.c_str(); }
+enum { FORM_EMPTY = 0, FORM_LATENT = 1, FORM_SPLIT = 2 };
 
-const char* mla_version(void) { return "mla355 0.1 gfx950"; }
-
-size_t mla_workspace_size(void) { return mla::kWorkspaceBytes; }
-
-mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
-                   const mla_rows* k_rope, const mla_rows* v, int32_t B, int32_t Hq,
-                   int32_t Hkv, int64_t Nq, int64_t Nkv, int32_t dq, int32_t dr, int32_t dv,
-                   const int32_t* seq_lens, int32_t n_seqs, float scale, uint32_t flags,
-                   int64_t q_offset, int64_t kv_offset, const mla_rows* prev_out,
-                   const mla_rows* prev_lse, const mla_rows* out, const mla_rows* lse,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+// Validates one mla_fwd call and fills its kernel parameters; *form says
+// which kernel serves it (FORM_EMPTY: nothing to launch).
+mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
+                       const mla_rows* k_rope, const mla_rows* v, int32_t B, int32_t Hq,
+                       int32_t Hkv, int64_t Nq, int64_t Nkv, int32_t dq, int32_t dr, int32_t dv,
+                       const int32_t* seq_lens, int32_t n_seqs, float scale, uint32_t flags,
+                       int64_t q_offset, int64_t kv_offset, const mla_rows* prev_out,
+                       const mla_rows* prev_lse, const mla_rows* out, const mla_rows* lse,
+                       void* workspace, size_t workspace_bytes, mla::AttnParams* pp, int* form) {
   mla_status st;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nkv < 0)
     return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, Hq > 0, Hkv > 0, Nq >= 0, Nkv >= 0");
@@ -200,7 +197,8 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv
     if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_INVALID_ARG, "seq_lens must be 4-byte aligned");
   }
 
-  mla::AttnParams p{};
+  mla::AttnParams& p = *pp;
+  p = mla::AttnParams{};
   p.qa = rc(q);
   p.qb = q_rope ? rc(q_rope) : rc(q);
   p.ka = rc(kv);
@@ -225,7 +223,6 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv
   p.out_f32 = out_f32 ? 1 : 0;
   p.prev_f32 = prev_f32 ? 1 : 0;
   p.queue = static_cast<unsigned*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
 
   const bool latent = !v && Hkv == 1 && dq + dr == 576 && dv == 512 && (dr == 0 || dr == 64) && !seq_lens;
   const bool split = v && q_rope && dq == 128 && dr == 64 && dv == 128;
@@ -240,19 +237,80 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv
     if (n_qblk * n_hgrp * B > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
     p.n_qblk = (int32_t)n_qblk;
     p.n_hgrp = (int32_t)n_hgrp;
-    if (Nq == 0 || B == 0) return MLA_OK;
-    return hip_status(mla::launch_latent_dense(p, s), "latent attention launch");
+    *form = Nq == 0 || B == 0 ? FORM_EMPTY : FORM_LATENT;
+    return MLA_OK;
   }
   if (split) {
     const int64_t qb = seq_lens ? (Nq + 127) / 128 + n_seqs : (Nq + 127) / 128 * B;
     if (qb * Hq > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
-    if (Nq == 0 || B == 0) return MLA_OK;
-    return hip_status(mla::launch_split(p, s), "split attention launch");
+    *form = Nq == 0 || B == 0 ? FORM_EMPTY : FORM_SPLIT;
+    return MLA_OK;
   }
   return fail(MLA_ERR_UNSUPPORTED,
               "no kernel for Hq=%d Hkv=%d dq=%d dr=%d dv=%d v=%s seq_lens=%s (built: shared latent "
               "Hkv=1 dq+dr=576 dv=512 v=NULL; split dq=128 dr=64 dv=128 with v)",
               Hq, Hkv, dq, dr, dv, v ? "given" : "NULL", seq_lens ? "given" : "NULL");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+const char* mla_version(void) { return "mla355 0.1 gfx950"; }
+
+size_t mla_workspace_size(void) { return mla::kWorkspaceBytes; }
+
+mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
+                   const mla_rows* k_rope, const mla_rows* v, int32_t B, int32_t Hq,
+                   int32_t Hkv, int64_t Nq, int64_t Nkv, int32_t dq, int32_t dr, int32_t dv,
+                   const int32_t* seq_lens, int32_t n_seqs, float scale, uint32_t flags,
+                   int64_t q_offset, int64_t kv_offset, const mla_rows* prev_out,
+                   const mla_rows* prev_lse, const mla_rows* out, const mla_rows* lse,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mla::AttnParams p;
+  int form = FORM_EMPTY;
+  if (mla_status st = prepare_fwd(q, q_rope, kv, k_rope, v, B, Hq, Hkv, Nq, Nkv, dq, dr, dv, seq_lens, n_seqs,
+                                  scale, flags, q_offset, kv_offset, prev_out, prev_lse, out, lse, workspace,
+                                  workspace_bytes, &p, &form))
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (form == FORM_LATENT) return hip_status(mla::launch_latent_dense(p, s), "latent attention launch");
+  if (form == FORM_SPLIT) return hip_status(mla::launch_split(p, s), "split attention launch");
+  return MLA_OK;
+}
+
+mla_status mla_fwd_group(int32_t n, const mla_fwd_call* calls, void* stream) {
+  g_last_error.clear();
+  if (n < 0 || n > MLA_MAX_GROUP) return fail(MLA_ERR_INVALID_ARG, "n (%d) must lie in [0, %d]", n, MLA_MAX_GROUP);
+  if (n > 0 && !calls) return fail(MLA_ERR_INVALID_ARG, "calls: missing");
+  mla::GroupParams g{};
+  int64_t items = 0;
+  g.first[0] = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const mla_fwd_call& c = calls[i];
+    mla::AttnParams p;
+    int form = FORM_EMPTY;
+    if (mla_status st = prepare_fwd(c.q, c.q_rope, c.kv, c.k_rope, nullptr, c.B, c.Hq, 1, c.Nq, c.Nkv, c.dq, c.dr,
+                                    c.dv, nullptr, 0, c.scale, c.flags, c.q_offset, c.kv_offset, c.prev_out,
+                                    c.prev_lse, c.out, c.lse, nullptr, 0, &p, &form)) {
+      char buf[600];
+      snprintf(buf, sizeof(buf), "call %d: %s", i, g_last_error.c_str());
+      g_last_error = buf;
+      return st;
+    }
+    if (form == FORM_EMPTY) continue;
+    if (form != FORM_LATENT)
+      return fail(MLA_ERR_UNSUPPORTED, "call %d: a group holds shared-latent calls only", i);
+    items += (int64_t)p.n_qblk * p.n_hgrp * p.B;
+    if (items > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "group too large for one launch");
+    g.sub[g.n] = p;
+    g.first[++g.n] = (int32_t)items;
+  }
+  if (g.n == 0) return MLA_OK;
+  return hip_status(mla::launch_latent_group(g, static_cast<hipStream_t>(stream)), "group attention launch");
 }
 
 mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a, const mla_rows* out_b,

@@ -290,752 +290,21 @@ constexpr int kWavesPerEU = MODE == 1 ? 2 : 1;
 template <class C, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, kWavesPerEU<MODE>)))
 void attn_fwd_kernel(const AttnParams p) {
-  constexpr bool SP = MODE == SPARSE || MODE == SPARSE_PIPE;
-  constexpr int DA = C::DA, DV = C::DV;
-  constexpr int DK = DA + DB;
-  constexpr int KS = DK / 16;            // MFMA k-steps of Q.K
-  constexpr int KSA = DA / 16;           // k-steps served by the first sub-tile
-  constexpr int NGA = DA / 64;           // column groups of the first sub-tile
-  constexpr int NGV = C::VLAT ? NGA : DV / 64;
-  constexpr int NDVB = DV / 32 / WAVES;  // 32-column value blocks per wave
-  constexpr int KI = NGA + 1 + (C::VLAT ? 0 : NGV);  // copy instructions per wave per tile
-  // the latent form (and the sparse one for lists up to 2048) runs the
-  // softmax of tile t+1 inside the Q.K chain of tile t+2 (see the main
-  // loop) with four key-tile buffers; the others compute it beside P.V with
-  // three (the sparse form keeps its index list in LDS instead of a fourth)
-  constexpr bool SM_IN_QK = MODE == LATENT || MODE == SPARSE_PIPE;
-  constexpr int NB = SM_IN_QK ? 4 : 3;
-  // 64-column sub-tile buffers: only the Q.K chain reads them, so two are
-  // enough in the tile-step loop (the one being read and the one in flight);
-  // the pipelined sparse form needs that room for its index list
-  constexpr int NBB = MODE == SPARSE_PIPE ? 2 : NB;
-  constexpr int KIDX = MODE == SPARSE ? KMAX_IDX : MODE == SPARSE_PIPE ? KMAX_IDX_PIPE : 0;
-  using SM = Smem<C, NB, NBB, KIDX>;
-  static_assert(KS - KSA == 4, "second part is 64 columns");
-  static_assert(NB - 2 <= 2, "wait_tiles covers at most two tiles in flight");
+  constexpr int64_t first_wg = 0;
+#include "mla_attn_body.inc"
+}
 
-  __shared__ SM sm;
-
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int lane = tid & 63, h = lane >> 5, lr = lane & 31;  // (recomputed past the key loop)
-  __builtin_assume(w >= 0 && w < WAVES);
-
-  // ---------------------------------------------------------------- rows
-  // Work item: latent, a block of 32 query rows of WAVES heads, longest
-  // causal rows first; sparse, one query with all its heads.  With a queue
-  // the workgroup takes the next item from a device counter instead of its
-  // own index.  The hardware hands the workgroups of a launch to the XCDs in
-  // equal shares, whatever their clocks; through the counter a faster XCD
-  // also takes items sooner, and so the longer ones, and all finish
-  // together.
-  int64_t item = blockIdx.x;
-  if constexpr (MODE == LATENT || MODE == SPARSE_PIPE) {
-    if (p.queue) {
-      if (tid == 0) sm.epi.item = (int)atomicAdd(p.queue, 1u);
-      __syncthreads();
-      item = sm.epi.item;  // (P, which shares this space, is first written past a barrier)
-    }
-  }
-  Ctx cx;
-  cx.t0 = 0;
-  if constexpr (MODE == LATENT) {
-    const int per = p.n_hgrp * p.B;
-    const int id = (int)item;
-    const int qblk = p.n_qblk - 1 - id / per;  // longest causal rows first
-    const int rem = id % per;
-    cx.hbase = (rem % p.n_hgrp) * WAVES;
-    cx.b = rem / p.n_hgrp;
-    cx.q0 = (int64_t)qblk * 32;
-    cx.q_len = p.Nq;
-    cx.kv_len = p.Nkv;
-    const int64_t last_q = min(p.Nq - 1, cx.q0 + 31);
-    cx.kv_end = p.causal ? max<int64_t>(0, min<int64_t>(p.Nkv, p.q_offset + last_q - p.kv_offset + 1)) : p.Nkv;
-  } else if constexpr (MODE == SPLIT) {
-    const int id = blockIdx.x;
-    cx.hbase = id % p.Hq;
-    const int qb_lin = id / p.Hq;
-    if (p.seq_lens) {
-      int64_t cum = 0, t0 = 0, qb = 0, len = 0;
-      bool found = false;
-      for (int s = 0; s < p.n_seqs; ++s) {
-        int64_t L = p.seq_lens[s];
-        L = max<int64_t>(0, min<int64_t>(L, p.Nq - t0));
-        const int64_t nb = (L + ROWS - 1) / ROWS;
-        if (qb_lin < cum + nb) { found = true; qb = qb_lin - cum; len = L; break; }
-        cum += nb;
-        t0 += L;
-      }
-      if (!found) return;  // whole workgroup, before any barrier
-      cx.b = 0;
-      cx.t0 = t0;
-      cx.q_len = len;
-      cx.kv_len = len;
-      cx.q0 = qb * ROWS;
-    } else {
-      const int64_t nb = (p.Nq + ROWS - 1) / ROWS;
-      cx.b = (int)(qb_lin / nb);
-      cx.q0 = (nb - 1 - qb_lin % nb) * ROWS;  // longest causal rows first
-      cx.q_len = p.Nq;
-      cx.kv_len = p.Nkv;
-    }
-    const int64_t last_q = min(cx.q_len - 1, cx.q0 + ROWS - 1);
-    cx.kv_end = p.causal ? max<int64_t>(0, min<int64_t>(cx.kv_len, p.q_offset + last_q - p.kv_offset + 1)) : cx.kv_len;
-  } else {  // SPARSE
-    const int64_t id = item;
-    cx.b = (int)(id / p.Nq);
-    cx.q0 = id % p.Nq;
-    cx.hbase = 0;
-    cx.q_len = p.Nq;
-    cx.kv_len = p.topk;
-    cx.kv_end = p.topk;
-    if (p.decode) {  // the part of split q0's range inside the valid rows
-      int64_t len = p.kv_lens ? (int64_t)p.kv_lens[cx.b] : p.Nkv;
-      len = max<int64_t>(0, min<int64_t>(len, p.Nkv));
-      cx.kv_len = cx.kv_end = max<int64_t>(0, min<int64_t>(p.topk, len - cx.q0 * p.topk));
-    }
-  }
-
-  auto row_head = [&](int rb) -> int {
-    if constexpr (MODE == LATENT) return cx.hbase + rb;
-    else if constexpr (MODE == SPLIT) return cx.hbase;
-    else return rb * 32 + lr;
-  };
-  auto row_query = [&](int rb) -> int64_t {
-    if constexpr (MODE == LATENT) return cx.q0 + lr;
-    else if constexpr (MODE == SPLIT) return cx.q0 + rb * 32 + lr;
-    else return cx.q0;
-  };
-  auto row_valid = [&](int rb) -> bool { return row_head(rb) < p.Hq && row_query(rb) < cx.q_len; };
-  auto qtok = [&](int64_t q) -> int64_t { return cx.t0 + q; };
-
-  // ------------------------------------------------------------ Q -> VGPR
-  bf16x8 qf[KS];
-  {
-    const int hq = row_head(w) < p.Hq ? row_head(w) : 0;
-    const int64_t t = qtok(row_query(w) < cx.q_len ? row_query(w) : 0);
-    const uint16_t* ra = p.qa.p + cx.b * p.qa.sb + hq * p.qa.sh + t * p.qa.st;
-    const uint16_t* rb = p.qb.p + cx.b * p.qb.sb + hq * p.qb.sh + t * p.qb.st;
-#pragma unroll
-    for (int c = 0; c < KS; ++c) {
-      const int d = 16 * c + 8 * h;
-      qf[c] = c < KSA ? load16(ra + d) : load16(rb + (d - DA));
-    }
-  }
-
-  // ---------------------------------------------------------- key sources
-  const int kvh = SP ? 0 : row_head(0) / p.group;
-  const uint16_t* kA = p.ka.p + cx.b * p.ka.sb + (int64_t)kvh * p.ka.sh + cx.t0 * p.ka.st;
-  const uint16_t* kB = p.kb.p + cx.b * p.kb.sb + (int64_t)kvh * p.kb.sh + cx.t0 * p.kb.st;
-  const uint16_t* vS = C::VLAT ? kA : p.v.p + cx.b * p.v.sb + (int64_t)kvh * p.v.sh + cx.t0 * p.v.st;
-  const uint32_t stA = (uint32_t)(p.ka.st * 2), stB = (uint32_t)(p.kb.st * 2), stV = (uint32_t)(p.v.st * 2);
-
-  if constexpr (SP) {  // stage the query's index list in LDS
-    if (p.decode) {    // token generation: the rows of split q0, -1 past the valid ones
-      const int s0 = (int)(cx.q0 * p.topk), n = (int)cx.kv_end;
-      for (int k = tid; k < p.topk; k += 256) sm.idx[k] = k < n ? s0 + k : -1;
-    } else {
-      const int32_t* idx_row = p.idx + ((int64_t)cx.b * p.Nq + cx.q0) * p.topk;
-      for (int k = tid; k < p.topk; k += 256) sm.idx[k] = idx_row[k];
-    }
-    __syncthreads();
-  }
-  auto idx_ok = [&](int r) -> bool { return r >= 0 && r < p.Nkv; };
-
-  // loader: wave w copies rows 8w..8w+7 of every sub-tile; lane l handles
-  // row 8w + l/8, chunk position l%8
-  const int lrow = 8 * w + (lane >> 3);
-  const uint32_t lchunk = (uint32_t)(((lane & 7) ^ swz_f(lrow & 15)) << 4);
-  const uint32_t voA = (uint32_t)lrow * stA + lchunk;
-  const uint32_t voB = (uint32_t)lrow * stB + lchunk;
-  const uint32_t voV = (uint32_t)lrow * stV + lchunk;
-
-  // LDS byte addresses of the tile buffers (buffer i at + i * tile size)
-  const uint32_t lds_a = lds_addr(&sm.a[0][0]), lds_b = lds_addr(&sm.b[0][0]);
-  const uint32_t lds_v = C::VLAT ? lds_a : lds_addr(&sm.v[0][0]);
-
-  // Copies of one key tile: KI wave instructions, one per 64-column group of
-  // each sub-tile (A groups, then the B sub-tile, then the V groups).  The
-  // sources are worked out once per tile (tile_src); issue_copy<I> issues
-  // instruction I, so that the copies can be spread over the MFMA stream.
-  struct TileSrc {
-    u32x4 ra, rb, rv;
-    uint32_t oa, ob, la, lb, lv;
-  };
-  auto tile_src = [&](int t, int buf) __attribute__((always_inline)) -> TileSrc {
-    TileSrc c;
-    const int64_t k0 = (int64_t)t * BN;
-    // buf: the slot of the tile in the ring of buffers (the A buffer; the B
-    // buffer is the same slot modulo NBB)
-    c.la = lds_a + buf * SM::ATILE;
-    c.lb = lds_b + (buf % NBB) * SM::BTILE;
-    c.lv = lds_v + buf * SM::VTILE;
-    if constexpr (SP) {
-      const int r = (int)k0 + lrow;
-      const int ix = r < p.topk ? sm.idx[r] : -1;
-      const bool ok = idx_ok(ix);
-      c.ra = make_rsrc(kA, (uint32_t)(p.Nkv * stA));
-      c.rb = make_rsrc(kB, (uint32_t)(p.Nkv * stB));
-      c.oa = ok ? (uint32_t)ix * stA + lchunk : kOob;
-      c.ob = ok ? (uint32_t)ix * stB + lchunk : kOob;
-    } else {
-      // the buffer is the tile's rows [k0, min(k0 + BN, kv_len)); rows past it read zeros
-      const uint32_t nrows = (uint32_t)min<int64_t>(BN, cx.kv_len - k0);
-      c.ra = make_rsrc(kA + k0 * p.ka.st, nrows * stA);
-      c.rb = make_rsrc(kB + k0 * p.kb.st, nrows * stB);
-      if constexpr (!C::VLAT) c.rv = make_rsrc(vS + k0 * p.v.st, nrows * stV);
-      c.oa = voA;
-      c.ob = voB;
-    }
-    return c;
-  };
-  auto issue_copy = [&](const TileSrc& c, auto I) __attribute__((always_inline)) {
-    constexpr int i = decltype(I)::value;
-    if constexpr (i < NGA) copy_rows<NGA, i, i + 1>(c.ra, c.la, w, c.oa);
-    else if constexpr (i == NGA) copy_rows<1>(c.rb, c.lb, w, c.ob);
-    else copy_rows<NGV, i - NGA - 1, i - NGA>(c.rv, c.lv, w, voV);
-  };
-  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
-    const TileSrc c = tile_src(t, buf);
-    unroll<KI>([&](auto I) __attribute__((always_inline)) { issue_copy(c, I); });
-  };
-
-  // LDS byte offsets of this lane's K fragments (k-step c: + (c/4) KB)
-  // (k-step c: chunk 2(c%4) + h of column group c/4; the chunk index is
-  // XORed with the row swizzle, so k-step c%4 = k flips bits 5-6 by k)
-  const int koffA = tile_off(NGA, lr, h), koffB = tile_off(1, lr, h);
-
-  const int n_tiles = (int)((cx.kv_end + BN - 1) / BN);
-  // key rows visible to this lane's row: [0, vis_end), relative to the
-  // workgroup's key range (a key's position is kv_offset + its index)
-  int32_t vis_end, wave_vis_end;
-  {
-    const int64_t row_pos = p.q_offset + row_query(w);
-    const int64_t wave_pos = row_pos - lr;                // first row of the wave
-    int64_t ve = cx.kv_len, we = cx.kv_len;
-    if (p.causal && !SP) {
-      ve = min<int64_t>(ve, max<int64_t>(0, row_pos - p.kv_offset + 1));
-      we = min<int64_t>(we, max<int64_t>(0, wave_pos - p.kv_offset + 1));
-    }
-    vis_end = (int32_t)ve;        // <= kv_len, which fits 32 bits
-    wave_vis_end = __builtin_amdgcn_readfirstlane((int32_t)we);  // visible to every row of the wave
-  }
-
-  f32x16 O[WAVES][NDVB];
-  float m_ref = -INFINITY;  // reference max of this lane's row (log2 units)
-  float m_run = -INFINITY;  // running exact max
-  float l_part = 0.f;       // this lane's share of the row sum, relative to m_ref
-  float l_rnd = 0.f;        // the same over the bf16-rounded weights
-  bool over = false;
-
-  // S^T = K Q^T for one tile (lane: query row lr; keys (r/4)*8 + 4h + r%4)
-  // LDS byte addresses of this lane's K fragments in tile buffer `buf`
-  auto frag_addrs = [&](int buf, uint32_t* a, uint32_t* b) __attribute__((always_inline)) {
-    const uint32_t ta = lds_a + buf * SM::ATILE, tb = lds_b + (buf % NBB) * SM::BTILE;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      a[k] = (ta + koffA) ^ (uint32_t)(k << 5);
-      b[k] = (tb + koffB) ^ (uint32_t)(k << 5);
-    }
-  };
-  auto qk = [&](int buf) __attribute__((always_inline)) -> f32x16 {
-    f32x16 s;
-    if constexpr (KS == 36) {
-      uint32_t a[4], b[4];
-      frag_addrs(buf, a, b);
-      qk_chain(s, qf, a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
-    } else {
-      s = f32x16{};
-      const unsigned char* ta = sm.a[buf];
-      const unsigned char* tb = sm.b[buf];
-#pragma unroll
-      for (int c = 0; c < KS; ++c) {
-        const bf16x8 kf = c < KSA ? *reinterpret_cast<const bf16x8*>(ta + (koffA ^ ((c & 3) << 5)) + (c >> 2) * 1024)
-                                  : *reinterpret_cast<const bf16x8*>(tb + (koffB ^ ((c - KSA) << 5)));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s, 0, 0, 0);
-      }
-    }
-    return s;
-  };
-
-  // softmax, first half: scale to log2 units, mask, row max, reference max.
-  // `live` false: no tile (all scores masked).
-  auto scores = [&](const f32x16& s, int t, bool live, float* x) __attribute__((always_inline)) {
-    const int k0 = t * BN;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = s[r] * p.scale_log2;
-    bool need_mask;
-    unsigned vbits = 0xffffffffu;
-    if constexpr (SP) {
-      const int k = k0 + lr;
-      vbits = (unsigned)__ballot(live && k < p.topk && idx_ok(sm.idx[k < p.topk ? k : 0]));
-      need_mask = vbits != 0xffffffffu;
-    } else {
-      need_mask = !live || k0 + BN > wave_vis_end;
-    }
-    if (need_mask) {
-      // key kk of the tile (kk = (r/4)*8 + 4h + r%4) is visible iff
-      // k0 + kk < vis_end, i.e. (r/4)*8 + r%4 < vis_end - k0 - 4h
-      const int bound = live ? vis_end - k0 - 4 * h : -1000;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        bool ok;
-        if constexpr (SP) {
-          ok = (vbits >> ((r >> 2) * 8 + 4 * h + (r & 3))) & 1u;
-        } else {
-          ok = (r >> 2) * 8 + (r & 3) < bound;
-        }
-        x[r] = ok ? x[r] : -INFINITY;
-      }
-    }
-    float mt = x[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-    mt = xhalf_max(mt);
-    m_run = fmaxf(m_run, mt);
-    if (m_ref == -INFINITY) m_ref = mt;  // the row's first visible tile (pass 0)
-    over |= m_run > m_ref + TAU;
-  };
-
-  // softmax, second half, one quarter (4 of the lane's 16 scores) at a time,
-  // so that it can be spread over the P.V MFMAs: weights against the
-  // reference mu, row sums, and bf16 P^T fragments to LDS (a 16-key half
-  // once its two quarters are done).  The exact row sum gives the LSE; the
-  // sum of the weights as the P.V product sees them (rounded to bf16)
-  // normalises O, so its weights sum to one.
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  auto weights_q = [&](const float* x, int pb, float mu, bf16x4* bq, auto Q) __attribute__((always_inline)) {
-    constexpr int q = decltype(Q)::value;
-    f32x4 pq;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pq[r] = __builtin_amdgcn_exp2f(x[4 * q + r] - mu);
-    bq[q] = __builtin_convertvector(pq, bf16x4);
-    l_part += (pq[0] + pq[1]) + (pq[2] + pq[3]);
-    l_rnd += ((float)bq[q][0] + (float)bq[q][1]) + ((float)bq[q][2] + (float)bq[q][3]);
-    if constexpr (q & 1) {
-      const bf16x8 b = {bq[q - 1][0], bq[q - 1][1], bq[q - 1][2], bq[q - 1][3], bq[q][0], bq[q][1], bq[q][2], bq[q][3]};
-      *reinterpret_cast<bf16x8*>(sm.p[pb][w][q >> 1] + lane * 16) = b;
-    }
-  };
-  auto mu_of = [&]() __attribute__((always_inline)) { return m_ref == -INFINITY ? 0.f : m_ref; };
-
-  // O^T += V^T P^T over this wave's value columns for all 128 rows
-  // hook(integral_constant<int, g>) runs after MFMA group g (one value-column
-  // block of one 16-key half), g = 0 .. 2*NDVB-1.  The fragments of group
-  // g+1 are read before the MFMAs of group g: the hook may hold copies into
-  // LDS, which the compiler does not move LDS reads across.
-  auto pv = [&](int buf, int pb, auto&& hook) __attribute__((always_inline)) {
-    const unsigned char* vt = C::VLAT ? sm.a[buf] : sm.v[buf];
-    bf16x8 pf[WAVES];
-#pragma unroll
-    for (int rb = 0; rb < WAVES; ++rb) pf[rb] = *reinterpret_cast<const bf16x8*>(sm.p[pb][rb][0] + lane * 16);
-    bf16x8 vf = read_vt<NGV>(vt, w * NDVB, 0, lane);
-    unroll<2 * NDVB>([&](auto G) __attribute__((always_inline)) {
-      constexpr int g = decltype(G)::value, c = g / NDVB, j = g % NDVB;
-      bf16x8 vn = vf;
-      if constexpr (g + 1 < 2 * NDVB) vn = read_vt<NGV>(vt, w * NDVB + (g + 1) % NDVB, (g + 1) / NDVB, lane);
-#pragma unroll
-      for (int rb = 0; rb < WAVES; ++rb)
-        O[rb][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], O[rb][j], 0, 0, 0);
-      // interleave the VALU work of the previous hook (softmax) with these
-      // MFMAs: the MFMA unit runs each for several VALU issue slots
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int rb = 0; rb < WAVES; ++rb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-      }
-      // and keep the row sums of that work here rather than sunk to the barrier
-      asm volatile("" ::"v"(l_part), "v"(l_rnd));
-      if constexpr (g == NDVB - 1) {
-#pragma unroll
-        for (int rb = 0; rb < WAVES; ++rb) pf[rb] = *reinterpret_cast<const bf16x8*>(sm.p[pb][rb][1] + lane * 16);
-      }
-      hook(G);
-      vf = vn;
-      (void)c;
-    });
-  };
-
-  // Scores S(tp) = x ready for the chain's softmax, which neither scales nor
-  // masks: a tile that needs a mask (a key past the causal bound or the
-  // end, or an index outside the cache) or a scale that is not positive is
-  // scaled and masked here, and the chain then runs with scale 1 (returned).
-  auto prep_scores = [&](f32x16& x, int tp) __attribute__((always_inline)) -> float {
-    const int k0 = tp * BN;
-    bool mask;
-    unsigned vbits = 0xffffffffu;
-    if constexpr (SP) {
-      const int k = k0 + lr;  // key lr of the tile (lanes 32-63 repeat 0-31)
-      const int ix = sm.idx[k < p.topk ? k : 0];
-      vbits = (unsigned)__ballot((k < p.topk) & (ix >= 0) & (ix < p.Nkv));
-      mask = vbits != 0xffffffffu;
-    } else {
-      mask = k0 + BN > wave_vis_end;
-    }
-    mask = mask || !(p.scale_log2 > 0.f);  // wave-uniform
-    float sc = p.scale_log2;
-    if (mask) {
-      const int bound = vis_end - k0 - 4 * h;
-      const unsigned vb = vbits >> (4 * h);  // bit (r/4)*8 + r%4: this lane's key r
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        bool ok;
-        if constexpr (SP) {
-          ok = (vb >> ((r >> 2) * 8 + (r & 3))) & 1u;
-        } else {
-          ok = (r >> 2) * 8 + (r & 3) < bound;
-        }
-        x[r] = ok ? x[r] * p.scale_log2 : -INFINITY;
-      }
-      sc = 1.f;
-    }
-    return sc;
-  };
-  // Softmax of S(tp) = x to P buffer tp&1 inside the Q.K chain of tile tq;
-  // x returns S(tq).
-  auto chain_sm = [&](f32x16& x, int tp, int tq) __attribute__((always_inline)) {
-    if constexpr (KS == 36) {
-      const float sc = prep_scores(x, tp);
-      uint32_t a[4], b[4];
-      frag_addrs(tq & (NB - 1), a, b);
-      qk_chain_softmax(x, qf, a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], sc, m_ref, m_run, l_part, l_rnd,
-                       lds_addr(sm.p[tp & 1][w][0]) + lane * 16);
-    }
-  };
-
-  // ------------------------------------------------------------ main loop
-  // Iteration t computes S(t+1) = K(t+1) Q^T, then P(t) V(t) with the
-  // softmax of S(t+1) in between, and ends on the one barrier of the
-  // iteration.  Tiles t, t+1 and t+2 are resident (t+2 landed by the end of
-  // the iteration); the copies of tile t+NB-1 go into the buffer tile t-1
-  // left, spread over the P.V MFMAs.  P is double buffered.
-  constexpr int NPV = 2 * NDVB;  // MFMA groups of one P.V
-  bool redo = false;
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 1) {
-      if (!redo) break;      // workgroup-uniform
-      m_ref = m_run;         // exact row max: every weight is <= 1
-      l_part = 0.f;
-      l_rnd = 0.f;
-    }
-#pragma unroll
-    for (int rb = 0; rb < WAVES; ++rb)
-#pragma unroll
-      for (int j = 0; j < NDVB; ++j) O[rb][j] = f32x16{};
-
-    if constexpr (SM_IN_QK) {
-      // Iteration t: P(t) V(t) with the copies of tile t+3 (into the buffer
-      // tile t-1 left) spread over its MFMAs; then the Q.K chain of tile t+2
-      // with the softmax of S(t+1) inside it, which writes P(t+1); then the
-      // one barrier.  Tiles t..t+2 are resident, t+3 lands by the barrier.
-      // Unrolled twice so that the two score accumulators trade roles
-      // instead of being copied; the last two tiles have no chain.
-      auto pv_copy = [&](int t) __attribute__((always_inline)) {
-        const bool copy = t + NB - 1 < n_tiles;
-        const TileSrc src = tile_src(min(t + NB - 1, n_tiles - 1), (t + NB - 1) & (NB - 1));
-        pv(t & (NB - 1), t & 1, [&](auto G) __attribute__((always_inline)) {
-          constexpr int g = decltype(G)::value;
-          if (copy) {
-            unroll<(g + 1) * KI / NPV - g * KI / NPV>([&](auto I) __attribute__((always_inline)) {
-              issue_copy(src, std::integral_constant<int, g * KI / NPV + decltype(I)::value>{});
-            });
-          }
-        });
-      };
-      // Past the last tile the chain still runs: the scores of tile n_tiles
-      // are all masked (-inf), which leaves the row stats as they are, and
-      // the tile it multiplies is stale and unused; copies past the last
-      // tile read zeros (an empty buffer range) into a free buffer.
-      if (n_tiles > 0) {
-        const int pre = min(n_tiles, NB - 1);
-        f32x16 sc;
-        if constexpr (NBB >= NB - 1) {
-          for (int u = 0; u < pre; ++u) issue_tile(u, u);
-          wait_tiles<KI>(0);
-          __syncthreads();
-          sc = qk(0);
-          chain_sm(sc, 0, 1);
-          __syncthreads();
-        } else {
-          // two 64-column buffers: tile 2's goes into tile 0's once every
-          // wave has read that in Q.K(0)
-          for (int u = 0; u < min(pre, 2); ++u) issue_tile(u, u);
-          const TileSrc c2 = tile_src(min(2, n_tiles - 1), 2);
-          if (pre > 2) unroll<NGA>([&](auto I) __attribute__((always_inline)) { issue_copy(c2, I); });
-          wait_tiles<KI>(0);
-          __syncthreads();
-          sc = qk(0);
-          __syncthreads();
-          if (pre > 2) issue_copy(c2, std::integral_constant<int, NGA>{});
-          chain_sm(sc, 0, 1);
-          wait_tiles<KI>(0);
-          __syncthreads();
-        }
-        // this lane's V fragment offsets for value blocks 4w and 4w+1, key
-        // half 0 (other blocks and halves are instruction offsets)
-        uint32_t vbo[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) vbo[k] = vt_off<NGA>(w * NDVB + (k >> 1), 0, lane, k & 1);
-        for (int t = 0; t < n_tiles; ++t) {  // sc = S(t+1)
-          const float scl = prep_scores(sc, t + 1);
-          uint32_t a[4], b[4], vb[4];
-          frag_addrs((t + 2) & (NB - 1), a, b);
-          const uint32_t vtile = lds_a + (t & (NB - 1)) * SM::ATILE;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) vb[k] = vtile + vbo[k];
-          TileSrc src = tile_src(min(t + NB - 1, n_tiles - 1), (t + NB - 1) & (NB - 1));
-          if (t + NB - 1 >= n_tiles) {
-            src.ra[2] = 0;
-            src.rb[2] = 0;
-          }
-          tile_step(sc, O, qf, a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], scl, m_ref, m_run, l_part, l_rnd,
-                    lds_addr(sm.p[(t + 1) & 1][w][0]) + lane * 16, lds_addr(sm.p[t & 1][0][0]) + lane * 16, vb,
-                    src.oa, src.ob, src.ra, src.rb, src.la + (uint32_t)(w * NGA) * 1024u, src.lb + (uint32_t)w * 1024u);
-          wait_tiles<KI>(0);  // tile t+3
-          __syncthreads();
-        }
-        // the step's last MFMAs write O (AGPRs) without the wait states that
-        // a following VALU access of O needs
-        asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
-      }
-    } else {
-      if (n_tiles > 0) {
-        const int pre = min(n_tiles, NB - 1);
-        for (int u = 0; u < pre; ++u) issue_tile(u, u);
-        wait_tiles<KI>(pre - min(pre, 2));   // tiles 0 and 1 have landed
-        __syncthreads();
-        {
-          float x[16];
-          scores(qk(0), 0, true, x);
-          const float mu = mu_of();
-          bf16x4 bq[4];
-          unroll<4>([&](auto Q) __attribute__((always_inline)) { weights_q(x, 0, mu, bq, Q); });
-        }
-        __syncthreads();
-        int buf = 0;
-        for (int t = 0; t < n_tiles; ++t) {
-          const int nbuf = buf == NB - 1 ? 0 : buf + 1;
-          const int cbuf = buf == 0 ? NB - 1 : buf - 1;
-          const bool live = t + 1 < n_tiles;
-          f32x16 s = f32x16{};
-          if (live) s = qk(nbuf);
-          float x[16];
-          float mu = 0.f;
-          bf16x4 bq[4];
-          const bool copy = t + NB - 1 < n_tiles;
-          const TileSrc src = tile_src(min(t + NB - 1, n_tiles - 1), cbuf);
-          // P(t) V(t); along the way the copies of tile t+NB-1 and the softmax
-          // of S(t+1): its first half after MFMA group 0, its quarters after
-          // groups NPV/5, 2NPV/5, 3NPV/5 and 4NPV/5
-          pv(buf, t & 1, [&](auto G) __attribute__((always_inline)) {
-            constexpr int g = decltype(G)::value;
-            if (copy) {
-              unroll<(g + 1) * KI / NPV - g * KI / NPV>([&](auto I) __attribute__((always_inline)) {
-                issue_copy(src, std::integral_constant<int, g * KI / NPV + decltype(I)::value>{});
-              });
-            }
-            if constexpr (g == 0) {
-              scores(s, t + 1, live, x);
-              mu = mu_of();
-            }
-            unroll<4>([&](auto Q) __attribute__((always_inline)) {
-              if constexpr ((decltype(Q)::value + 1) * NPV / 5 == g) weights_q(x, (t + 1) & 1, mu, bq, Q);
-            });
-          });
-          // tile t+2 must have landed; the copies of tile t+NB-1 may stay in flight
-          wait_tiles<KI>(min(n_tiles - 1, t + NB - 1) - (t + 2));
-          __syncthreads();
-          buf = nbuf;
-        }
-      }
-    }
-    if (pass == 0) {
-      over |= m_run > m_ref + TAU;  // (the softmax in the Q.K chain tracks only m_run)
-      // the P buffers are idle now: their space carries the overflow flags
-      const bool any = __ballot(over) != 0ull;
-      if (lane == 0) sm.epi.flag[w] = any;
-      __syncthreads();
-      redo = (sm.epi.flag[0] | sm.epi.flag[1] | sm.epi.flag[2] | sm.epi.flag[3]) != 0;
-    }
-  }
-
-  // Lane-derived values are recomputed here rather than held across the key
-  // loop, where the register pressure would spill them to be reloaded one
-  // after another, each reload a round trip to memory.
-  {
-    int t = threadIdx.x;
-    asm volatile("" : "+v"(t));
-    lane = t & 63;
-    h = lane >> 5;
-    lr = lane & 31;
-  }
-
-  // ------------------------------------------------------------- epilogue
-  {
-    const float l_row = xhalf_sum(l_part);
-    const float l_row_rnd = xhalf_sum(l_rnd);
-    const float lse_cur = l_row > 0.f ? (m_ref + log2f(l_row)) * LN2 : -INFINITY;
-    const float inv = l_row_rnd > 0.f ? 1.f / l_row_rnd : 0.f;
-    const bool ok = row_valid(w);
-    float lp = -INFINITY;
-    const int hq = row_head(w);
-    const int64_t tq = qtok(row_query(w));
-    if (p.prev_lse.p && ok) lp = p.prev_lse.p[cx.b * p.prev_lse.sb + hq * p.prev_lse.sh + tq * p.prev_lse.st];
-    const float mx = fmaxf(lp, lse_cur);
-    float L, wp, wc;
-    if (mx == -INFINITY) {
-      L = -INFINITY; wp = 0.f; wc = 0.f;
-    } else {
-      const float ea = lp == -INFINITY ? 0.f : expf(lp - mx);
-      const float eb = lse_cur == -INFINITY ? 0.f : expf(lse_cur - mx);
-      const float z = ea + eb;
-      L = mx + logf(z);
-      wp = ea / z;
-      wc = eb / z * inv;
-    }
-    if (h == 0) {
-      sm.epi.wprev[w * 32 + lr] = wp;
-      sm.epi.wcur[w * 32 + lr] = wc;
-      if (p.lse.p && ok) p.lse.p[cx.b * p.lse.sb + hq * p.lse.sh + tq * p.lse.st] = L;
-    }
-  }
-  __syncthreads();
-
-  if (!p.prev_out.p && !p.out_f32) {
-    // Plain bf16 output: O^T sits in the accumulators with one output row per
-    // lane, so direct stores would be 8-byte pieces of 32 rows each.  Instead
-    // the scaled bf16 rows go through LDS (the idle tile buffers; the row
-    // stride is padded by 16 bytes to spread the banks) and leave as whole
-    // rows, 16 bytes a lane.
-    constexpr int RS = DV * 2 + 16;           // LDS row stride, bytes
-    constexpr int LPR = DV * 2 / 16;          // lanes per output row
-    constexpr int RPI = 64 / LPR;             // rows per store instruction
-    // staging space: the tile buffers and what follows them up to P
-    constexpr int CAP = (int)(sizeof(sm.a) + sizeof(sm.b) + sizeof(sm.v) + sizeof(sm.idx));
-    constexpr int NPASS = ROWS * RS <= CAP ? 1 : 2;  // halves of the rows at a time
-    static_assert(ROWS * RS <= 2 * CAP, "half of the rows fits the staging space");
-    constexpr int RBP = WAVES / NPASS;        // row blocks per pass
-    const uint32_t stage = lds_addr(&sm.a[0][0]);
-    // output row rl of row block rb (workgroup row 32 rb + rl) is at element
-    // out_off + rb * o_srb + rl * o_srl; it exists iff rb < o_nrb and
-    // rl < o_nrl (latent) or 32 rb + rl < o_nr (split, sparse)
-    int64_t out_off, o_srb, o_srl;
-    int o_nrb = 0, o_nrl = 0, o_nr = 0;
-    if constexpr (MODE == LATENT) {
-      out_off = cx.b * p.out.sb + cx.hbase * p.out.sh + qtok(cx.q0) * p.out.st;
-      o_srb = p.out.sh;
-      o_srl = p.out.st;
-      o_nrb = p.Hq - cx.hbase;
-      o_nrl = (int)min<int64_t>(32, cx.q_len - cx.q0);
-    } else if constexpr (MODE == SPLIT) {
-      out_off = cx.b * p.out.sb + cx.hbase * p.out.sh + qtok(cx.q0) * p.out.st;
-      o_srb = 32 * p.out.st;
-      o_srl = p.out.st;
-      o_nr = (int)min<int64_t>(ROWS, cx.q_len - cx.q0);
-    } else {
-      out_off = cx.b * p.out.sb + qtok(cx.q0) * p.out.st;
-      o_srb = 32 * p.out.sh;
-      o_srl = p.out.sh;
-      o_nr = p.Hq;
-    }
-#pragma unroll
-    for (int pass_ = 0; pass_ < NPASS; ++pass_) {
-#pragma unroll
-      for (int rbl = 0; rbl < RBP; ++rbl) {
-        const int rb = pass_ * RBP + rbl;
-        const float wc = sm.epi.wcur[rb * 32 + lr];
-        const uint32_t row = stage + (uint32_t)(rbl * 32 + lr) * RS;
-#pragma unroll
-        for (int j = 0; j < NDVB; ++j) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = 32 * (w * NDVB + j) + 8 * g + 4 * h;
-            const u32x2 v = {pack_bf16x2(wc * O[rb][j][4 * g], wc * O[rb][j][4 * g + 1]),
-                             pack_bf16x2(wc * O[rb][j][4 * g + 2], wc * O[rb][j][4 * g + 3])};
-            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)(row + d * 2)) = v;
-          }
-        }
-      }
-      __syncthreads();
-      // this wave stores staged rows w*RPI + k*WAVES*RPI (+ lane/LPR), k < NST,
-      // reading a batch of them from LDS before storing the batch.  Staged
-      // row k sits in row block rb0 + k/KB of the workgroup at row
-      // rl0 + (k%KB)*WAVES*RPI of the block.
-      constexpr int NST = RBP * 32 / (WAVES * RPI);
-      constexpr int BATCH = NST < 8 ? NST : 8;
-      constexpr int KB = 32 / (WAVES * RPI);
-      static_assert(NST % BATCH == 0 && 32 % (WAVES * RPI) == 0, "store batches");
-      const int rb0 = pass_ * RBP, rl0 = w * RPI + lane / LPR;
-      // this lane's element address in the output, stepped along the rows in
-      // vector registers (the scalar ones are all taken here)
-      int64_t orow = out_off + (int64_t)rb0 * o_srb + (int64_t)rl0 * o_srl + (lane % LPR) * 8;
-      int64_t ostep = (int64_t)(WAVES * RPI) * o_srl, oblk = o_srb - (int64_t)KB * ostep;
-      asm volatile("" : "+v"(orow), "+v"(ostep), "+v"(oblk));
-#pragma unroll
-      for (int k0 = 0; k0 < NST; k0 += BATCH) {
-        u32x4 v[BATCH];
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k) {
-          const int rs = (w + (k0 + k) * WAVES) * RPI + lane / LPR;
-          v[k] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-              (uintptr_t)(stage + (uint32_t)rs * RS + (lane % LPR) * 16));
-        }
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k) {
-          const int kk = k0 + k, rb = rb0 + kk / KB, rl = rl0 + (kk % KB) * (WAVES * RPI);
-          const bool ok = MODE == LATENT ? rb < o_nrb && rl < o_nrl : rb * 32 + rl < o_nr;
-          if (ok) *reinterpret_cast<u32x4*>(p.out.p + orow) = v[k];
-          orow += (kk + 1) % KB ? ostep : ostep + oblk;
-        }
-      }
-      if (NPASS > 1 && pass_ + 1 < NPASS) __syncthreads();
-    }
-    return;
-  }
-
-#pragma unroll
-  for (int rb = 0; rb < WAVES; ++rb) {
-    if (!row_valid(rb)) continue;
-    const float wp = sm.epi.wprev[rb * 32 + lr];
-    const float wc = sm.epi.wcur[rb * 32 + lr];
-    const int hq = row_head(rb);
-    const int64_t tq = qtok(row_query(rb));
-    const int64_t oel = cx.b * p.out.sb + hq * p.out.sh + tq * p.out.st;
-    const int64_t pel = cx.b * p.prev_out.sb + hq * p.prev_out.sh + tq * p.prev_out.st;
-    const bool fold = p.prev_out.p && wp != 0.f;
-#pragma unroll
-    for (int j = 0; j < NDVB; ++j) {
-      const int dvb = 32 * (w * NDVB + j);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = dvb + 8 * g + 4 * h;
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = wc * O[rb][j][4 * g + e];
-        if (fold) {
-          if (p.prev_f32) {
-            const f32x4 pv4 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.prev_out.p) + pel + d);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] += wp * pv4[e];
-          } else {
-            const u32x2 pv2 = *reinterpret_cast<const u32x2*>(p.prev_out.p + pel + d);
-            y[0] += wp * __uint_as_float(pv2[0] << 16);
-            y[1] += wp * __uint_as_float(pv2[0] & 0xffff0000u);
-            y[2] += wp * __uint_as_float(pv2[1] << 16);
-            y[3] += wp * __uint_as_float(pv2[1] & 0xffff0000u);
-          }
-        }
-        if (p.out_f32) {
-          const f32x4 st = {y[0], y[1], y[2], y[3]};
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out.p) + oel + d) = st;
-        } else {
-          const u32x2 st = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-          *reinterpret_cast<u32x2*>(p.out.p + oel + d) = st;
-        }
-      }
-    }
-  }
+// Several calls in one launch: the workgroup serves the call whose range of
+// workgroups holds blockIdx.x.
+template <class C, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, kWavesPerEU<MODE>)))
+void attn_fwd_group_kernel(const GroupParams g) {
+  int call = 0;
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < g.n && (int)blockIdx.x >= g.first[i]) call = i;
+  const AttnParams& p = g.sub[call];
+  const int64_t first_wg = g.first[call];
+#include "mla_attn_body.inc"
 }
 
 // Debug gather: one workgroup stages the listed rows tile by tile through the
@@ -1110,6 +379,13 @@ hipError_t launch_latent_dense(const AttnParams& p, hipStream_t s) {
   const int64_t items = (int64_t)p.n_qblk * p.n_hgrp * p.B;
   if (items == 0) return hipSuccess;
   return launch_items<LATENT>(p, items, s);
+}
+
+hipError_t launch_latent_group(const GroupParams& g, hipStream_t s) {
+  const int64_t items = g.first[g.n];
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_group_kernel<LatentCfg, LATENT>), dim3((unsigned)items), dim3(256), 0, s, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_latent_sparse(const AttnParams& p, hipStream_t s) {

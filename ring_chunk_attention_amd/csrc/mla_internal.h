@@ -66,6 +66,16 @@ struct AttnParams {
   const int32_t* kv_lens;   // decode: valid rows per sequence [B], or nullptr (Nkv)
 };
 
+// Several shared-latent calls in one launch (a ring step for all query
+// chunks): call k serves workgroups [first[k], first[k+1]).
+constexpr int kMaxGroup = 4;
+struct GroupParams {
+  int32_t n;
+  int32_t first[kMaxGroup + 1];
+  AttnParams sub[kMaxGroup];
+};
+static_assert(sizeof(GroupParams) <= 4096, "kernel arguments are limited to 4 KB");
+
 // Decode split-K reduction: partial results of S key ranges per (b, h),
 // element (b, s, h, d) of po at ((b * S + s) * H + h) * dv + d and its LSE
 // at pl[(b * S + s) * H + h].
@@ -97,6 +107,7 @@ struct GatherParams {
 };
 
 hipError_t launch_latent_dense(const AttnParams& p, hipStream_t s);
+hipError_t launch_latent_group(const GroupParams& g, hipStream_t s);
 hipError_t launch_latent_sparse(const AttnParams& p, hipStream_t s);
 hipError_t launch_split(const AttnParams& p, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);

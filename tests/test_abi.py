@@ -189,3 +189,18 @@ def test_decode_workspace_size(lib):
     assert lib.mla_decode_workspace_size(64, 128, 8192, 0) == 256 + 64 * 4 * 128 * 4 + 64 * 4 * 128 * 512 * 4
     assert lib.mla_decode_workspace_size(4, 128, 8192, 2) == 0      # a split would exceed 2048 rows
     assert lib.mla_decode_workspace_size(4, 128, 200000, 0) == 0    # beyond 64 splits
+
+
+def test_group_rejects_bad_calls(lib):
+    from ring_chunk_attention_amd.binding import MlaFwdCall, MlaRows
+    q, kv, out = MlaRows(FAKE, 0, 8192 * 576, 576), MlaRows(FAKE, 0, 8192 * 576, 576), MlaRows(FAKE, 0, 8192 * 512, 512)
+    good = MlaFwdCall(ctypes.pointer(q), None, ctypes.pointer(kv), None, 1, 16, 1024, 1024, 576, 0, 512, 0.07, 1,
+                      0, 0, None, None, ctypes.pointer(out), None)
+    bad = MlaFwdCall(ctypes.pointer(q), None, ctypes.pointer(kv), None, 1, 16, 1024, 1024, 576, 0, 500, 0.07, 1,
+                     0, 0, None, None, ctypes.pointer(out), None)
+    arr = (MlaFwdCall * 5)(good, bad, good, good, good)
+    assert lib.mla_fwd_group(5, arr, None) == MLA_ERR_INVALID_ARG
+    assert "[0, 4]" in lib.mla_last_error().decode()
+    assert lib.mla_fwd_group(2, arr, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_last_error().decode().startswith("call 1:")
+    assert lib.mla_fwd_group(0, None, None) == MLA_OK

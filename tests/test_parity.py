@@ -493,3 +493,30 @@ def test_decode_config_sampled(mla):
     o_ref, l_ref = oracle.decode_mla(c.q[seqs], c.kv[seqs], c.kv_lens[seqs], 512, c.scale)
     assert report("decode cfg O", host(out[seqs]), o_ref) <= O_TOL
     assert report("decode cfg LSE", host(lse[seqs]), l_ref) <= LSE_TOL
+
+
+# ---------------------------------------------------------------------------
+# several calls in one launch (a ring step for all query chunks)
+# ---------------------------------------------------------------------------
+def test_group_bit_identical_to_separate_calls(mla):
+    """Calls of different shapes, offsets, masks and fold options in one
+    mla_fwd_group launch give the same bits as one mla_fwd each."""
+    c = W.dense_case(B=2, H=8, N=600, Nkv=900, seed=80)
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    g = torch.Generator().manual_seed(81)
+    p_out = torch.randn((2, 8, 100, 512), generator=g).cuda()            # fp32 running output
+    p_lse = (torch.rand((2, 8, 100), generator=g) * 8).cuda()
+    def calls():
+        return [dict(q=q[:, :, :256], kv=kv[:, :, :300], scale=c.scale, causal=True, q_offset=44),
+                dict(q=q[:, :5, 256:], kv=kv[:, :, 300:], scale=c.scale, causal=False),
+                dict(q=q[:, :, 100:200], kv=kv, scale=c.scale, causal=True, q_offset=800,
+                     prev=(p_out, p_lse), out=torch.empty_like(p_out)),
+                dict(q=q[:1, :, :33], kv=kv[:1, :, :40], scale=c.scale, causal=True, q_offset=7)]
+    grouped = mla.fwd_group(calls())
+    separate = [mla.fwd(workspace=None, **k) for k in calls()]
+    torch.cuda.synchronize()
+    for (og, lg), (os_, ls) in zip(grouped, separate):
+        assert og.dtype == os_.dtype
+        assert torch.equal(og.view(torch.int16) if og.dtype == torch.bfloat16 else og.view(torch.int32),
+                           os_.view(torch.int16) if os_.dtype == torch.bfloat16 else os_.view(torch.int32))
+        assert torch.equal(lg, ls)
