@@ -310,6 +310,9 @@ mla_status mla_fwd_group(int32_t n, const mla_fwd_call* calls, void* stream) {
     g.first[++g.n] = (int32_t)items;
   }
   if (g.n == 0) return MLA_OK;
+  g.interleave = 1;
+  for (int k = 1; k < g.n; ++k)
+    if (g.first[k + 1] - g.first[k] != g.first[1]) g.interleave = 0;
   return hip_status(mla::launch_latent_group(g, static_cast<hipStream_t>(stream)), "group attention launch");
 }
 

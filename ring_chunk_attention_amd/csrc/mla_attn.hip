@@ -290,20 +290,28 @@ constexpr int kWavesPerEU = MODE == 1 ? 2 : 1;
 template <class C, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, kWavesPerEU<MODE>)))
 void attn_fwd_kernel(const AttnParams p) {
-  constexpr int64_t first_wg = 0;
+  const int64_t call_item = blockIdx.x;
 #include "mla_attn_body.inc"
 }
 
-// Several calls in one launch: the workgroup serves the call whose range of
-// workgroups holds blockIdx.x.
+// Several calls in one launch.  Calls with equal item counts (the query
+// chunks of a ring step) take workgroups in turn, so that the launch runs
+// the longest items of every call first; otherwise call k takes the
+// workgroups [first[k], first[k+1]).
 template <class C, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, kWavesPerEU<MODE>)))
 void attn_fwd_group_kernel(const GroupParams g) {
   int call = 0;
-  for (int i = 1; i < kMaxGroup; ++i)
-    if (i < g.n && (int)blockIdx.x >= g.first[i]) call = i;
+  int64_t call_item;
+  if (g.interleave) {
+    call = (int)(blockIdx.x % (unsigned)g.n);
+    call_item = blockIdx.x / (unsigned)g.n;
+  } else {
+    for (int i = 1; i < kMaxGroup; ++i)
+      if (i < g.n && (int)blockIdx.x >= g.first[i]) call = i;
+    call_item = (int64_t)blockIdx.x - g.first[call];
+  }
   const AttnParams& p = g.sub[call];
-  const int64_t first_wg = g.first[call];
 #include "mla_attn_body.inc"
 }
 

@@ -67,10 +67,12 @@ struct AttnParams {
 };
 
 // Several shared-latent calls in one launch (a ring step for all query
-// chunks): call k serves workgroups [first[k], first[k+1]).
+// chunks): call k serves workgroups [first[k], first[k+1]), or every n-th
+// workgroup when the calls have equal item counts (interleave).
 constexpr int kMaxGroup = 4;
 struct GroupParams {
   int32_t n;
+  int32_t interleave;       // all calls have the same item count: item i of call k is workgroup i*n + k
   int32_t first[kMaxGroup + 1];
   AttnParams sub[kMaxGroup];
 };

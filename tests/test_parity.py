@@ -520,3 +520,27 @@ def test_group_bit_identical_to_separate_calls(mla):
         assert torch.equal(og.view(torch.int16) if og.dtype == torch.bfloat16 else og.view(torch.int32),
                            os_.view(torch.int16) if os_.dtype == torch.bfloat16 else os_.view(torch.int32))
         assert torch.equal(lg, ls)
+
+
+def test_group_equal_calls_interleaved_bit_identical(mla):
+    """Calls with equal workgroup counts take workgroups in turn; still the
+    same bits as separate calls (here: the three query chunks of a ring step
+    with different KV chunks, prev folds and both output types)."""
+    c = W.dense_case(B=1, H=8, N=384, seed=82)
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    g = torch.Generator().manual_seed(83)
+    prev = [(torch.randn((1, 8, 128, 512), generator=g).cuda(), (torch.rand((1, 8, 128), generator=g) * 6).cuda())
+            for _ in range(3)]
+    def calls():
+        return [dict(q=q[:, :, 128 * r:128 * (r + 1)], kv=kv[:, :, 128 * k:128 * (k + 1)], scale=c.scale,
+                     causal=True, q_offset=128 * r, kv_offset=128 * k, prev=prev[r],
+                     out=torch.empty((1, 8, 128, 512), dtype=torch.float32 if r else torch.bfloat16,
+                                     device="cuda"))
+                for r, k in ((0, 0), (1, 0), (2, 1))]
+    grouped = mla.fwd_group(calls())
+    separate = [mla.fwd(workspace=None, **k) for k in calls()]
+    torch.cuda.synchronize()
+    for (og, lg), (os_, ls) in zip(grouped, separate):
+        view = torch.int16 if og.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(og.view(view), os_.view(view))
+        assert torch.equal(lg, ls)
