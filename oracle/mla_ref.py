@@ -247,9 +247,14 @@ def sparse_mla(q_lift, q_pe, c_kv, k_pe, idx, scale: float,
 # token generation: one new query per sequence over its valid cache rows
 # ---------------------------------------------------------------------------
 def decode_mla(q: np.ndarray, kv: np.ndarray, kv_lens: Optional[Sequence[int]],
-               head_dim_v: int, scale: float) -> Tuple[np.ndarray, np.ndarray]:
-    """q [B, H, dk] (the newest token of each sequence), kv [B, Nkv, dk],
+               head_dim_v: int, scale: float,
+               kv_slots: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """q [B, H, dk] (the newest token of each sequence), kv [n_slots, Nkv, dk],
     kv_lens [B] (None: Nkv for every sequence) -> out [B, H, dv], lse [B, H].
+
+    kv_slots [B] (TT-NN ring_mla kv_cache_batch_idx: one batch slot of an
+    indexed cache) names the cache slot sequence b reads; None reads slot b.
+    A slot outside [0, n_slots) leaves the sequence without valid rows.
 
     Mojo mha_single_batch_pipelined (token generation, seq_len = 1, with
     num_keys valid cache entries per sequence): the query of sequence b is
@@ -261,15 +266,16 @@ def decode_mla(q: np.ndarray, kv: np.ndarray, kv_lens: Optional[Sequence[int]],
     page's split-K with its separate reduction.
     """
     B, H, dk = q.shape
-    Nkv = kv.shape[1]
+    n_slots, Nkv = kv.shape[0], kv.shape[1]
     lens = [Nkv] * B if kv_lens is None else [int(x) for x in kv_lens]
+    slots = list(range(B)) if kv_slots is None else [int(x) for x in kv_slots]
     out = np.zeros((B, H, head_dim_v))
     lse = np.full((B, H), NEG_INF)
     for b in range(B):
         n = max(0, min(Nkv, lens[b]))
-        if n == 0:
+        if n == 0 or not 0 <= slots[b] < n_slots:
             continue
-        k = kv[b, :n]
+        k = kv[slots[b], :n]
         o, l = attention(q[b], k, k[:, :head_dim_v], scale, causal=False,
                          q_pos=np.zeros(H, dtype=np.int64), k_pos=np.zeros(n, dtype=np.int64))
         out[b], lse[b] = o, l

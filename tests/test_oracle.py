@@ -509,6 +509,21 @@ def test_decode_split_keys_merge_to_whole(cut):
     np.testing.assert_allclose(l, whole[1], atol=1e-12)
 
 
+def test_decode_slots_select_cache_rows():
+    """kv_slots: sequence b reads cache slot kv_slots[b]; the same as decoding
+    against the cache rearranged so that slot b holds that slot; a slot out of
+    range gives (0, -inf)."""
+    rng = np.random.default_rng(64)
+    q = _rand(rng, 4, 3, 7)
+    kv = _rand(rng, 5, 20, 7)
+    slots, lens = [3, 0, 3, 9], [20, 6, 11, 20]
+    out, lse = oracle.decode_mla(q, kv, lens, 4, 0.6, kv_slots=slots)
+    ref_o, ref_l = oracle.decode_mla(q[:3], kv[[3, 0, 3]], lens[:3], 4, 0.6)
+    np.testing.assert_array_equal(out[:3], ref_o)
+    np.testing.assert_array_equal(lse[:3], ref_l)
+    assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
+
+
 # ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by a pin above
 # ---------------------------------------------------------------------------
@@ -568,9 +583,9 @@ def test_planted_merge_sign_is_caught(monkeypatch):
 def test_planted_decode_short_by_one_is_caught(monkeypatch):
     orig = mla_ref.decode_mla
 
-    def mutant(q, kv, kv_lens, head_dim_v, scale):
+    def mutant(q, kv, kv_lens, head_dim_v, scale, kv_slots=None):
         lens = [kv.shape[1]] * q.shape[0] if kv_lens is None else list(kv_lens)
-        return orig(q, kv, [max(0, int(n) - 1) for n in lens], head_dim_v, scale)
+        return orig(q, kv, [max(0, int(n) - 1) for n in lens], head_dim_v, scale, kv_slots)
     monkeypatch.setattr(oracle, "decode_mla", mutant)
     with pytest.raises(AssertionError):
         test_decode_zero_scale_prefix_mean()
