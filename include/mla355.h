@@ -237,12 +237,16 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe,
  *
  * q [B, H, dq] plus, optionally, q_rope [B, H, dr]: the newest token of each
  * sequence (views with b = sequence, h = head; stride_t is ignored).
- * kv [B, Nkv, dq] plus, optionally, k_rope [B, Nkv, dr]: the latent cache
- * (views with t = cache row; stride_h is ignored).  kv_lens: device int32
- * [B], the valid rows of each sequence (clamped to [0, Nkv]), or NULL for
- * Nkv everywhere.  Sequence b's query sees its first kv_lens[b] rows, all of
- * them; the score is scale * q.row over dq + dr columns, the value the first
- * dv columns of the row.
+ * kv [n_slots, Nkv, dq] plus, optionally, k_rope [n_slots, Nkv, dr]: the
+ * latent cache (views with b = cache slot, t = cache row; stride_h is
+ * ignored).  kv_slots: device int32 [B], the cache slot each sequence reads
+ * (TT-NN ring_mla kv_cache_batch_idx: one batch slot of an indexed cache),
+ * with n_slots > 0 slots; a slot outside [0, n_slots) leaves the sequence
+ * without valid rows.  NULL: sequence b reads slot b (n_slots 0 or >= B).
+ * kv_lens: device int32 [B], the valid rows of each sequence (clamped to
+ * [0, Nkv]), or NULL for Nkv everywhere.  Sequence b's query sees the first
+ * kv_lens[b] rows of its slot, all of them; the score is scale * q.row over
+ * dq + dr columns, the value the first dv columns of the row.
  *
  * out [B, H, dv] bf16 and lse [B, H] fp32 natural-log LSE (or NULL), views
  * with stride_t ignored.  A sequence with no valid row gets out = 0 and
@@ -267,6 +271,7 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe,
 mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope,
                           const mla_rows* kv, const mla_rows* k_rope,
                           const int32_t* kv_lens,
+                          const int32_t* kv_slots, int32_t n_slots,
                           int32_t B, int32_t H, int64_t Nkv,
                           int32_t dq, int32_t dr, int32_t dv, float scale,
                           int32_t n_splits,

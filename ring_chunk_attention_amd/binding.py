@@ -82,7 +82,8 @@ def _load():
     lib.mla_workspace_size.restype = ctypes.c_size_t
     lib.mla_workspace_size.argtypes = []
     lib.mla_decode_fwd.restype = ctypes.c_int
-    lib.mla_decode_fwd.argtypes = [_P, _P, _P, _P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+    lib.mla_decode_fwd.argtypes = [_P, _P, _P, _P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]
@@ -391,16 +392,18 @@ _DECODE_WS = {}
 
 
 def decode_fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float,
-               kv_lens: Optional[torch.Tensor] = None, head_dim_v: int = 512,
+               kv_lens: Optional[torch.Tensor] = None, kv_slots: Optional[torch.Tensor] = None,
+               head_dim_v: int = 512,
                q_rope: Optional[torch.Tensor] = None, k_rope: Optional[torch.Tensor] = None,
                n_splits: int = 0, out: Optional[torch.Tensor] = None,
                lse: Optional[torch.Tensor] = None, want_lse: bool = True,
                workspace: Optional[torch.Tensor] = None
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Token generation (mla_decode_fwd): q [B, H, dq] (the newest token of
-    each sequence), kv [B, Nkv, dq] (the latent cache), optional q_rope
-    [B, H, dr] / k_rope [B, Nkv, dr], kv_lens int32 [B] on the GPU (valid
-    rows; None = Nkv).  Returns (out [B, H, dv] bf16, lse [B, H] fp32 or
+    each sequence), kv [n_slots, Nkv, dq] (the latent cache), optional q_rope
+    [B, H, dr] / k_rope [n_slots, Nkv, dr], kv_lens int32 [B] on the GPU
+    (valid rows; None = Nkv), kv_slots int32 [B] on the GPU (the cache slot
+    of each sequence; None = slot b).  Returns (out [B, H, dv] bf16, lse [B, H] fp32 or
     None).  n_splits = 0 lets the library split the keys; ``workspace`` (a
     uint8 GPU tensor) defaults to a cached per-stream buffer."""
     B, H, dq = q.shape
@@ -416,10 +419,12 @@ def decode_fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float,
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.bfloat16)
-    if kv_lens is not None:
-        _need(kv_lens, "kv_lens", torch.int32)
-        if kv_lens.shape != (B,) or not kv_lens.is_contiguous():
-            raise ValueError("kv_lens: expected a contiguous [B] tensor")
+    for t, n in ((kv_lens, "kv_lens"), (kv_slots, "kv_slots")):
+        if t is not None:
+            _need(t, n, torch.int32)
+            if t.shape != (B,) or not t.is_contiguous():
+                raise ValueError(f"{n}: expected a contiguous [B] tensor")
+    n_slots = kv.shape[0] if kv_slots is not None else 0
     need = int(LIB.mla_decode_workspace_size(B, H, Nkv, n_splits))
     if need == 0:
         raise MlaError(2, f"no key split fits Nkv={Nkv} with n_splits={n_splits}")
@@ -442,6 +447,7 @@ def decode_fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float,
         vl = MlaRows(lse.data_ptr(), lse.stride(0), lse.stride(1), 0)
     _check(LIB.mla_decode_fwd(ctypes.byref(vq), _ref(vqr), ctypes.byref(vkv), _ref(vkr),
                               kv_lens.data_ptr() if kv_lens is not None else None,
+                              kv_slots.data_ptr() if kv_slots is not None else None, n_slots,
                               B, H, Nkv, dq, dr, dv, float(scale), n_splits,
                               ctypes.byref(vo), _ref(vl), workspace.data_ptr(), workspace.numel(),
                               _stream(q.device)))

@@ -400,7 +400,8 @@ size_t mla_decode_workspace_size(int32_t B, int32_t H, int64_t Nkv, int32_t n_sp
 }
 
 mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
-                          const mla_rows* k_rope, const int32_t* kv_lens, int32_t B, int32_t H,
+                          const mla_rows* k_rope, const int32_t* kv_lens, const int32_t* kv_slots,
+                          int32_t n_slots, int32_t B, int32_t H,
                           int64_t Nkv, int32_t dq, int32_t dr, int32_t dv, float scale,
                           int32_t n_splits, const mla_rows* out, const mla_rows* lse,
                           void* workspace, size_t workspace_bytes, void* stream) {
@@ -423,6 +424,10 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_r
   if (lse && (st = check_lse(lse, "lse"))) return st;
   if (kv_lens && (reinterpret_cast<uintptr_t>(kv_lens) & 3u))
     return fail(MLA_ERR_INVALID_ARG, "kv_lens must be 4-byte aligned");
+  if (kv_slots && (reinterpret_cast<uintptr_t>(kv_slots) & 3u))
+    return fail(MLA_ERR_INVALID_ARG, "kv_slots must be 4-byte aligned");
+  if (kv_slots ? n_slots <= 0 : n_slots != 0 && n_slots < B)
+    return fail(MLA_ERR_INVALID_ARG, "n_slots: need n_slots > 0 with kv_slots, else 0 or at least B");
   if (Nkv * kv->stride_t * 2 > kMaxGrid || (k_rope && Nkv * k_rope->stride_t * 2 > kMaxGrid))
     return fail(MLA_ERR_UNSUPPORTED, "one sequence of the cache must span less than 2 GiB (row offsets are 32-bit)");
   int32_t S = 0, chunk = 0;
@@ -463,6 +468,8 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_r
   p.scale_log2 = scale * kLog2e;
   p.decode = 1;
   p.kv_lens = kv_lens;
+  p.kv_slots = kv_slots;
+  p.n_slots = kv_slots ? n_slots : B;
   p.queue = reinterpret_cast<unsigned*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mla::RowsM o_final{static_cast<uint16_t*>(out->data), out->stride_b, out->stride_h, 0};

@@ -278,6 +278,7 @@ struct Ctx {
   int64_t q_len;      // valid query rows of the sequence / batch
   int64_t q0;         // first query of the workgroup (latent/split), query index (sparse)
   int hbase;          // first head (latent), head (split)
+  int kv_slot;        // decode: the cache slot of the sequence
 };
 
 // The latent and sparse forms use the whole register file and LDS of a CU

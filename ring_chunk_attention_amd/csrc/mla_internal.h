@@ -64,6 +64,8 @@ struct AttnParams {
   // [q0 * topk, (q0 + 1) * topk) of its sequence's valid cache rows
   int32_t decode;
   const int32_t* kv_lens;   // decode: valid rows per sequence [B], or nullptr (Nkv)
+  const int32_t* kv_slots;  // decode: cache slot of each sequence [B], or nullptr (slot b)
+  int32_t n_slots;          // decode: slots of the cache
 };
 
 // Several shared-latent calls in one launch (a ring step for all query

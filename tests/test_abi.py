@@ -152,15 +152,17 @@ def test_binding_raises_with_message(lib):
         _check(MLA_ERR_INVALID_ARG)
 
 
-def call_decode(lib, q=None, kv=None, out=None, lse=None, kv_lens=None, B=4, H=128, Nkv=8192, dq=576,
-                dr=0, dv=512, scale=0.072, n_splits=0, workspace=0x20000000, workspace_bytes=1 << 40):
+def call_decode(lib, q=None, kv=None, out=None, lse=None, kv_lens=None, kv_slots=None, n_slots=0, B=4, H=128,
+                Nkv=8192, dq=576, dr=0, dv=512, scale=0.072, n_splits=0, workspace=0x20000000,
+                workspace_bytes=1 << 40):
     from ring_chunk_attention_amd.binding import MlaRows
     def conv(r):
         return None if r is None else ctypes.byref(MlaRows(r.data, r.stride_b, r.stride_h, r.stride_t))
     q = rows(sb=128 * 576, sh=576, st=0) if q is None else q
     kv = rows(sb=8192 * 576, sh=0, st=576) if kv is None else kv
     out = rows(sb=128 * 512, sh=512, st=0) if out is None else out
-    return lib.mla_decode_fwd(conv(q), None, conv(kv), None, kv_lens, B, H, Nkv, dq, dr, dv, scale, n_splits,
+    return lib.mla_decode_fwd(conv(q), None, conv(kv), None, kv_lens, kv_slots, n_slots, B, H, Nkv, dq, dr, dv,
+                              scale, n_splits,
                               conv(out), conv(lse), workspace, workspace_bytes, None)
 
 
@@ -176,6 +178,9 @@ def call_decode(lib, q=None, kv=None, out=None, lse=None, kv_lens=None, B=4, H=1
     (dict(n_splits=2), MLA_ERR_INVALID_ARG, "no split"),          # 4096 rows a split > 2048
     (dict(Nkv=200000), MLA_ERR_UNSUPPORTED, "no split"),          # > 64 splits of 2048
     (dict(kv_lens=FAKE + 2), MLA_ERR_INVALID_ARG, "kv_lens"),
+    (dict(kv_slots=FAKE + 2, n_slots=4), MLA_ERR_INVALID_ARG, "kv_slots"),
+    (dict(kv_slots=FAKE, n_slots=0), MLA_ERR_INVALID_ARG, "n_slots"),
+    (dict(n_slots=3), MLA_ERR_INVALID_ARG, "n_slots"),
 ])
 def test_decode_rejects_invalid_arguments(lib, kw, code, msg):
     assert call_decode(lib, **kw) == code

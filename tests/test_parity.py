@@ -544,3 +544,19 @@ def test_group_equal_calls_interleaved_bit_identical(mla):
         view = torch.int16 if og.dtype == torch.bfloat16 else torch.int32
         assert torch.equal(og.view(view), os_.view(view))
         assert torch.equal(lg, ls)
+
+
+def test_decode_indexed_cache_slots(mla):
+    """Sequences read cache slots through kv_slots (an indexed cache): two
+    sequences share slot 3, one slot is out of range (no valid rows)."""
+    rng = np.random.default_rng(84)
+    q = W.normal_bf16(rng, (4, 128, 576))
+    kv = W.normal_bf16(rng, (5, 2500, 576))
+    slots = np.array([3, 0, 3, 7], dtype=np.int32)
+    lens = np.array([2500, 640, 1200, 2500], dtype=np.int32)
+    out, lse = mla.decode_fwd(dev_bf16(q), dev_bf16(kv), scale=W.SCALE_192, kv_lens=dev(lens),
+                              kv_slots=dev(slots))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode_mla(q, kv, lens, 512, W.SCALE_192, kv_slots=slots)
+    assert report("slots O", host(out), o_ref) <= O_TOL
+    assert report("slots LSE", host(lse), l_ref) <= LSE_TOL
