@@ -290,13 +290,13 @@ def fwd_group(calls) -> list:
 def split_fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Tensor,
               v: torch.Tensor, *, scale: float, seq_lens: Optional[torch.Tensor] = None,
               causal: bool = True, prev: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
-              ) -> Tuple[torch.Tensor, torch.Tensor]:
+              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+              workspace="auto") -> Tuple[torch.Tensor, torch.Tensor]:
     """Split query/key ring step over [T, H, D] tensors (mla_fwd, Ascend
     RingMLAOperation layout): q1 [T, H, 128], q2 [T, H, 64], k1 [T, Hkv, 128],
     k2 [T, Hkv, 64], v [T, Hkv, 128]; seq_lens int32 [batch] on the GPU;
     prev = (prev_out [T, H, 128], prev_lse [H, T]).  Returns out [T, H, 128]
-    and lse [H, T]."""
+    and lse [H, T].  ``workspace`` as for fwd."""
     T, H, dq = q1.shape
     Hkv = k1.shape[1]
     dr = q2.shape[2]
@@ -320,8 +320,8 @@ def split_fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Te
                        seq_lens.data_ptr() if seq_lens is not None else None,
                        seq_lens.numel() if seq_lens is not None else 0,
                        float(scale), MLA_CAUSAL if causal else 0, 0, 0,
-                       _ref(vpo), _ref(vpl), ctypes.byref(vout), ctypes.byref(vl), None, 0,
-                       _stream(q1.device)))
+                       _ref(vpo), _ref(vpl), ctypes.byref(vout), ctypes.byref(vl),
+                       *_workspace(q1.device, workspace), _stream(q1.device)))
     return out, lse
 
 

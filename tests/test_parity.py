@@ -560,3 +560,16 @@ def test_decode_indexed_cache_slots(mla):
     o_ref, l_ref = oracle.decode_mla(q, kv, lens, 512, W.SCALE_192, kv_slots=slots)
     assert report("slots O", host(out), o_ref) <= O_TOL
     assert report("slots LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_split_workspace_bit_identical(mla):
+    """Split varlen step (1888 row blocks) with and without a workspace."""
+    c = W.split_case(seq_lens=[3000, 2500, 1800], H=32, Hkv=32, seed=85, with_prev=True)
+    args = [dev_bf16(x) for x in (c.q1, c.q2, c.k1, c.k2, c.v)]
+    sl = dev(c.seq_lens)
+    prev = (dev_bf16(c.prev_out), dev(c.prev_lse))
+    o1, l1 = mla.split_fwd(*args, scale=c.scale, seq_lens=sl, prev=prev, workspace=None)
+    o2, l2 = mla.split_fwd(*args, scale=c.scale, seq_lens=sl, prev=prev, workspace="auto")
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
