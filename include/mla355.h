@@ -83,6 +83,7 @@ typedef struct {
 #define MLA_CAUSAL 1u        /* key j visible to query i iff kv_offset + j <= q_offset + i */
 #define MLA_OUT_F32 2u       /* out holds float32 instead of bf16 */
 #define MLA_PREV_OUT_F32 4u  /* prev_out holds float32 instead of bf16 */
+#define MLA_VALID_LENS 8u    /* seq_lens holds the valid rows of each batch of padded tensors */
 
 /*
  * mla_fwd -- one attention call (one ring step).
@@ -110,6 +111,13 @@ typedef struct {
  * checked before launch (a negative length counts as 0, the sum is clipped to
  * T, and tokens past the sum are left unwritten).
  *
+ * Padded batches (MLA_VALID_LENS; shared-latent form): seq_lens is a device
+ * int32 [B] array (n_seqs == B) of valid lengths: batch b's query rows
+ * [0, min(len_b, Nq)) attend its key rows [0, min(len_b, Nkv)) (with the
+ * usual offsets and mask); later query rows are not written and later key
+ * rows are not attended (TT-NN ring_mla: padded chunks with a valid length,
+ * kv_actual_isl).  A negative length counts as 0.
+ *
  * Ring fold (Ascend calcType): prev_out [B, Hq, Nq, dv] and prev_lse
  * [B, Hq, Nq] are both NULL (first ring step) or both given; when given the
  * result is folded into them:  L = logaddexp(prev_lse, lse_new),
@@ -132,7 +140,7 @@ typedef struct {
  *
  * Kernels exist for:
  *   - shared latent:  Hkv == 1, v == NULL, dq + dr == 576, dv == 512
- *     (dr == 0 or 64), no seq_lens;
+ *     (dr == 0 or 64), no packed seq_lens (MLA_VALID_LENS is supported);
  *   - split:          v != NULL, q_rope and k_rope given, dq == 128, dr == 64,
  *     dv == 128, Hq % Hkv == 0, with or without seq_lens.
  * Other shapes return MLA_ERR_UNSUPPORTED.

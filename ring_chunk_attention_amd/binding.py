@@ -20,6 +20,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla355.
 MLA_CAUSAL = 1
 MLA_OUT_F32 = 2
 MLA_PREV_OUT_F32 = 4
+MLA_VALID_LENS = 8
 
 
 class MlaRows(ctypes.Structure):
@@ -229,7 +230,8 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 51
         v: Optional[torch.Tensor] = None,
         prev: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-        want_lse: bool = True, workspace="auto") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        want_lse: bool = True, workspace="auto", valid_lens: Optional[torch.Tensor] = None
+        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Attention over [B, H, N, D] tensors (mla_fwd).
 
     q [B, Hq, Nq, dq], kv [B, Hkv, Nkv, dq]; optional q_rope/k_rope
@@ -241,14 +243,22 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 51
     folds); their dtype selects the flag.  ``workspace``: "auto" (a cached
     per-stream buffer: row blocks from a device queue), None (row blocks by
     launch index) or a uint8 GPU tensor of at least mla_workspace_size()
-    bytes.
+    bytes.  ``valid_lens`` (int32 [B] on the GPU, shared-latent form): the
+    valid rows of each batch of padded tensors (MLA_VALID_LENS); later query
+    rows are not written and later key rows not attended.
     """
     a, out, lse = _fwd_args(q, kv, scale, head_dim_v, causal, q_offset, kv_offset, q_rope, k_rope, v,
                             prev, out, lse, want_lse)
     ws, ws_bytes = _workspace(q.device, workspace)
+    lens_ptr, flags = None, a["flags"]
+    if valid_lens is not None:
+        _need(valid_lens, "valid_lens", torch.int32)
+        if valid_lens.shape != (a["B"],) or not valid_lens.is_contiguous():
+            raise ValueError("valid_lens: expected a contiguous [B] tensor")
+        lens_ptr, flags = valid_lens.data_ptr(), flags | MLA_VALID_LENS
     _check(LIB.mla_fwd(ctypes.byref(a["q"]), _ref(a["q_rope"]), ctypes.byref(a["kv"]), _ref(a["k_rope"]),
                        _ref(a["v"]), a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["dq"], a["dr"], a["dv"],
-                       None, 0, a["scale"], a["flags"], a["q_offset"], a["kv_offset"],
+                       lens_ptr, a["B"] if lens_ptr else 0, a["scale"], flags, a["q_offset"], a["kv_offset"],
                        _ref(a["prev_out"]), _ref(a["prev_lse"]), ctypes.byref(a["out"]), _ref(a["lse"]),
                        ws, ws_bytes, _stream(q.device)))
     return out, lse

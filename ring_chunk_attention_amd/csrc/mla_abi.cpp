@@ -161,7 +161,7 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
   if (Hq % Hkv) return fail(MLA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (dq <= 0 || dr < 0 || dv <= 0 || dq % 8 || dr % 8 || dv % 8)
     return fail(MLA_ERR_INVALID_ARG, "head dims must be positive multiples of 8 (dq=%d dr=%d dv=%d)", dq, dr, dv);
-  if (flags & ~(MLA_CAUSAL | MLA_OUT_F32 | MLA_PREV_OUT_F32))
+  if (flags & ~(MLA_CAUSAL | MLA_OUT_F32 | MLA_PREV_OUT_F32 | MLA_VALID_LENS))
     return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
   if ((st = check_workspace(workspace, workspace_bytes))) return st;
@@ -189,7 +189,12 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
     return fail(MLA_ERR_INVALID_ARG, "out may alias prev_out only as the identical view");
   if (prev_lse && lse && lse->data == prev_lse->data && !same_view(lse, prev_lse))
     return fail(MLA_ERR_INVALID_ARG, "lse may alias prev_lse only as the identical view");
-  if (seq_lens) {
+  const bool valid_lens = flags & MLA_VALID_LENS;
+  if (valid_lens) {
+    if (!seq_lens) return fail(MLA_ERR_INVALID_ARG, "MLA_VALID_LENS needs seq_lens (valid rows per batch)");
+    if (n_seqs != B) return fail(MLA_ERR_INVALID_ARG, "MLA_VALID_LENS needs n_seqs == B (one length per batch)");
+    if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_INVALID_ARG, "seq_lens must be 4-byte aligned");
+  } else if (seq_lens) {
     if (B != 1) return fail(MLA_ERR_INVALID_ARG, "seq_lens requires B == 1 (tokens packed along t)");
     if (n_seqs <= 0) return fail(MLA_ERR_INVALID_ARG, "seq_lens given with n_seqs <= 0");
     if (Nq != Nkv) return fail(MLA_ERR_INVALID_ARG, "seq_lens requires Nq == Nkv (same lengths for query and key)");
@@ -208,8 +213,9 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
   p.prev_out = prev_out ? rc(prev_out) : mla::RowsC{nullptr, 0, 0, 0};
   p.lse = lm(lse);
   p.prev_lse = lc(prev_lse);
-  p.seq_lens = seq_lens;
-  p.n_seqs = seq_lens ? n_seqs : 0;
+  p.seq_lens = valid_lens ? nullptr : seq_lens;
+  p.n_seqs = seq_lens && !valid_lens ? n_seqs : 0;
+  p.valid_lens = valid_lens ? seq_lens : nullptr;
   p.da = dq;
   p.B = B;
   p.Hq = Hq;
@@ -224,8 +230,9 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
   p.prev_f32 = prev_f32 ? 1 : 0;
   p.queue = static_cast<unsigned*>(workspace);
 
-  const bool latent = !v && Hkv == 1 && dq + dr == 576 && dv == 512 && (dr == 0 || dr == 64) && !seq_lens;
-  const bool split = v && q_rope && dq == 128 && dr == 64 && dv == 128;
+  const bool latent = !v && Hkv == 1 && dq + dr == 576 && dv == 512 && (dr == 0 || dr == 64) &&
+                      (!seq_lens || valid_lens);
+  const bool split = v && q_rope && dq == 128 && dr == 64 && dv == 128 && !valid_lens;
   if (latent) {
     if (dr == 0) {
       // one 576-column tensor: the kernel reads its last 64 columns as the RoPE part
@@ -248,6 +255,7 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
   }
   return fail(MLA_ERR_UNSUPPORTED,
               "no kernel for Hq=%d Hkv=%d dq=%d dr=%d dv=%d v=%s seq_lens=%s (built: shared latent "
+              "(packed seq_lens: no; MLA_VALID_LENS: yes) "
               "Hkv=1 dq+dr=576 dv=512 v=NULL; split dq=128 dr=64 dv=128 with v)",
               Hq, Hkv, dq, dr, dv, v ? "given" : "NULL", seq_lens ? "given" : "NULL");
 }

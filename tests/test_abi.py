@@ -82,7 +82,7 @@ def call_fwd(lib, q=None, kv=None, out=None, lse=None, v=None, q_rope=None, k_ro
     (dict(Hq=6, Hkv=4), MLA_ERR_INVALID_ARG, "multiple of Hkv"),
     (dict(Hq=0), MLA_ERR_INVALID_ARG, "sizes"),
     (dict(dv=500), MLA_ERR_INVALID_ARG, "multiples of 8"),
-    (dict(flags=8), MLA_ERR_INVALID_ARG, "flag"),
+    (dict(flags=16), MLA_ERR_INVALID_ARG, "flag"),
     (dict(flags=5), MLA_ERR_INVALID_ARG, "without prev_out"),
     (dict(scale=float("nan")), MLA_ERR_INVALID_ARG, "scale"),
     (dict(q=Rows(FAKE + 2, 0, 576, 576)), MLA_ERR_INVALID_ARG, "aligned"),
@@ -209,3 +209,20 @@ def test_group_rejects_bad_calls(lib):
     assert lib.mla_fwd_group(2, arr, None) == MLA_ERR_INVALID_ARG
     assert lib.mla_last_error().decode().startswith("call 1:")
     assert lib.mla_fwd_group(0, None, None) == MLA_OK
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(flags=9), MLA_ERR_INVALID_ARG, "needs seq_lens"),
+    (dict(flags=9, seq_lens=FAKE, n_seqs=3, B=2), MLA_ERR_INVALID_ARG, "n_seqs == B"),
+    (dict(flags=9, seq_lens=FAKE + 2, n_seqs=1), MLA_ERR_INVALID_ARG, "aligned"),
+])
+def test_fwd_valid_lens_rejects(lib, kw, code, msg):
+    assert call_fwd(lib, **kw) == code
+    assert msg in lib.mla_last_error().decode()
+
+
+def test_fwd_valid_lens_split_form_unsupported(lib):
+    r = rows(sb=0, sh=128, st=32 * 128)
+    st = call_fwd(lib, q=r, kv=r, v=r, q_rope=r, k_rope=r, dq=128, dr=64, dv=128, Hq=32, Hkv=32, flags=9,
+                  seq_lens=FAKE, n_seqs=1, out=r)
+    assert st == MLA_ERR_UNSUPPORTED

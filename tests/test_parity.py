@@ -573,3 +573,30 @@ def test_split_workspace_bit_identical(mla):
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("B,H,N,lens,seed", [
+    (3, 8, 300, [300, 77, 0], 86),         # full, ragged tail inside a row block, empty
+    (2, 128, 1100, [1037, 5000], 87),      # 128 heads; a length past N clamps to N
+])
+def test_dense_valid_lens_padded_batch(mla, B, H, N, lens, seed):
+    """Padded batch with per-batch valid lengths (MLA_VALID_LENS): batch b
+    equals the oracle on its first lens[b] rows; rows past it are untouched.
+    Value columns are halved (exact) so that |O| < 2: over 128 heads x 1037
+    rows, a few rows that see only a few keys reach |O| > 2 otherwise, where
+    the bf16 output's half ulp (2^-7) alone takes most of the 1e-2 bound."""
+    c = W.dense_case(B=B, H=H, N=N, seed=seed)
+    c.kv = _times_pow2(c.kv, 0.5, slice(0, 512))
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    out = torch.full((B, H, N, 512), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), 7.0, dtype=torch.float32, device="cuda")
+    mla.fwd(q, kv, scale=c.scale, out=out, lse=lse, valid_lens=dev(np.array(lens, dtype=np.int32)))
+    torch.cuda.synchronize()
+    o, l = host(out), host(lse)
+    for b, n in enumerate(lens):
+        n = min(n, N)
+        if n:
+            o_ref, l_ref = oracle.dense_mla(c.q[b:b + 1, :, :n], c.kv[b:b + 1, :, :n], 512, c.scale)
+            assert report(f"b{b} O", o[b:b + 1, :, :n], o_ref) <= O_TOL
+            assert report(f"b{b} LSE", l[b:b + 1, :, :n], l_ref) <= LSE_TOL
+        assert np.all(o[b, :, n:] == 7.0) and np.all(l[b, :, n:] == 7.0)
