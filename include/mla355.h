@@ -226,12 +226,19 @@ mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a,
  * the page's row-major h*L + l order); lse [B, S, H] fp32 (view with t =
  * query, h = head) or NULL.  L == 512, R == 64, H <= 128, 1 <= K <= 4096
  * (larger K returns MLA_ERR_UNSUPPORTED).
+ *
+ * flags: 0 or MLA_OUT_MX4.  With MLA_OUT_MX4 each head's L latent columns
+ * are written in MX 4-pack order (NKI mla_sparse_attention_cte_kernel,
+ * "Returns" and "Notes": the layout its o_proj load expects): natural column
+ * l = 4 * group + sub is stored at sub * (L / 4) + group.  Other bits return
+ * MLA_ERR_INVALID_ARG.
  */
+#define MLA_OUT_MX4 1u
 mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe,
                           const mla_rows* c_kv, const mla_rows* k_pe,
                           const int32_t* topk_idx,
                           int32_t B, int64_t S, int64_t S_kv, int32_t H,
-                          int32_t L, int32_t R, int32_t K, float scale,
+                          int32_t L, int32_t R, int32_t K, float scale, uint32_t flags,
                           const mla_rows* out, const mla_rows* lse,
                           void* workspace, size_t workspace_bytes,
                           void* stream /* hipStream_t */);

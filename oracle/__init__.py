@@ -37,6 +37,8 @@ Functions and the passages they follow:
 * :func:`sparse_mla`  -- per-query attention over the top-k listed latent
   cache rows (NKI ``mla_sparse_attention_cte_kernel``, "Parameters" and
   "Returns").
+* :func:`mx4_pack`    -- the MX 4-pack column order of the sparse output
+  (NKI ``mla_sparse_attention_cte_kernel``, "Returns" and "Notes").
 * :func:`decode_mla`  -- token generation: each sequence's newest query over
   its valid cache rows (Mojo ``mha_single_batch_pipelined``: seq_len = 1,
   ``num_keys``; split-K with a separate reduction).
@@ -45,8 +47,8 @@ Every function is pinned by ``tests/test_oracle.py`` against brute force on
 tiny inputs, ``torch.nn.functional.scaled_dot_product_attention`` in float64,
 closed forms, hand-worked values and the chunking invariants.
 """
-from .mla_ref import (attention, decode_mla, dense_mla, merge, ring, ring_order, split_mla,
+from .mla_ref import (attention, decode_mla, dense_mla, merge, mx4_pack, ring, ring_order, split_mla,
                       sparse_mla)
 
-__all__ = ["attention", "decode_mla", "dense_mla", "merge", "ring", "ring_order", "split_mla",
+__all__ = ["attention", "decode_mla", "dense_mla", "merge", "mx4_pack", "ring", "ring_order", "split_mla",
            "sparse_mla"]

@@ -243,6 +243,25 @@ def sparse_mla(q_lift, q_pe, c_kv, k_pe, idx, scale: float,
     return out, lse
 
 
+def mx4_pack(out: np.ndarray, L: int) -> np.ndarray:
+    """Sparse output [..., H*L] in natural column order -> the same values
+    with each head's L columns in MX 4-pack order (NKI
+    ``mla_sparse_attention_cte_kernel``, "Returns" and "Notes"): the value of
+    natural latent column l = 4*group + sub lands at column sub*(L//4) + group
+    of its head.  Written as the scatter the pages state, one column at a time.
+    """
+    if L % 4:
+        raise ValueError("L must be a multiple of 4")
+    lead = out.shape[:-1]
+    H = out.shape[-1] // L
+    nat = out.reshape(*lead, H, L)
+    phys = np.empty_like(nat)
+    for l in range(L):
+        group, sub = divmod(l, 4)
+        phys[..., sub * (L // 4) + group] = nat[..., l]
+    return phys.reshape(out.shape)
+
+
 # ---------------------------------------------------------------------------
 # token generation: one new query per sequence over its valid cache rows
 # ---------------------------------------------------------------------------

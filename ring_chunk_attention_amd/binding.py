@@ -21,6 +21,7 @@ MLA_CAUSAL = 1
 MLA_OUT_F32 = 2
 MLA_PREV_OUT_F32 = 4
 MLA_VALID_LENS = 8
+MLA_OUT_MX4 = 1  # mla_sparse_fwd
 
 
 class MlaRows(ctypes.Structure):
@@ -70,7 +71,7 @@ def _load():
     lib.mla_sparse_fwd.restype = ctypes.c_int
     lib.mla_sparse_fwd.argtypes = [_P, _P, _P, _P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                   ctypes.c_int32, ctypes.c_float, _P, _P, ctypes.c_void_p,
+                                   ctypes.c_int32, ctypes.c_float, ctypes.c_uint32, _P, _P, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_debug_gather.restype = ctypes.c_int
     lib.mla_debug_gather.argtypes = [_P, _P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
@@ -353,12 +354,12 @@ def merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: 
 
 def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_pe: torch.Tensor,
                topk_idx: torch.Tensor, *, scale: float, out: Optional[torch.Tensor] = None,
-               lse: Optional[torch.Tensor] = None, want_lse: bool = True, workspace="auto"
-               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True, workspace="auto",
+               mx4: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Top-k sparse latent attention (mla_sparse_fwd): q_lift [B,S,H,L],
     q_pe [B,S,H,R], c_kv [B,S_kv,L], k_pe [B,S_kv,R], topk_idx int32
     [B,S,K] -> out [B, S, H*L] bf16 and lse [B, S, H] fp32.  ``workspace`` as
-    for fwd."""
+    for fwd.  ``mx4``: each head's columns in MX 4-pack order (MLA_OUT_MX4)."""
     B, S, H, L = q_lift.shape
     R = q_pe.shape[3]
     S_kv = c_kv.shape[1]
@@ -392,7 +393,7 @@ def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
         v_l = MlaRows(lse.data_ptr(), lse.stride(0), lse.stride(2), lse.stride(1))
     _check(LIB.mla_sparse_fwd(ctypes.byref(v_ql), ctypes.byref(v_qp), ctypes.byref(v_ck),
                               ctypes.byref(v_kp), topk_idx.data_ptr(), B, S, S_kv, H, L, R, K,
-                              float(scale), ctypes.byref(v_o), _ref(v_l),
+                              float(scale), MLA_OUT_MX4 if mx4 else 0, ctypes.byref(v_o), _ref(v_l),
                               *_workspace(q_lift.device, workspace), _stream(q_lift.device)))
     return out, lse
 

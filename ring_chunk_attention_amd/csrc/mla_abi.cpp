@@ -358,7 +358,7 @@ mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a, const mla
 mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const mla_rows* c_kv,
                           const mla_rows* k_pe, const int32_t* topk_idx, int32_t B, int64_t S,
                           int64_t S_kv, int32_t H, int32_t L, int32_t R, int32_t K, float scale,
-                          const mla_rows* out, const mla_rows* lse, void* workspace,
+                          uint32_t flags, const mla_rows* out, const mla_rows* lse, void* workspace,
                           size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   mla_status st;
@@ -369,6 +369,7 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
   if (K > mla::kSparseMaxTopk)
     return fail(MLA_ERR_UNSUPPORTED, "sparse kernel handles up to %d indices per query (got %d)", mla::kSparseMaxTopk, K);
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+  if (flags & ~MLA_OUT_MX4) return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~MLA_OUT_MX4);
   if ((st = check_workspace(workspace, workspace_bytes))) return st;
   if ((st = check_rows(q_lift, "q_lift")) || (st = check_rows(q_pe, "q_pe")) || (st = check_rows(out, "out")))
     return st;
@@ -395,6 +396,7 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
   p.Nkv = S_kv;
   p.topk = K;
   p.scale_log2 = scale * kLog2e;
+  p.mx4 = (flags & MLA_OUT_MX4) ? 1 : 0;
   p.queue = static_cast<unsigned*>(workspace);
   if (S == 0 || B == 0) return MLA_OK;
   return hip_status(mla::launch_latent_sparse(p, static_cast<hipStream_t>(stream)), "sparse attention launch");

@@ -59,6 +59,7 @@ struct AttnParams {
   int32_t causal;
   int32_t out_f32;          // out holds float32 (else bf16)
   int32_t prev_f32;         // prev_out holds float32 (else bf16)
+  int32_t mx4;              // sparse: each head's latent columns in MX 4-pack order
   int32_t n_qblk, n_hgrp;   // grid factors (see each launcher)
   unsigned* queue;          // item queue's counter, or nullptr
   // token generation (sparse kernel): each item's list is the range

@@ -123,13 +123,13 @@ def test_sparse_rejects_unsupported_dims(lib):
     from ring_chunk_attention_amd.binding import MlaRows
     r = MlaRows(FAKE, 0, 512, 512)
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
-                            1, 16, 1024, 128, 256, 64, 128, 0.07, ctypes.byref(r), None, None, 0, None)
+                            1, 16, 1024, 128, 256, 64, 128, 0.07, 0, ctypes.byref(r), None, None, 0, None)
     assert st == MLA_ERR_UNSUPPORTED
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
-                            1, 16, 1024, 256, 512, 64, 128, 0.07, ctypes.byref(r), None, None, 0, None)
+                            1, 16, 1024, 256, 512, 64, 128, 0.07, 0, ctypes.byref(r), None, None, 0, None)
     assert st == MLA_ERR_UNSUPPORTED
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
-                            1, 16, 1024, 128, 512, 64, 4097, 0.07, ctypes.byref(r), None, None, 0, None)
+                            1, 16, 1024, 128, 512, 64, 4097, 0.07, 0, ctypes.byref(r), None, None, 0, None)
     assert st == MLA_ERR_UNSUPPORTED and "4096" in lib.mla_last_error().decode()
 
 
@@ -137,7 +137,7 @@ def test_sparse_rejects_short_workspace(lib):
     from ring_chunk_attention_amd.binding import MlaRows
     r = MlaRows(FAKE, 0, 512, 512)
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
-                            1, 16, 1024, 128, 512, 64, 128, 0.07, ctypes.byref(r), None, FAKE, 16, None)
+                            1, 16, 1024, 128, 512, 64, 128, 0.07, 0, ctypes.byref(r), None, FAKE, 16, None)
     assert st == MLA_ERR_INVALID_ARG and "workspace" in lib.mla_last_error().decode()
 
 
@@ -226,3 +226,11 @@ def test_fwd_valid_lens_split_form_unsupported(lib):
     st = call_fwd(lib, q=r, kv=r, v=r, q_rope=r, k_rope=r, dq=128, dr=64, dv=128, Hq=32, Hkv=32, flags=9,
                   seq_lens=FAKE, n_seqs=1, out=r)
     assert st == MLA_ERR_UNSUPPORTED
+
+
+def test_sparse_rejects_unknown_flags(lib):
+    from ring_chunk_attention_amd.binding import MlaRows
+    r = MlaRows(FAKE, 0, 512, 512)
+    st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
+                            1, 16, 1024, 128, 512, 64, 128, 0.07, 2, ctypes.byref(r), None, None, 0, None)
+    assert st == MLA_ERR_INVALID_ARG and "flag" in lib.mla_last_error().decode()

@@ -419,6 +419,28 @@ def test_split_default_draw_lengths():
     assert int(lens.sum()) == 27610
 
 
+def test_mx4_pack_hand_worked():
+    """The MX 4-pack column order on the hand-worked L = 8, H = 2 example."""
+    g = json.load(open(GOLDEN))["mx4"]
+    got = oracle.mx4_pack(np.array(g["natural"], dtype=np.float64)[None], g["L"])
+    np.testing.assert_array_equal(got[0], np.array(g["physical"], dtype=np.float64))
+
+
+def test_mx4_pack_is_a_per_head_permutation():
+    """At L = 512: every head's columns are a permutation of its own columns,
+    natural column 4g + s sits at s*128 + g, and the four subs of a group land
+    in the four quarters of the head."""
+    H, L = 3, 512
+    nat = np.arange(H * L, dtype=np.float64).reshape(1, 1, H * L)
+    phys = oracle.mx4_pack(nat, L).reshape(H, L)
+    for h in range(H):
+        assert sorted(phys[h]) == list(range(h * L, (h + 1) * L))
+    l = np.arange(L)
+    np.testing.assert_array_equal(phys[:, (l % 4) * (L // 4) + l // 4], nat.reshape(H, L))
+    np.testing.assert_array_equal(phys[0, :4], [0, 4, 8, 12])
+    np.testing.assert_array_equal(phys[0, 128:132], [1, 5, 9, 13])
+
+
 # ---------------------------------------------------------------------------
 # weight absorption: latent form == per-head form
 # ---------------------------------------------------------------------------

@@ -283,6 +283,26 @@ def test_sparse_small(mla, H, K, seed):
     assert report("sparse LSE", host(lse), l_ref) <= LSE_TOL
 
 
+def test_sparse_mx4_output_order(mla):
+    """MLA_OUT_MX4: the kernel's output equals the oracle's natural-order
+    result put through the MX 4-pack permutation, and the natural-order call
+    permuted the same way is bit-identical to it."""
+    c = W.sparse_case(S=24, S_kv=3000, pos0=2900, H=128, K=700, seed=88)
+    args = [dev_bf16(x) for x in (c.q_lift, c.q_pe, c.c_kv, c.k_pe)] + [dev(c.idx)]
+    o_mx, l_mx = mla.sparse_fwd(*args, scale=c.scale, mx4=True)
+    o_nat, l_nat = mla.sparse_fwd(*args, scale=c.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale)
+    assert report("mx4 O", host(o_mx), oracle.mx4_pack(o_ref, 512)) <= O_TOL
+    assert report("mx4 LSE", host(l_mx), l_ref) <= LSE_TOL
+    perm = oracle.mx4_pack(np.arange(512, dtype=np.float64), 512).astype(np.int64)
+    nat = o_nat.view(torch.int16).view(1, 24, 128, 512).cpu().numpy()
+    want = np.empty_like(nat)
+    want[..., np.arange(512)] = nat[..., perm]
+    assert np.array_equal(o_mx.view(torch.int16).view(1, 24, 128, 512).cpu().numpy(), want)
+    assert torch.equal(l_mx, l_nat)
+
+
 def test_sparse_duplicates_and_invalid_indices(mla):
     c = W.sparse_case(S=8, S_kv=500, pos0=300, H=128, K=64, seed=43)
     idx = c.idx.copy()
