@@ -39,6 +39,9 @@ Functions and the passages they follow:
   "Returns").
 * :func:`mx4_pack`    -- the MX 4-pack column order of the sparse output
   (NKI ``mla_sparse_attention_cte_kernel``, "Returns" and "Notes").
+* :func:`vup`         -- the V-up projection of the latent output by the
+  per-head ``v_b_proj`` weight (TensorRT-LLM ``mla.py``,
+  ``forward_absorption_context`` and ``forward_absorption_generation``).
 * :func:`decode_mla`  -- token generation: each sequence's newest query over
   its valid cache rows (Mojo ``mha_single_batch_pipelined``: seq_len = 1,
   ``num_keys``; split-K with a separate reduction).
@@ -48,7 +51,7 @@ tiny inputs, ``torch.nn.functional.scaled_dot_product_attention`` in float64,
 closed forms, hand-worked values and the chunking invariants.
 """
 from .mla_ref import (attention, decode_mla, dense_mla, merge, mx4_pack, ring, ring_order, split_mla,
-                      sparse_mla)
+                      sparse_mla, vup)
 
 __all__ = ["attention", "decode_mla", "dense_mla", "merge", "mx4_pack", "ring", "ring_order", "split_mla",
-           "sparse_mla"]
+           "sparse_mla", "vup"]

@@ -263,6 +263,29 @@ def mx4_pack(out: np.ndarray, L: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# V-up projection of the latent output
+# ---------------------------------------------------------------------------
+def vup(o: np.ndarray, w_uv: np.ndarray, mx4: bool = False) -> np.ndarray:
+    """o [B, H, T, L], w_uv [H, dvh, L] -> [B, H, T, dvh] with
+    out[b, h, t, c] = sum_l o[b, h, t, l] * w_uv[h, c, l] (TensorRT-LLM
+    ``mla.py``, ``forward_absorption_context``: the per-head product of the
+    latent attention output [heads, tokens, kv_lora_rank] with ``v_b_proj``
+    transposed).  ``mx4``: o's columns are in MX 4-pack order (see
+    :func:`mx4_pack`); they are put back in natural order first.
+    """
+    o = _f64(o)
+    L = o.shape[-1]
+    if mx4:
+        l = np.arange(L)
+        o = o[..., (l % 4) * (L // 4) + l // 4]
+    w = _f64(w_uv)
+    out = np.empty(o.shape[:-1] + (w.shape[1],))
+    for h in range(o.shape[1]):
+        out[:, h] = o[:, h] @ w[h].T
+    return out
+
+
+# ---------------------------------------------------------------------------
 # token generation: one new query per sequence over its valid cache rows
 # ---------------------------------------------------------------------------
 def decode_mla(q: np.ndarray, kv: np.ndarray, kv_lens: Optional[Sequence[int]],

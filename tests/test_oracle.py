@@ -460,13 +460,51 @@ def test_absorbed_equals_non_absorbed():
     q_abs = np.concatenate([q_lift, q_pe.transpose(1, 0, 2)], -1)[None]
     kv = np.concatenate([c_kv, k_pe], -1)[None, None]
     o_lat, l_lat = oracle.dense_mla(q_abs, kv, L, scale)
-    o_abs = np.einsum("hnl,hvl->nhv", o_lat[0], w_uv)
+    o_abs = oracle.vup(o_lat, w_uv)[0].transpose(1, 0, 2)
     k_nope = np.einsum("nl,hdl->nhd", c_kv, w_uk)
     v = np.einsum("nl,hvl->nhv", c_kv, w_uv)
     k_pe_h = np.repeat(k_pe[:, None, :], H, axis=1)
     o_per, l_per = oracle.split_mla(q_nope, q_pe, k_nope, k_pe_h, v, [N], scale)
     np.testing.assert_allclose(o_abs, o_per, atol=1e-10)
     np.testing.assert_allclose(l_lat[0], l_per, atol=1e-10)
+
+
+def test_vup_brute_force():
+    """V-up with Python loops over every (b, h, t, c) on a tiny case."""
+    rng = np.random.default_rng(18)
+    B, H, T, L, dvh = 2, 3, 4, 8, 5
+    o = _rand(rng, B, H, T, L); w = _rand(rng, H, dvh, L)
+    got = oracle.vup(o, w)
+    for b, h, t, c in itertools.product(range(B), range(H), range(T), range(dvh)):
+        want = sum(float(o[b, h, t, l]) * float(w[h, c, l]) for l in range(L))
+        assert abs(got[b, h, t, c] - want) < 1e-12
+
+
+def test_vup_commutes_with_merge():
+    """Folding two partial results and then projecting equals projecting each
+    and folding with the same LSE weights (TensorRT-LLM mla.py,
+    _helix_project_v_partials: the combine is a per-head weighted sum, so it
+    commutes with the per-head V projection)."""
+    rng = np.random.default_rng(19)
+    B, H, T, L, dvh = 1, 3, 5, 16, 4
+    oa, ob = _rand(rng, B, H, T, L), _rand(rng, B, H, T, L)
+    la, lb = _rand(rng, B, H, T), _rand(rng, B, H, T)
+    la[0, 1, 2] = -np.inf
+    w = _rand(rng, H, dvh, L)
+    o_m, l_m = oracle.merge(oa, la, ob, lb)
+    p_m, l_p = oracle.merge(oracle.vup(oa, w), la, oracle.vup(ob, w), lb)
+    np.testing.assert_allclose(oracle.vup(o_m, w), p_m, atol=1e-12)
+    np.testing.assert_array_equal(l_m, l_p)
+
+
+def test_vup_mx4_input_equals_natural():
+    """V-up of an MX 4-pack ordered input (mx4=True) equals V-up of the
+    natural-order input, and treating the packed input as natural does not."""
+    rng = np.random.default_rng(20)
+    o = _rand(rng, 1, 2, 3, 16); w = _rand(rng, 2, 4, 16)
+    packed = oracle.mx4_pack(o, 16)
+    np.testing.assert_allclose(oracle.vup(packed, w, mx4=True), oracle.vup(o, w), atol=1e-12)
+    assert np.abs(oracle.vup(packed, w) - oracle.vup(o, w)).max() > 1e-3
 
 
 # ---------------------------------------------------------------------------

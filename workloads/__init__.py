@@ -18,7 +18,12 @@ the workload lists its tensors.  The shapes follow the pages:
   member table of ``AtbRingMLAGetWorkspaceSize``);
 * the sparse top-k latent path with ``q_lift``, ``q_pe``, ``c_kv``, ``k_pe``
   and flat int32 indices (NKI ``mla_sparse_attention_cte_kernel``,
-  "Parameters").
+  "Parameters");
+* the V-up projection after latent attention, with a synthetic weight
+  ``w_uv`` [H, 128, 512] (TensorRT-LLM ``mla.py``, ``v_b_proj``): there are no
+  trained weights here, so it is drawn N(0,1) and divided by sqrt(512) before
+  the bf16 rounding, which keeps the projected values at the scale of the
+  latent output.
 """
 from __future__ import annotations
 
@@ -215,6 +220,25 @@ def split_ring_step(seed: int = 0) -> SplitCase:
 
 def sparse_topk(seed: int = 0) -> SparseCase:
     return sparse_case(seed=seed, name="sparse top-k MLA S=4096 S_kv=16384 H=128 K=2048")
+
+
+@dataclass
+class VupCase:
+    o: np.ndarray      # [B, H, T, L] latent attention output (bf16 bits)
+    w_uv: np.ndarray   # [H, dvh, L] (bf16 bits)
+    name: str = ""
+
+
+def vup_case(B: int = 1, H: int = 4, T: int = 64, L: int = 512, dvh: int = 128, seed: int = 0,
+             name: str = "") -> VupCase:
+    rng = np.random.default_rng(seed)
+    o = normal_bf16(rng, (B, H, T, L))
+    w = to_bf16_bits(rng.standard_normal((H, dvh, L), dtype=np.float32) / np.float32(math.sqrt(L)))
+    return VupCase(o, w, name)
+
+
+def dsv3_vup(seed: int = 0) -> VupCase:
+    return vup_case(B=1, H=128, T=8192, seed=seed, name="DeepSeek-V3 V-up projection H=128 T=8192")
 
 
 def dsv3_decode(seed: int = 0) -> DecodeCase:
