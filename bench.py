@@ -12,7 +12,7 @@ Rank 0 prints ONE JSON line with the headline, its roofline against the
 dense bf16 MFMA peak, the fp64 CPU oracle timed on a bounded sample of the
 same workload, and measured lines for the other steps of the path (one-device
 ring with LSE folds, split varlen ring step, sparse top-k, standalone merge,
-token-generation decode).
+token-generation decode, V-up projection).
 """
 from __future__ import annotations
 
@@ -391,6 +391,22 @@ def measure_rows(mla, W, to_dev, steps, warmup):
     rows["decode_b64_kv8192_h128"] = {
         "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
         "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+        "GBps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+        "bytes": nbytes}
+    del q, kv, lens, do, dl
+
+    # V-up projection of a prefill's latent output: [1, 128, 8192, 512] x
+    # per-head [128, 512] weights -> [8192, 128 * 128]; HBM-bound
+    print("bench: V-up workload", file=sys.stderr, flush=True)
+    c = W.dsv3_vup(0)
+    o, w = to_dev(c.o), to_dev(c.w_uv)
+    B, H, T, L = c.o.shape
+    vo = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
+    ms, _, _ = time_launches(lambda: mla.vup(o, w, out=vo), steps, warmup)
+    fl = B * H * T * L * 128 * 2
+    nbytes = o.numel() * 2 + w.numel() * 2 + vo.numel() * 2   # each operand once
+    rows["vup_h128_t8192"] = {
+        "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
         "GBps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
         "bytes": nbytes}
     return rows

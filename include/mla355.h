@@ -299,6 +299,31 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope,
 size_t mla_decode_workspace_size(int32_t B, int32_t H, int64_t Nkv, int32_t n_splits);
 
 /*
+ * mla_vup -- V-up projection of the latent attention output (TensorRT-LLM
+ * mla.py, forward_absorption_context and forward_absorption_generation: the
+ * per-head product [heads, tokens, kv_lora_rank] x [heads, kv_lora_rank,
+ * v_head_dim] after latent attention, which yields o_proj's input):
+ *
+ *   out[b, h, t, c] = sum_l o[b, h, t, l] * w_uv[h, c, l],  l < L, c < dvh
+ *
+ * o: bf16 rows view [B, H, T, L] (mla_fwd's out as it is; mla_sparse_fwd's
+ * out [B, S, H*L] as stride_b, stride_h = L, stride_t = H*L; mla_decode_fwd's
+ * out [B, H, dv] with T = 1).  w_uv: device bf16 [H, dvh, L] contiguous, 16-byte
+ * aligned (the page's v_b_proj layout [heads, v_head_dim, kv_lora_rank]).
+ * out: bf16 rows view [B, H, T, dvh] (for o_proj's [tokens, H*dvh] input:
+ * stride_h = dvh, stride_t = H*dvh).  fp32 accumulation, out rounded to bf16
+ * (round to nearest even).  L == 512 and dvh == 128 (else
+ * MLA_ERR_UNSUPPORTED); out must not overlap o or w_uv.
+ *
+ * flags: 0 or MLA_OUT_MX4 -- o's columns of each head are in MX 4-pack order
+ * (as mla_sparse_fwd writes them with that flag); the result is the same
+ * projection of the natural-order values.  Other bits: MLA_ERR_INVALID_ARG.
+ */
+mla_status mla_vup(const mla_rows* o, const void* w_uv, int32_t B, int32_t H, int64_t T,
+                   int32_t L, int32_t dvh, uint32_t flags, const mla_rows* out,
+                   void* stream /* hipStream_t */);
+
+/*
  * mla_debug_gather -- test export.  Gathers the top-k rows of one query's
  * index list through the same device tile loader mla_sparse_fwd uses (with
  * its LDS swizzle undone on the way out): rows_out [K, L + R] bf16 contiguous,

@@ -89,6 +89,9 @@ def _load():
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_vup.restype = ctypes.c_int
+    lib.mla_vup.argtypes = [_P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                            ctypes.c_int32, ctypes.c_uint32, _P, ctypes.c_void_p]
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
     lib.mla_decode_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                               ctypes.c_int32]
@@ -98,8 +101,8 @@ def _load():
 LIB = _load()
 LIB_PATH = _LIB_PATH
 
-EXPORTS = ("mla_fwd", "mla_fwd_group", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd", "mla_debug_gather",
-           "mla_last_error", "mla_version", "mla_workspace_size", "mla_decode_workspace_size")
+EXPORTS = ("mla_fwd", "mla_fwd_group", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd", "mla_vup",
+           "mla_debug_gather", "mla_last_error", "mla_version", "mla_workspace_size", "mla_decode_workspace_size")
 
 
 class MlaError(RuntimeError):
@@ -396,6 +399,29 @@ def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
                               float(scale), MLA_OUT_MX4 if mx4 else 0, ctypes.byref(v_o), _ref(v_l),
                               *_workspace(q_lift.device, workspace), _stream(q_lift.device)))
     return out, lse
+
+
+def vup(o: torch.Tensor, w_uv: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+        mx4: bool = False) -> torch.Tensor:
+    """V-up projection of the latent attention output (mla_vup): o is a
+    [B, H, T, 512] bf16 view (fwd's out; sparse_fwd's out as
+    ``out.view(B, S, H, 512).transpose(1, 2)``; decode_fwd's out as
+    ``out.unsqueeze(2)``), w_uv bf16 [H, 128, 512] contiguous.  Returns out
+    [B, T, H, 128] bf16 (o_proj's input row per token), or writes the given
+    ``out`` of that shape.  ``mx4``: o's columns are in MX 4-pack order."""
+    B, H, T, L = o.shape
+    _need(w_uv, "w_uv", torch.bfloat16)
+    if w_uv.dim() != 3 or w_uv.shape[0] != H or w_uv.shape[2] != L or not w_uv.is_contiguous():
+        raise ValueError("w_uv: expected a contiguous [H, dvh, L] tensor")
+    dvh = w_uv.shape[1]
+    if out is None:
+        out = torch.empty((B, T, H, dvh), dtype=torch.bfloat16, device=o.device)
+    if out.shape != (B, T, H, dvh):
+        raise ValueError("out: expected [B, T, H, dvh]")
+    vo = _rows_bhtd(out.transpose(1, 2), "out")
+    _check(LIB.mla_vup(ctypes.byref(_rows_bhtd(o, "o")), w_uv.data_ptr(), B, H, T, L, dvh,
+                       MLA_OUT_MX4 if mx4 else 0, ctypes.byref(vo), _stream(o.device)))
+    return out
 
 
 # Decode workspaces, one per (device, stream), grown to the largest call.

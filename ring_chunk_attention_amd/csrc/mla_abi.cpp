@@ -507,6 +507,28 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_r
   return hip_status(mla::launch_combine(c, s), "decode combine launch");
 }
 
+mla_status mla_vup(const mla_rows* o, const void* w_uv, int32_t B, int32_t H, int64_t T, int32_t L, int32_t dvh,
+                   uint32_t flags, const mla_rows* out, void* stream) {
+  g_last_error.clear();
+  mla_status st;
+  if (B < 0 || H <= 0 || T < 0) return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, H > 0, T >= 0");
+  if (L != 512 || dvh != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "V-up is built for L = 512, dvh = 128 (got %d, %d)", L, dvh);
+  if (flags & ~MLA_OUT_MX4) return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~MLA_OUT_MX4);
+  if ((st = check_rows(o, "o")) || (st = check_rows(out, "out"))) return st;
+  if (!w_uv || !aligned16(w_uv)) return fail(MLA_ERR_INVALID_ARG, "w_uv: missing or not 16-byte aligned");
+  if ((int64_t)H * 512 > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "too many heads for one launch");
+  mla::VupParams p{};
+  p.o = rc(o);
+  p.w = static_cast<const uint16_t*>(w_uv);
+  p.out = rm(out);
+  p.B = B;
+  p.H = H;
+  p.T = T;
+  p.mx4 = (flags & MLA_OUT_MX4) ? 1 : 0;
+  return hip_status(mla::launch_vup(p, static_cast<hipStream_t>(stream)), "V-up launch");
+}
+
 mla_status mla_debug_gather(const mla_rows* c_kv, const mla_rows* k_pe, const int32_t* idx, int32_t b,
                             int64_t S_kv, int32_t L, int32_t R, int32_t K, uint16_t* rows_out,
                             void* stream) {

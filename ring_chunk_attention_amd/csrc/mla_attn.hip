@@ -356,19 +356,6 @@ void debug_gather_kernel(const GatherParams p) {
 
 __global__ void queue_reset_kernel(unsigned* q) { q[0] = 0u; }
 
-// Compute units of the current device, cached per device (0 if unknown).
-int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 // One workgroup per item of a latent or sparse kernel (each fills a CU's
 // LDS).  The item queue pays off only when the items outnumber the CUs
 // several times over (a launch that fits the chip at once has no tail to
@@ -383,6 +370,19 @@ hipError_t launch_items(AttnParams p, int64_t items, hipStream_t s) {
 }
 
 }  // namespace
+
+// Compute units of the current device, cached per device.
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 hipError_t launch_latent_dense(const AttnParams& p, hipStream_t s) {
   const int64_t items = (int64_t)p.n_qblk * p.n_hgrp * p.B;

@@ -103,6 +103,18 @@ struct MergeParams {
   int32_t dv;
 };
 
+// V-up projection: out[b, h, t, c] = sum_l o[b, h, t, l] * w[h, c, l]
+// (l < 512, c < 128; w contiguous [H, 128, 512]).
+struct VupParams {
+  RowsC o;
+  const uint16_t* w;
+  RowsM out;
+  int32_t B, H;
+  int64_t T;
+  int32_t mx4;              // o's columns in MX 4-pack order
+  int64_t blocks_per_part;  // set by the launcher
+};
+
 struct GatherParams {
   RowsC ka, kb;
   const int32_t* idx;
@@ -120,5 +132,9 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, int64_t items, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_debug_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_vup(const VupParams& p, hipStream_t s);
+
+// Compute units of the current device, cached per device (0 if unknown).
+int cu_count();
 
 }  // namespace mla

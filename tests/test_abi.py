@@ -234,3 +234,21 @@ def test_sparse_rejects_unknown_flags(lib):
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
                             1, 16, 1024, 128, 512, 64, 128, 0.07, 2, ctypes.byref(r), None, None, 0, None)
     assert st == MLA_ERR_INVALID_ARG and "flag" in lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    (dict(L=256), MLA_ERR_UNSUPPORTED, "L = 512"),
+    (dict(dvh=64), MLA_ERR_UNSUPPORTED, "dvh = 128"),
+    (dict(flags=2), MLA_ERR_INVALID_ARG, "flag"),
+    (dict(H=0), MLA_ERR_INVALID_ARG, "sizes"),
+    (dict(w=FAKE + 8), MLA_ERR_INVALID_ARG, "w_uv"),
+    (dict(w=None), MLA_ERR_INVALID_ARG, "w_uv"),
+])
+def test_vup_rejects(lib, args, code, msg):
+    from ring_chunk_attention_amd.binding import MlaRows
+    a = dict(B=1, H=4, T=64, L=512, dvh=128, flags=0, w=FAKE)
+    a.update(args)
+    r = MlaRows(FAKE, 0, 512, 512)
+    st = lib.mla_vup(ctypes.byref(r), a["w"], a["B"], a["H"], a["T"], a["L"], a["dvh"], a["flags"],
+                     ctypes.byref(r), None)
+    assert st == code and msg in lib.mla_last_error().decode()

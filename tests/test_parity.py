@@ -620,3 +620,55 @@ def test_dense_valid_lens_padded_batch(mla, B, H, N, lens, seed):
             assert report(f"b{b} O", o[b:b + 1, :, :n], o_ref) <= O_TOL
             assert report(f"b{b} LSE", l[b:b + 1, :, :n], l_ref) <= LSE_TOL
         assert np.all(o[b, :, n:] == 7.0) and np.all(l[b, :, n:] == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# V-up projection
+# ---------------------------------------------------------------------------
+def _vup_ok(name, got, ref):
+    """Element-wise bound: the bf16 rounding of the result (at most 2^-8 of
+    its magnitude) plus the fp32 accumulation over 512 products (at most
+    512 * 2^-24 * sum |o w|, below 1e-3 for these inputs, where sum |o w| is
+    about 512 * 0.8 * 0.035)."""
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-3
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    print(f"{name}: max err {err.max():.3e}, worst vs bound {err[worst]:.3e} <= {bound[worst]:.3e} at {worst}")
+    return bool(np.all(err <= bound))
+
+
+@pytest.mark.parametrize("B,H,T,seed", [(2, 5, 77, 90), (3, 128, 1, 91), (1, 16, 300, 92)])
+def test_vup_small(mla, B, H, T, seed):
+    """Every element; ragged row blocks, rows of several batches in one block
+    (T = 1, the decode shape)."""
+    c = W.vup_case(B=B, H=H, T=T, seed=seed)
+    out = mla.vup(dev_bf16(c.o), dev_bf16(c.w_uv))
+    torch.cuda.synchronize()
+    ref = oracle.vup(c.o, c.w_uv)
+    assert _vup_ok("vup", host(out).transpose(0, 2, 1, 3), ref)
+
+
+def test_vup_sparse_layout_mx4(mla):
+    """Input in the sparse output's [B, S, H*L] layout with MX 4-pack
+    columns (a strided view), result equal to the natural projection."""
+    c = W.vup_case(B=1, H=128, T=40, seed=93)
+    packed = oracle.mx4_pack(W.bf16_bits_to_f32(c.o), 512)            # exact: a permutation
+    flat = np.ascontiguousarray(packed.transpose(0, 2, 1, 3)).reshape(1, 40, 128 * 512)
+    o = torch.from_numpy(flat).cuda().to(torch.bfloat16)
+    out = mla.vup(o.view(1, 40, 128, 512).transpose(1, 2), dev_bf16(c.w_uv), mx4=True)
+    torch.cuda.synchronize()
+    assert _vup_ok("vup mx4", host(out).transpose(0, 2, 1, 3), oracle.vup(c.o, c.w_uv))
+
+
+def test_vup_config_sampled(mla):
+    """The V-up workload the benchmark times (H = 128, T = 8192): sampled
+    rows against the oracle, row by row."""
+    c = W.dsv3_vup(0)
+    out = mla.vup(dev_bf16(c.o), dev_bf16(c.w_uv))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(94)
+    hs = rng.integers(0, 128, 48)
+    ts = np.concatenate([rng.integers(0, 8192, 46), [0, 8191]])
+    got = out[0, torch.from_numpy(ts), torch.from_numpy(hs)].float().cpu().numpy().astype(np.float64)
+    ref = np.stack([oracle.vup(c.o[:, h:h + 1, t:t + 1], c.w_uv[h:h + 1])[0, 0, 0] for h, t in zip(hs, ts)])
+    assert _vup_ok("vup config", got, ref)
