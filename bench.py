@@ -34,7 +34,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "causal MLA prefill TFLOP/s and % of bf16 MFMA peak on 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_latent_dsv3_prefill_hbm_traffic.json")
 KERNEL_SRCS = [os.path.join(ROOT, "ring_chunk_attention_amd", "csrc", f)
-               for f in ("mla_attn.hip", "mla_attn_body.inc", "mla_qk_chain.inc")]
+               for f in ("mla_attn.hip", "mla_attn_kernels.inc", "mla_attn_body.inc", "mla_qk_chain.inc")]
 
 
 def causal_pairs(n_q: int, n_kv: int, q_offset: int = 0, kv_offset: int = 0) -> int:
@@ -45,8 +45,8 @@ def causal_pairs(n_q: int, n_kv: int, q_offset: int = 0, kv_offset: int = 0) -> 
 
 
 def kernel_hash() -> str:
-    """Hash of the attention kernel's sources (the kernel file and the Q.K
-    chain it includes)."""
+    """Hash of the attention kernel's sources (the launcher file, the kernel
+    template and body it includes, and the generated Q.K chain)."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
         with open(path, "rb") as f:
@@ -323,11 +323,16 @@ def measure_rows(mla, W, to_dev, steps, warmup):
     q, kv = to_dev(c.q), to_dev(c.kv)
     o = torch.empty((1, 16, 4096, 512), dtype=torch.bfloat16, device="cuda")
     l = torch.empty((1, 16, 4096), dtype=torch.float32, device="cuda")
+    # balanced schedule (the default): full calls packed 2 + 2 + 2, then the
+    # 4 diagonals; ring order: 4 diagonals, then 3, 2 and 1 full calls
     ms, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l), steps, warmup)
+    ms_ring, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l, order="ring"),
+                                  steps, warmup)
     fl = 16 * causal_pairs(4096, 4096) * 2176
     rows["ring_4x1024_h16"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
                                "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-                               "calls": 10, "launches": 4, "folds_in_epilogue": 6}
+                               "calls": 10, "launches": 4, "folds_in_epilogue": 6,
+                               "schedule": "balanced", "ring_order_ms": round(ms_ring, 4)}
     # the same workload unchunked, for the cost of chunking
     ms1, _, _ = time_launches(lambda: mla.fwd(q, kv, scale=c.scale, out=o, lse=l), steps, warmup)
     rows["ring_4x1024_h16"]["unchunked_ms"] = round(ms1, 4)

@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import Optional, Sequence, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 import torch
 
@@ -518,14 +518,56 @@ def ring_order(r: int, n_chunks: int) -> Sequence[int]:
     return [(r - s) % n_chunks for s in range(n_chunks) if (r - s) % n_chunks <= r]
 
 
+def ring_schedule(n_chunks: int, order: str = "balanced") -> List[List[Tuple[int, int]]]:
+    """Launches of a one-device ring: a list of launches, each a list of
+    (query chunk r, KV chunk k) calls that run together.  Every pair k <= r
+    appears once; a query chunk has at most one call per launch, and its
+    calls run in launch order, each folding into the previous one's result.
+
+    "ring": launch s is ring step s, in which query chunk r meets KV chunk
+    (r - s) mod P, as each device of a P-device ring does at that step.  The
+    step launches hold P, P - 1, ..., 1 calls (the diagonals first).
+
+    "balanced": the same calls packed so that launches are equally full.
+    The fold is commutative (the result does not depend on the order in
+    which a query chunk meets its KV chunks), so each query chunk's full
+    calls (k < r) go to the least-filled of the first P - 1 launches, longest
+    chains first, and all diagonal calls (k = r, half the work of a full
+    call) run together in the last launch.  For P = 4 the launches hold 2,
+    2, 2 full calls and then the 4 diagonals, against 4 diagonals, 3, 2 and
+    1 full calls in ring order: with 128 workgroups a call, each launch then
+    fills the 256 compute units once instead of 1.5 or 0.5 times."""
+    if n_chunks < 1:
+        raise ValueError("n_chunks must be >= 1")
+    P = n_chunks
+    if order == "ring":
+        steps = [[] for _ in range(P)]
+        for r in range(P):
+            for s, k in enumerate(ring_order(r, P)):
+                steps[s].append((r, k))
+        return steps
+    if order != "balanced":
+        raise ValueError(f"unknown ring schedule {order!r}")
+    full = [[] for _ in range(max(P - 1, 0))]
+    for r in range(P - 1, 0, -1):
+        # the r least-filled launches (ties: the earlier one), in launch order
+        slots = sorted(sorted(range(P - 1), key=lambda j: (len(full[j]), j))[:r])
+        for k, j in enumerate(slots):
+            full[j].append((r, k))
+    return [l for l in full if l] + [[(r, r) for r in range(P)]]
+
+
 def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
              head_dim_v: int = 512, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None,
-             carry: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+             carry: Optional[torch.Tensor] = None,
+             order: str = "balanced") -> Tuple[torch.Tensor, torch.Tensor]:
     """Causal shared-latent attention of q [B,H,N,dk] over kv [B,1,N,dk]
     processed as a ring of ``n_chunks`` contiguous chunks on one device.
 
-    Query chunk r meets each KV chunk k <= r in ring order; every call passes
+    Query chunk r meets each KV chunk k <= r (``order``: see ring_schedule;
+    "ring" visits them in ring order, "balanced", the default, packs the
+    launches evenly); every call passes
     the global offsets (r*C, k*C), so the kernel applies the causal mask on
     the diagonal chunk and none on earlier chunks, and every call after the
     first folds its result into the running (out, lse) through the prev
@@ -534,9 +576,9 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
     kept in float32 (``carry``, [n_chunks, B, H, C, dv], allocated if not
     given) and only the last step of each query chunk writes bf16 ``out``.
 
-    The query chunks are independent of one another: each ring step runs as
-    one launch for all of them (mla_fwd_group, up to four chunks a launch),
-    on the caller's stream."""
+    The query chunks are independent of one another: each launch of the
+    schedule runs their calls together (mla_fwd_group, up to four calls a
+    launch), on the caller's stream."""
     B, H, N, dk = q.shape
     if N % n_chunks:
         raise ValueError("sequence length must be a multiple of the chunk count")
@@ -547,18 +589,17 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if carry is None and n_chunks > 1:
         carry = torch.empty((n_chunks, B, H, C, head_dim_v), dtype=torch.float32, device=q.device)
-    orders = [ring_order(r, n_chunks) for r in range(n_chunks)]
-    for step in range(n_chunks):
+    launches = ring_schedule(n_chunks, order)
+    done = [0] * n_chunks   # calls of each query chunk issued so far
+    for launch in launches:
         calls = []
-        for r in range(n_chunks):
-            if step >= len(orders[r]):
-                continue
-            k = orders[r][step]
+        for r, k in launch:
             qs = slice(r * C, (r + 1) * C)
-            last = step == len(orders[r]) - 1
+            first, last = done[r] == 0, done[r] == r   # query chunk r makes r + 1 calls
+            done[r] += 1
             calls.append(dict(q=q[:, :, qs], kv=kv[:, :, k * C:(k + 1) * C], scale=scale,
                               head_dim_v=head_dim_v, causal=True, q_offset=r * C, kv_offset=k * C,
-                              prev=None if step == 0 else (carry[r], lse[:, :, qs]),
+                              prev=None if first else (carry[r], lse[:, :, qs]),
                               out=out[:, :, qs] if last else carry[r], lse=lse[:, :, qs]))
         for i in range(0, len(calls), MAX_GROUP):
             fwd_group(calls[i:i + MAX_GROUP])

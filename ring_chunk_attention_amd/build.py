@@ -21,7 +21,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla355.so")
 
-SOURCES = ["mla_attn.hip", "mla_merge.hip", "mla_vup.hip", "mla_abi.cpp"]
+SOURCES = ["mla_attn.hip", "mla_attn_split.hip", "mla_merge.hip", "mla_vup.hip", "mla_abi.cpp"]
+
+# Per-source device flags: the split form keeps its MFMA accumulators in
+# VGPRs (an LLVM option, given to the device compile only).
+EXTRA_FLAGS = {"mla_attn_split.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -63,7 +67,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmds.append([hipcc, *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src),
+                     "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

@@ -252,3 +252,36 @@ def test_vup_rejects(lib, args, code, msg):
     st = lib.mla_vup(ctypes.byref(r), a["w"], a["B"], a["H"], a["T"], a["L"], a["dvh"], a["flags"],
                      ctypes.byref(r), None)
     assert st == code and msg in lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("order", ["ring", "balanced"])
+@pytest.mark.parametrize("P", range(1, 10))
+def test_ring_schedule_is_a_valid_fold_order(P, order):
+    """Host ring driver: every pair k <= r is called once, a query chunk has
+    at most one call per launch (its calls fold one after another), and the
+    ring order's launch s is ring step s."""
+    from ring_chunk_attention_amd import ring_order, ring_schedule
+    launches = ring_schedule(P, order)
+    seen = [(r, k) for launch in launches for r, k in launch]
+    assert sorted(seen) == sorted((r, k) for r in range(P) for k in range(r + 1))
+    for launch in launches:
+        rs = [r for r, _ in launch]
+        assert len(rs) == len(set(rs))
+    if order == "ring":
+        for s, launch in enumerate(launches):
+            assert sorted(launch) == sorted((r, ring_order(r, P)[s]) for r in range(P) if s < r + 1)
+    else:
+        # the diagonals together, last; the full calls spread evenly over the
+        # launches before them
+        assert sorted(launches[-1]) == [(r, r) for r in range(P)]
+        sizes = [len(l) for l in launches[:-1]]
+        assert len(launches) == P
+        if sizes:
+            assert max(sizes) - min(sizes) <= 1
+            assert sum(sizes) == P * (P - 1) // 2
+
+
+def test_ring_schedule_rejects_unknown_order():
+    from ring_chunk_attention_amd import ring_schedule
+    with pytest.raises(ValueError):
+        ring_schedule(4, "zigzag")

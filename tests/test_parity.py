@@ -192,21 +192,24 @@ def test_merge_in_place_dv128(mla):
     assert report("merge in place LSE", host(tl), l_ref) <= LSE_TOL
 
 
-@pytest.mark.parametrize("H,N,P", [(4, 256, 4), (3, 192, 3), (2, 96, 1)])
-def test_ring_small_equals_unchunked_oracle(mla, H, N, P):
+@pytest.mark.parametrize("order", ["ring", "balanced"])
+@pytest.mark.parametrize("H,N,P", [(4, 256, 4), (3, 192, 3), (2, 96, 1), (2, 640, 5)])
+def test_ring_small_equals_unchunked_oracle(mla, H, N, P, order):
     c = W.dense_case(B=1, H=H, N=N, seed=30 + P)
-    out, lse = mla.ring_fwd(dev_bf16(c.q), dev_bf16(c.kv), P, scale=c.scale)
+    out, lse = mla.ring_fwd(dev_bf16(c.q), dev_bf16(c.kv), P, scale=c.scale, order=order)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
     assert report("ring O", host(out), o_ref) <= O_TOL
     assert report("ring LSE", host(lse), l_ref) <= LSE_TOL
 
 
-def test_ring4_config_sampled(mla):
-    """16 heads, N = 4096 in 4 chunks of 1024 in ring order: sampled rows of
-    four heads against the unchunked oracle."""
+@pytest.mark.parametrize("order", ["ring", "balanced"])
+def test_ring4_config_sampled(mla, order):
+    """16 heads, N = 4096 in 4 chunks of 1024, in ring order and in the
+    balanced schedule: sampled rows of four heads against the unchunked
+    oracle."""
     c = W.ring4(0)
-    out, lse = mla.ring_fwd(dev_bf16(c.q), dev_bf16(c.kv), 4, scale=c.scale)
+    out, lse = mla.ring_fwd(dev_bf16(c.q), dev_bf16(c.kv), 4, scale=c.scale, order=order)
     torch.cuda.synchronize()
     heads = [0, 5, 10, 15]
     rows = np.array([0, 1, 511, 1023, 1024, 1025, 2047, 2048, 3071, 3072, 3073, 4094, 4095])
