@@ -35,6 +35,12 @@
  *   page are such views.  Data pointers and the b/h/t strides of bf16 views
  *   must be multiples of 8 elements (16 bytes).  LSE views use the same
  *   struct with d absent (D = 1, any strides).
+ * - Empty views: a view that holds no rows (a zero size: B, the query or
+ *   token count, or the key/cache row count) may have a NULL data pointer;
+ *   nothing is read or written through it.  A call whose output has no rows
+ *   enqueues nothing.  With query rows but no key rows (Nkv = 0) every row
+ *   sees no key: out = 0 and lse = -inf, or the previous pair unchanged
+ *   when one is folded in.
  * - Errors: every function validates all arguments before enqueuing anything.
  *   On failure it enqueues nothing, returns a non-zero mla_status and
  *   mla_last_error() describes the first problem found.  A HIP launch error

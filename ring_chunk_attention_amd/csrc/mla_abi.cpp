@@ -54,7 +54,8 @@ bool decode_split(int32_t B, int64_t Nkv, int32_t req, int32_t* S, int32_t* chun
     const int64_t s_min = (n + kMaxChunk - 1) / kMaxChunk;
     const int64_t s_fill = B > 0 ? (kTargetItems + B - 1) / B : 1;
     const int64_t s_cap = std::max<int64_t>(1, (n + kMinChunk - 1) / kMinChunk);
-    s = std::max(s_min, std::min(s_fill, s_cap));
+    // (never past the most ranges there may be: few long sequences ask for more)
+    s = std::max(s_min, std::min({s_fill, s_cap, kMaxSplits}));
   }
   int64_t c = (n + s - 1) / s;
   c = (c + 31) / 32 * 32;
@@ -87,9 +88,12 @@ mla_status hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // A bf16 row view used by a kernel: data 16-byte aligned, b/h/t strides
-// multiples of 8 elements, non-negative.
-mla_status check_rows(const mla_rows* r, const char* name, bool need_h = true) {
-  if (!r || !r->data) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+// multiples of 8 elements, non-negative.  `empty`: the view holds no rows
+// (a zero size), so its data pointer may be NULL (nothing is read or
+// written through it).
+mla_status check_rows(const mla_rows* r, const char* name, bool need_h = true, bool empty = false) {
+  if (!r) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+  if (!r->data && !empty) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
   if (!aligned16(r->data)) return fail(MLA_ERR_INVALID_ARG, "%s: data pointer must be 16-byte aligned", name);
   if (r->stride_b < 0 || r->stride_h < 0 || r->stride_t < 0)
     return fail(MLA_ERR_INVALID_ARG, "%s: negative stride", name);
@@ -99,8 +103,9 @@ mla_status check_rows(const mla_rows* r, const char* name, bool need_h = true) {
 }
 
 // A float32 row view: data 16-byte aligned, b/h/t strides multiples of 4.
-mla_status check_rows_f32(const mla_rows* r, const char* name) {
-  if (!r || !r->data) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+mla_status check_rows_f32(const mla_rows* r, const char* name, bool empty = false) {
+  if (!r) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+  if (!r->data && !empty) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
   if (!aligned16(r->data)) return fail(MLA_ERR_INVALID_ARG, "%s: data pointer must be 16-byte aligned", name);
   if (r->stride_b < 0 || r->stride_h < 0 || r->stride_t < 0)
     return fail(MLA_ERR_INVALID_ARG, "%s: negative stride", name);
@@ -109,8 +114,9 @@ mla_status check_rows_f32(const mla_rows* r, const char* name) {
   return MLA_OK;
 }
 
-mla_status check_lse(const mla_rows* r, const char* name) {
-  if (!r || !r->data) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+mla_status check_lse(const mla_rows* r, const char* name, bool empty = false) {
+  if (!r) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+  if (!r->data && !empty) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
   if (reinterpret_cast<uintptr_t>(r->data) & 3u) return fail(MLA_ERR_INVALID_ARG, "%s: data pointer must be 4-byte aligned", name);
   if (r->stride_b < 0 || r->stride_h < 0 || r->stride_t < 0)
     return fail(MLA_ERR_INVALID_ARG, "%s: negative stride", name);
@@ -166,28 +172,33 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
   if ((st = check_workspace(workspace, workspace_bytes))) return st;
   const bool out_f32 = flags & MLA_OUT_F32, prev_f32 = flags & MLA_PREV_OUT_F32;
-  if ((st = check_rows(q, "q")) || (st = check_rows(kv, "kv"))) return st;
-  if ((st = out_f32 ? check_rows_f32(out, "out") : check_rows(out, "out"))) return st;
+  // query-side views are empty without query rows, key-side ones without key rows
+  const bool no_q = B == 0 || Nq == 0, no_kv = B == 0 || Nkv == 0;
+  if ((st = check_rows(q, "q", true, no_q)) || (st = check_rows(kv, "kv", true, no_kv))) return st;
+  if ((st = out_f32 ? check_rows_f32(out, "out", no_q) : check_rows(out, "out", true, no_q))) return st;
   if ((q_rope == nullptr) != (k_rope == nullptr))
     return fail(MLA_ERR_INVALID_ARG, "q_rope and k_rope must both be given or both be NULL");
   if ((q_rope == nullptr) != (dr == 0))
     return fail(MLA_ERR_INVALID_ARG, "dr must be 0 exactly when q_rope/k_rope are NULL");
-  if (q_rope && ((st = check_rows(q_rope, "q_rope")) || (st = check_rows(k_rope, "k_rope")))) return st;
-  if (v && (st = check_rows(v, "v"))) return st;
+  if (q_rope && ((st = check_rows(q_rope, "q_rope", true, no_q)) || (st = check_rows(k_rope, "k_rope", true, no_kv))))
+    return st;
+  if (v && (st = check_rows(v, "v", true, no_kv))) return st;
   if (!v && dv > dq)
     return fail(MLA_ERR_INVALID_ARG, "head_dim_v (%d) must not exceed the kv width (%d) when V is the KV prefix", dv, dq);
   if ((prev_out == nullptr) != (prev_lse == nullptr))
     return fail(MLA_ERR_INVALID_ARG, "prev_out and prev_lse must both be given or both be NULL");
   if (prev_f32 && !prev_out) return fail(MLA_ERR_INVALID_ARG, "MLA_PREV_OUT_F32 given without prev_out");
-  if (prev_out && ((st = prev_f32 ? check_rows_f32(prev_out, "prev_out") : check_rows(prev_out, "prev_out")) ||
-                   (st = check_lse(prev_lse, "prev_lse"))))
+  if (prev_out && ((st = prev_f32 ? check_rows_f32(prev_out, "prev_out", no_q)
+                                  : check_rows(prev_out, "prev_out", true, no_q)) ||
+                   (st = check_lse(prev_lse, "prev_lse", no_q))))
     return st;
-  if (prev_out && out->data == prev_out->data && out_f32 != prev_f32)
+  // (aliasing is judged on real buffers: empty views may all be NULL)
+  if (prev_out && out->data && out->data == prev_out->data && out_f32 != prev_f32)
     return fail(MLA_ERR_INVALID_ARG, "out may alias prev_out only with the same element type");
-  if (lse && (st = check_lse(lse, "lse"))) return st;
-  if (prev_out && out->data == prev_out->data && !same_view(out, prev_out))
+  if (lse && (st = check_lse(lse, "lse", no_q))) return st;
+  if (prev_out && out->data && out->data == prev_out->data && !same_view(out, prev_out))
     return fail(MLA_ERR_INVALID_ARG, "out may alias prev_out only as the identical view");
-  if (prev_lse && lse && lse->data == prev_lse->data && !same_view(lse, prev_lse))
+  if (prev_lse && lse && lse->data && lse->data == prev_lse->data && !same_view(lse, prev_lse))
     return fail(MLA_ERR_INVALID_ARG, "lse may alias prev_lse only as the identical view");
   const bool valid_lens = flags & MLA_VALID_LENS;
   if (valid_lens) {
@@ -236,8 +247,9 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
   if (latent) {
     if (dr == 0) {
       // one 576-column tensor: the kernel reads its last 64 columns as the RoPE part
+      // (kv may be NULL when it has no rows: the kernel then loads no key tile)
       p.qb.p = p.qa.p + (dq - 64);
-      p.kb.p = p.ka.p + (dq - 64);
+      p.kb.p = p.ka.p ? p.ka.p + (dq - 64) : nullptr;
       p.da = dq - 64;
     }
     const int64_t n_qblk = (Nq + 31) / 32, n_hgrp = (Hq + 3) / 4;
@@ -331,10 +343,13 @@ mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a, const mla
   mla_status st;
   if (B < 0 || H <= 0 || N < 0 || dv <= 0 || dv % 8)
     return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, H > 0, N >= 0, dv > 0 and a multiple of 8");
-  if ((st = check_rows(out_a, "out_a")) || (st = check_rows(out_b, "out_b")) || (st = check_rows(out, "out")))
+  const bool none = B == 0 || N == 0;  // no rows: the views may be NULL
+  if ((st = check_rows(out_a, "out_a", true, none)) || (st = check_rows(out_b, "out_b", true, none)) ||
+      (st = check_rows(out, "out", true, none)))
     return st;
-  if ((st = check_lse(lse_a, "lse_a")) || (st = check_lse(lse_b, "lse_b"))) return st;
-  if (lse && (st = check_lse(lse, "lse"))) return st;
+  if ((st = check_lse(lse_a, "lse_a", none)) || (st = check_lse(lse_b, "lse_b", none))) return st;
+  if (lse && (st = check_lse(lse, "lse", none))) return st;
+  if (none) return MLA_OK;
   if ((out->data == out_a->data && !same_view(out, out_a)) || (out->data == out_b->data && !same_view(out, out_b)))
     return fail(MLA_ERR_INVALID_ARG, "out may alias out_a/out_b only as the identical view");
   if (lse && ((lse->data == lse_a->data && !same_view(lse, lse_a)) || (lse->data == lse_b->data && !same_view(lse, lse_b))))
@@ -371,12 +386,15 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
   if (flags & ~MLA_OUT_MX4) return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~MLA_OUT_MX4);
   if ((st = check_workspace(workspace, workspace_bytes))) return st;
-  if ((st = check_rows(q_lift, "q_lift")) || (st = check_rows(q_pe, "q_pe")) || (st = check_rows(out, "out")))
+  const bool no_q = B == 0 || S == 0;  // no queries: the query-side views may be NULL
+  if ((st = check_rows(q_lift, "q_lift", true, no_q)) || (st = check_rows(q_pe, "q_pe", true, no_q)) ||
+      (st = check_rows(out, "out", true, no_q)))
     return st;
-  if ((st = check_rows(c_kv, "c_kv", false)) || (st = check_rows(k_pe, "k_pe", false))) return st;
-  if (!topk_idx || (reinterpret_cast<uintptr_t>(topk_idx) & 3u))
+  if ((st = check_rows(c_kv, "c_kv", false, B == 0)) || (st = check_rows(k_pe, "k_pe", false, B == 0))) return st;
+  if ((!topk_idx && !no_q) || (reinterpret_cast<uintptr_t>(topk_idx) & 3u))
     return fail(MLA_ERR_INVALID_ARG, "topk_idx: missing or not 4-byte aligned");
-  if (lse && (st = check_lse(lse, "lse"))) return st;
+  if (lse && (st = check_lse(lse, "lse", no_q))) return st;
+  if (no_q) return MLA_OK;
   if ((int64_t)B * S > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
   if (S_kv * c_kv->stride_t * 2 > kMaxGrid || S_kv * k_pe->stride_t * 2 > kMaxGrid)
     return fail(MLA_ERR_UNSUPPORTED, "one batch of the cache must span less than 2 GiB (row offsets are 32-bit)");
@@ -428,10 +446,14 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_r
     return fail(MLA_ERR_INVALID_ARG, "q_rope and k_rope must both be given or both be NULL");
   if ((q_rope == nullptr) != (dr == 0))
     return fail(MLA_ERR_INVALID_ARG, "dr must be 0 exactly when q_rope/k_rope are NULL");
-  if ((st = check_rows(q, "q", true)) || (st = check_rows(kv, "kv", false)) || (st = check_rows(out, "out")))
+  // no sequences: every view may be NULL; no cache rows: the cache may be
+  const bool no_b = B == 0, no_kv = B == 0 || Nkv == 0;
+  if ((st = check_rows(q, "q", true, no_b)) || (st = check_rows(kv, "kv", false, no_kv)) ||
+      (st = check_rows(out, "out", true, no_b)))
     return st;
-  if (q_rope && ((st = check_rows(q_rope, "q_rope")) || (st = check_rows(k_rope, "k_rope", false)))) return st;
-  if (lse && (st = check_lse(lse, "lse"))) return st;
+  if (q_rope && ((st = check_rows(q_rope, "q_rope", true, no_b)) || (st = check_rows(k_rope, "k_rope", false, no_kv))))
+    return st;
+  if (lse && (st = check_lse(lse, "lse", no_b))) return st;
   if (kv_lens && (reinterpret_cast<uintptr_t>(kv_lens) & 3u))
     return fail(MLA_ERR_INVALID_ARG, "kv_lens must be 4-byte aligned");
   if (kv_slots && (reinterpret_cast<uintptr_t>(kv_slots) & 3u))
@@ -467,7 +489,7 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_r
                 : mla::RowsC{p.qa.p + (dq - 64), q->stride_b, q->stride_h, 0};
   p.ka = mla::RowsC{static_cast<const uint16_t*>(kv->data), kv->stride_b, 0, kv->stride_t};
   p.kb = k_rope ? mla::RowsC{static_cast<const uint16_t*>(k_rope->data), k_rope->stride_b, 0, k_rope->stride_t}
-                : mla::RowsC{p.ka.p + (dq - 64), kv->stride_b, 0, kv->stride_t};
+                : mla::RowsC{p.ka.p ? p.ka.p + (dq - 64) : nullptr, kv->stride_b, 0, kv->stride_t};
   p.da = dr == 0 ? dq - 64 : dq;
   p.B = B;
   p.Hq = H;
@@ -515,8 +537,10 @@ mla_status mla_vup(const mla_rows* o, const void* w_uv, int32_t B, int32_t H, in
   if (L != 512 || dvh != 128)
     return fail(MLA_ERR_UNSUPPORTED, "V-up is built for L = 512, dvh = 128 (got %d, %d)", L, dvh);
   if (flags & ~MLA_OUT_MX4) return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~MLA_OUT_MX4);
-  if ((st = check_rows(o, "o")) || (st = check_rows(out, "out"))) return st;
+  const bool none = B == 0 || T == 0;  // no rows: o and out may be NULL
+  if ((st = check_rows(o, "o", true, none)) || (st = check_rows(out, "out", true, none))) return st;
   if (!w_uv || !aligned16(w_uv)) return fail(MLA_ERR_INVALID_ARG, "w_uv: missing or not 16-byte aligned");
+  if (none) return MLA_OK;
   if ((int64_t)H * 512 > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "too many heads for one launch");
   mla::VupParams p{};
   p.o = rc(o);

@@ -194,6 +194,8 @@ def test_decode_workspace_size(lib):
     assert lib.mla_decode_workspace_size(64, 128, 8192, 0) == 256 + 64 * 4 * 128 * 4 + 64 * 4 * 128 * 512 * 4
     assert lib.mla_decode_workspace_size(4, 128, 8192, 2) == 0      # a split would exceed 2048 rows
     assert lib.mla_decode_workspace_size(4, 128, 200000, 0) == 0    # beyond 64 splits
+    # the longest cache with few sequences: the library's choice stops at 64 splits of 2048
+    assert lib.mla_decode_workspace_size(2, 128, 131072, 0) == 256 + 2 * 64 * 128 * 4 + 2 * 64 * 128 * 512 * 4
 
 
 def test_group_rejects_bad_calls(lib):
@@ -285,3 +287,48 @@ def test_ring_schedule_rejects_unknown_order():
     from ring_chunk_attention_amd import ring_schedule
     with pytest.raises(ValueError):
         ring_schedule(4, "zigzag")
+
+
+# ---------------------------------------------------------------------------
+# empty problems: a view with no rows may be NULL (PyTorch gives an empty
+# GPU tensor a NULL data pointer); nothing is launched, so these run on the
+# host
+# ---------------------------------------------------------------------------
+NULL_ROWS = Rows(0, 0, 0, 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(Nq=0, q=NULL_ROWS, out=NULL_ROWS),
+    dict(B=0, q=NULL_ROWS, kv=NULL_ROWS, out=NULL_ROWS),
+    dict(Nq=0, q=NULL_ROWS, out=NULL_ROWS, lse=NULL_ROWS, prev_out=NULL_ROWS, prev_lse=NULL_ROWS, flags=1),
+])
+def test_fwd_empty_problem_accepts_null_views(lib, kw):
+    assert call_fwd(lib, **kw) == MLA_OK, lib.mla_last_error().decode()
+
+
+def test_fwd_empty_problem_still_checks_shapes(lib):
+    # an empty problem of a shape without a kernel is still reported
+    assert call_fwd(lib, Nq=0, q=NULL_ROWS, out=NULL_ROWS, Hkv=2) == MLA_ERR_UNSUPPORTED
+    # and a NULL view that holds rows is still missing, even where no row would be read
+    assert call_fwd(lib, Nq=0, q=NULL_ROWS, out=NULL_ROWS, kv=NULL_ROWS) == MLA_ERR_INVALID_ARG
+    assert "kv: missing" in lib.mla_last_error().decode()
+    assert call_fwd(lib, Nkv=0, kv=NULL_ROWS, q=NULL_ROWS) == MLA_ERR_INVALID_ARG
+    assert "q: missing" in lib.mla_last_error().decode()
+
+
+def test_merge_sparse_vup_decode_empty_accept_null_views(lib):
+    from ring_chunk_attention_amd.binding import MlaRows
+    n = MlaRows(0, 0, 0, 0)
+    r = MlaRows(FAKE, 0, 512, 512)
+    assert lib.mla_merge_lse(ctypes.byref(n), ctypes.byref(n), ctypes.byref(n), ctypes.byref(n),
+                             1, 4, 0, 512, ctypes.byref(n), ctypes.byref(n), None) == MLA_OK
+    assert lib.mla_merge_lse(ctypes.byref(n), ctypes.byref(n), ctypes.byref(n), ctypes.byref(n),
+                             1, 4, 5, 512, ctypes.byref(n), ctypes.byref(n), None) == MLA_ERR_INVALID_ARG
+    # sparse: no queries -> the query side and the index list may be NULL
+    assert lib.mla_sparse_fwd(ctypes.byref(n), ctypes.byref(n), ctypes.byref(r), ctypes.byref(r), None,
+                              1, 0, 1024, 128, 512, 64, 128, 0.07, 0, ctypes.byref(n), None, None, 0,
+                              None) == MLA_OK
+    # V-up: no rows
+    assert lib.mla_vup(ctypes.byref(n), FAKE, 1, 4, 0, 512, 128, 0, ctypes.byref(n), None) == MLA_OK
+    # decode: no sequences
+    assert call_decode(lib, B=0, q=NULL_ROWS, kv=NULL_ROWS, out=NULL_ROWS) == MLA_OK

@@ -277,9 +277,10 @@ def _sparse_gpu(mla, c, idx=None):
 
 
 @pytest.mark.parametrize("H,K,seed", [(128, 96, 40), (20, 2048, 41), (128, 40, 42),
-                                      (16, 2049, 46), (128, 1, 47), (8, 2900, 49)])
+                                      (16, 2049, 46), (128, 1, 47), (8, 2900, 49),
+                                      (24, 4096, 50)])   # the longest list the kernel takes
 def test_sparse_small(mla, H, K, seed):
-    c = W.sparse_case(S=24, S_kv=3000, pos0=2900, H=H, K=K, seed=seed)
+    c = W.sparse_case(S=24, S_kv=max(3000, K + 100), pos0=max(2900, K + 50), H=H, K=K, seed=seed)
     out, lse = _sparse_gpu(mla, c)
     o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale)
     assert report("sparse O", host(out), o_ref) <= O_TOL
@@ -675,3 +676,59 @@ def test_vup_config_sampled(mla):
     got = out[0, torch.from_numpy(ts), torch.from_numpy(hs)].float().cpu().numpy().astype(np.float64)
     ref = np.stack([oracle.vup(c.o[:, h:h + 1, t:t + 1], c.w_uv[h:h + 1])[0, 0, 0] for h, t in zip(hs, ts)])
     assert _vup_ok("vup config", got, ref)
+
+
+# ---------------------------------------------------------------------------
+# degenerate and extreme sizes
+# ---------------------------------------------------------------------------
+def test_empty_sizes(mla):
+    """Empty inputs: no query rows, no batches, no key rows (every row sees
+    nothing: O = 0 and LSE = -inf, and a fold leaves the previous result as it
+    is), and empty merge, sparse, V-up and decode calls.  An empty GPU tensor
+    has a NULL data pointer, which the library accepts for a view that holds
+    no rows."""
+    rng = np.random.default_rng(95)
+    z = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    sc = W.SCALE_192
+    q = dev_bf16(W.normal_bf16(rng, (1, 4, 40, 576)))
+    kv = dev_bf16(W.normal_bf16(rng, (1, 1, 64, 576)))
+    out, lse = mla.fwd(z(1, 4, 0, 576), kv, scale=sc)                  # no query rows
+    assert out.shape == (1, 4, 0, 512) and lse.shape == (1, 4, 0)
+    out, lse = mla.fwd(z(0, 4, 40, 576), z(0, 1, 64, 576), scale=sc)   # no batches
+    assert out.shape == (0, 4, 40, 512)
+    for causal in (True, False):                                       # no key rows
+        out, lse = mla.fwd(q, z(1, 1, 0, 576), scale=sc, causal=causal)
+        torch.cuda.synchronize()
+        assert (host(out) == 0).all() and np.isneginf(host(lse)).all()
+    p_out = dev_bf16(W.normal_bf16(rng, (1, 4, 40, 512)))
+    p_lse = dev(rng.uniform(0, 12, (1, 4, 40)).astype(np.float32))
+    out, lse = mla.fwd(q, z(1, 1, 0, 576), scale=sc, prev=(p_out, p_lse))
+    torch.cuda.synchronize()
+    assert torch.equal(out, p_out) and torch.equal(lse, p_lse)         # the fold identity
+    e = z(1, 4, 0, 512)
+    el = torch.empty((1, 4, 0), dtype=torch.float32, device="cuda")
+    mo, ml = mla.merge(e, el, e, el)                                   # merge of no rows
+    assert mo.shape == (1, 4, 0, 512)
+    idx = torch.empty((1, 0, 128), dtype=torch.int32, device="cuda")
+    so, sl = mla.sparse_fwd(z(1, 0, 16, 512), z(1, 0, 16, 64), dev_bf16(W.normal_bf16(rng, (1, 300, 512))),
+                            dev_bf16(W.normal_bf16(rng, (1, 300, 64))), idx, scale=sc)
+    assert so.shape == (1, 0, 16 * 512)
+    w = dev_bf16(W.normal_bf16(rng, (4, 128, 512)))
+    vo = mla.vup(z(1, 4, 0, 512), w)                                   # V-up of no rows
+    assert vo.numel() == 0
+    do, dl = mla.decode_fwd(z(0, 16, 576), z(0, 100, 576), scale=sc)   # no sequences
+    assert do.shape == (0, 16, 512)
+    do, dl = mla.decode_fwd(dev_bf16(W.normal_bf16(rng, (2, 16, 576))), z(2, 0, 576), scale=sc)  # no cache rows
+    torch.cuda.synchronize()
+    assert (host(do) == 0).all() and np.isneginf(host(dl)).all()
+
+
+def test_decode_longest_cache(mla):
+    """The longest cache decode takes: 131,072 rows in 64 ranges of 2048, one
+    sequence at full length and one ragged, against the oracle."""
+    c = W.decode_case(B=2, H=128, Nkv=131072, kv_lens=[131072, 100001], seed=96)
+    out, lse = mla.decode_fwd(dev_bf16(c.q), dev_bf16(c.kv), scale=c.scale, kv_lens=dev(c.kv_lens))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode_mla(c.q, c.kv, c.kv_lens, 512, c.scale)
+    assert report("decode 131072 O", host(out), o_ref) <= O_TOL
+    assert report("decode 131072 LSE", host(lse), l_ref) <= LSE_TOL
