@@ -54,9 +54,30 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def time_launches(fn, steps: int, warmup: int):
+_HOLD = {}
+
+
+def hold_stream():
+    """Enqueue about 1 ms of unrelated GPU work (a 8192^3 bf16 matmul) on
+    the current stream, so that the calls enqueued behind it while it runs
+    reach the GPU back to back: a call shorter than the Python binding's
+    marshalling would otherwise be timed with that host latency in it."""
+    import torch
+    if "a" not in _HOLD:
+        _HOLD["a"] = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+        _HOLD["c"] = torch.empty_like(_HOLD["a"])
+    torch.mm(_HOLD["a"], _HOLD["a"], out=_HOLD["c"])
+
+
+def time_launches(fn, steps: int, warmup: int, hold: bool = False, per_launch: bool = True):
     """Warm up, then time `steps` calls with HIP events on the current stream;
-    returns (ms per step over the whole region, mean ms per launch)."""
+    returns (ms per step over the whole region, mean ms per launch, min ms per
+    launch).  ``per_launch`` False: only the region is bracketed by events
+    (each event record is a packet of its own on the queue, a few
+    microseconds beside short calls) and the per-launch figures are the
+    region's mean.  ``hold``: the calls also queue up behind hold_stream()
+    first, so that a call shorter than its own host-side marshalling is timed
+    on the GPU alone (the standalone merge)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -67,14 +88,20 @@ def time_launches(fn, steps: int, warmup: int):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if hold:
+        hold_stream()
     t0.record(stream)
     for k in range(steps):
-        starts[k].record(stream)
+        if per_launch:
+            starts[k].record(stream)
         fn()
-        ends[k].record(stream)
+        if per_launch:
+            ends[k].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     region = t0.elapsed_time(t1) / steps
+    if not per_launch:
+        return region, region, region
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return region, float(np.mean(per)), float(np.min(per))
 
@@ -311,7 +338,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measure_rows(mla, W, to_dev, steps, warmup):
+def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False):
     """Time the other steps of the path at their workload shapes."""
     import torch
     rows = {}
@@ -325,22 +352,23 @@ def measure_rows(mla, W, to_dev, steps, warmup):
     l = torch.empty((1, 16, 4096), dtype=torch.float32, device="cuda")
     # balanced schedule (the default): full calls packed 2 + 2 + 2, then the
     # 4 diagonals; ring order: 4 diagonals, then 3, 2 and 1 full calls
-    ms, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l), steps, warmup)
+    ms, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l), steps, warmup, per_launch=False)
     ms_ring, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l, order="ring"),
-                                  steps, warmup)
+                                  steps, warmup, per_launch=False)
     fl = 16 * causal_pairs(4096, 4096) * 2176
     rows["ring_4x1024_h16"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
                                "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                                "calls": 10, "launches": 4, "folds_in_epilogue": 6,
                                "schedule": "balanced", "ring_order_ms": round(ms_ring, 4)}
     # the same workload unchunked, for the cost of chunking
-    ms1, _, _ = time_launches(lambda: mla.fwd(q, kv, scale=c.scale, out=o, lse=l), steps, warmup)
+    ms1, _, _ = time_launches(lambda: mla.fwd(q, kv, scale=c.scale, out=o, lse=l), steps, warmup, per_launch=False)
     rows["ring_4x1024_h16"]["unchunked_ms"] = round(ms1, 4)
     # standalone merge of two [1, 16, 1024, 512] partials (HBM-bound)
     a, b = o[:, :, :1024].contiguous(), o[:, :, 1024:2048].contiguous()
     la, lb = l[:, :, :1024].contiguous(), l[:, :, 1024:2048].contiguous()
     mo, ml = torch.empty_like(a), torch.empty_like(la)
-    ms, _, _ = time_launches(lambda: mla.merge(a, la, b, lb, out=mo, lse=ml), steps, warmup)
+    ms, _, _ = time_launches(lambda: mla.merge(a, la, b, lb, out=mo, lse=ml), steps, warmup, hold=True,
+                             per_launch=False)
     nbytes = 3 * a.numel() * 2 + 3 * la.numel() * 4
     rows["merge_h16_1024x512"] = {"ms": round(ms, 4), "GBps": round(nbytes / ms / 1e6, 1),
                                   "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
@@ -356,7 +384,7 @@ def measure_rows(mla, W, to_dev, steps, warmup):
     so = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
     sL = torch.empty((32, T), dtype=torch.float32, device="cuda")
     ms, _, _ = time_launches(lambda: mla.split_fwd(*args, scale=c.scale, seq_lens=sl, prev=prev,
-                                                   out=so, lse=sL), steps, warmup)
+                                                   out=so, lse=sL), steps, warmup, per_launch=False)
     fl = 32 * sum(causal_pairs(int(L), int(L)) for L in c.seq_lens) * (2 * 192 + 2 * 128)
     rows["split_varlen_8seq_h32"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
                                      "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
@@ -370,7 +398,7 @@ def measure_rows(mla, W, to_dev, steps, warmup):
     idx = torch.from_numpy(c.idx).cuda()
     so = torch.empty((1, 4096, 128 * 512), dtype=torch.bfloat16, device="cuda")
     sL = torch.empty((1, 4096, 128), dtype=torch.float32, device="cuda")
-    ms, _, _ = time_launches(lambda: mla.sparse_fwd(*t, idx, scale=c.scale, out=so, lse=sL), steps, warmup)
+    ms, _, _ = time_launches(lambda: mla.sparse_fwd(*t, idx, scale=c.scale, out=so, lse=sL), steps, warmup, per_launch=False)
     fl = 4096 * 128 * 2048 * 2176
     gathered = 4096 * 2048 * 1152
     rows["sparse_topk_s4096_k2048_h128"] = {
@@ -388,7 +416,7 @@ def measure_rows(mla, W, to_dev, steps, warmup):
     do = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
     dl = torch.empty((B, H), dtype=torch.float32, device="cuda")
     ms, _, _ = time_launches(lambda: mla.decode_fwd(q, kv, scale=c.scale, kv_lens=lens, out=do, lse=dl),
-                             steps, warmup)
+                             steps, warmup, per_launch=False)
     keys = int(c.kv_lens.astype(np.int64).sum())
     fl = H * keys * 2176
     # algorithmic HBM bytes: each cache row once, the queries, outputs and LSEs
@@ -407,7 +435,7 @@ def measure_rows(mla, W, to_dev, steps, warmup):
     o, w = to_dev(c.o), to_dev(c.w_uv)
     B, H, T, L = c.o.shape
     vo = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
-    ms, _, _ = time_launches(lambda: mla.vup(o, w, out=vo), steps, warmup)
+    ms, _, _ = time_launches(lambda: mla.vup(o, w, out=vo), steps, warmup, per_launch=False)
     fl = B * H * T * L * 128 * 2
     nbytes = o.numel() * 2 + w.numel() * 2 + vo.numel() * 2   # each operand once
     rows["vup_h128_t8192"] = {

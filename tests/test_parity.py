@@ -192,6 +192,31 @@ def test_merge_in_place_dv128(mla):
     assert report("merge in place LSE", host(tl), l_ref) <= LSE_TOL
 
 
+def test_merge_wide_rows_nan_side_and_empty_rows(mla):
+    """dv = 1024 (columns past the first 512), a ragged row count, the output
+    written in place over the b side, a side of LSE -inf whose rows hold NaN
+    (weight 0: never multiplied) and rows with both sides -inf (O = 0,
+    LSE = -inf)."""
+    rng = np.random.default_rng(22)
+    oa = W.normal_bf16(rng, (1, 1, 37, 1024))
+    ob = W.normal_bf16(rng, (1, 1, 37, 1024))
+    la = rng.uniform(-5, 5, (1, 1, 37)).astype(np.float32)
+    lb = rng.uniform(-5, 5, (1, 1, 37)).astype(np.float32)
+    la[0, 0, 5:9] = -np.inf
+    oa[0, 0, 5:9] = 0x7fc0                        # bf16 NaN rows on the side of weight 0
+    lb[0, 0, 7:12] = -np.inf
+    ob[0, 0, 10:12] = 0x7fc0
+    tb, tl = dev_bf16(ob), dev(lb)
+    mla.merge(dev_bf16(oa), dev(la), tb, tl, out=tb, lse=tl)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.merge(oa, la, ob, lb)   # the oracle multiplies no weight-0 side either
+    got_o, got_l = host(tb), host(tl)
+    assert not np.isnan(got_o).any()
+    assert (got_o[0, 0, 7:9] == 0).all() and np.isneginf(got_l[0, 0, 7:9]).all()
+    assert report("merge wide O", got_o, o_ref) <= O_TOL
+    assert report("merge wide LSE", got_l, l_ref) <= LSE_TOL
+
+
 @pytest.mark.parametrize("order", ["ring", "balanced"])
 @pytest.mark.parametrize("H,N,P", [(4, 256, 4), (3, 192, 3), (2, 96, 1), (2, 640, 5)])
 def test_ring_small_equals_unchunked_oracle(mla, H, N, P, order):
