@@ -757,3 +757,37 @@ def test_decode_longest_cache(mla):
     o_ref, l_ref = oracle.decode_mla(c.q, c.kv, c.kv_lens, 512, c.scale)
     assert report("decode 131072 O", host(out), o_ref) <= O_TOL
     assert report("decode 131072 LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_ring_hip_graph_replays_match_eager(mla):
+    """The ring driver captured in a HIP graph (its group launches allocate
+    nothing and record no memset):
+    several replays, with eager work and synchronisations between them, each
+    bit-identical to the eager result."""
+    c = W.dense_case(B=1, H=8, N=1024, seed=97)
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    out = torch.empty((1, 8, 1024, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, 8, 1024), dtype=torch.float32, device="cuda")
+    carry = torch.empty((4, 1, 8, 256, 512), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # the eager result, off the capture stream
+        mla.ring_fwd(q, kv, 4, scale=c.scale, out=out, lse=lse, carry=carry)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    o_eager, l_eager = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mla.ring_fwd(q, kv, 4, scale=c.scale, out=out, lse=lse, carry=carry)
+    for rep in range(3):
+        out.fill_(0)
+        lse.fill_(0)
+        mla.fwd(q, kv, scale=c.scale)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_eager), f"replay {rep}: O differs from eager"
+        assert torch.equal(lse, l_eager), f"replay {rep}: LSE differs from eager"
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
+    assert report("graph ring O", host(out), o_ref) <= O_TOL
+    assert report("graph ring LSE", host(lse), l_ref) <= LSE_TOL
