@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -44,13 +45,22 @@ def causal_pairs(n_q: int, n_kv: int, q_offset: int = 0, kv_offset: int = 0) -> 
     return int(vis.sum())
 
 
+def _strip_comments(src: str) -> str:
+    """C++ source without its comments and trailing blanks (string literals
+    in these files hold no comment markers)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
+
+
 def kernel_hash() -> str:
-    """Hash of the attention kernel's sources (the launcher file, the kernel
-    template and body it includes, and the generated Q.K chain)."""
+    """Hash of the attention kernel's code (the launcher file, the kernel
+    template and body it includes, and the generated Q.K chain), comments
+    left out: a change of wording is not a change of the kernel."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 
