@@ -373,7 +373,7 @@ def emit_tile_step():
 
 def render():
     head = ("// Generated by gen_qk_chain.py from its description of the chain; do not\n"
-            "// edit by hand (rerun the script).  Included by mla_attn.hip inside its\n"
+            "// edit by hand (rerun the script).  Included by mla_attn_kernels.inc inside its\n"
             "// anonymous namespace, after the vector typedefs.\n\n")
     return (head
             + "// S^T = K Q^T over the 576 columns of one key tile.\n"

@@ -332,3 +332,10 @@ def test_merge_sparse_vup_decode_empty_accept_null_views(lib):
     assert lib.mla_vup(ctypes.byref(n), FAKE, 1, 4, 0, 512, 128, 0, ctypes.byref(n), None) == MLA_OK
     # decode: no sequences
     assert call_decode(lib, B=0, q=NULL_ROWS, kv=NULL_ROWS, out=NULL_ROWS) == MLA_OK
+
+
+def test_generated_qk_chain_is_current():
+    """mla_qk_chain.inc is the output of gen_qk_chain.py as it stands."""
+    gen = os.path.join(ROOT, "ring_chunk_attention_amd", "csrc", "gen_qk_chain.py")
+    r = subprocess.run(["python3", gen, "--check"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
