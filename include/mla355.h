@@ -195,6 +195,64 @@ typedef struct {
 mla_status mla_fwd_group(int32_t n, const mla_fwd_call* calls, void* stream /* hipStream_t */);
 
 /*
+ * mla_ring_fwd -- causal shared-latent attention of q over kv computed as a
+ * ring of n_chunks contiguous chunks on one device (TT-NN ring_mla: the
+ * sequence split into chunks, each query chunk meeting the KV chunks in
+ * turn, the output carried with its statistics; TensorRT-LLM mla.py,
+ * forward_context_with_chunked_prefill: earlier chunks with a full mask,
+ * the current one causal, partial outputs merged through their softmax
+ * stats; Ascend RingMLAOperation calcType: the first ring step has no prev).
+ *
+ * q [B, H, N, dq] and kv [B, 1, N, dq] (mla_rows views, the kv view's
+ * stride_h ignored), dq = 576 (512 latent + 64 RoPE columns in one row),
+ * value = the first dv = 512 columns of each kv row.  N must be a multiple
+ * of n_chunks (1 .. 64); C = N / n_chunks.  Query chunk r attends each KV
+ * chunk k <= r through one call equivalent to mla_fwd with q_offset = r*C
+ * and kv_offset = k*C (so the diagonal chunk is causal, earlier ones full,
+ * later ones are never visited: their keys lie in the causal future), and
+ * every call after a chunk's first folds into the running result.  The
+ * running result between folds is float32, kept in the workspace; only each
+ * query chunk's last call writes out (bf16) and its final lse.
+ *
+ * order: the launches the calls run in (mla_ring_schedule).  Results agree
+ * up to rounding between orders: the fold is commutative and associative.
+ *
+ * out [B, H, N, 512] bf16 and lse [B, H, N] fp32, both required.
+ * workspace: device memory of at least
+ * mla_ring_workspace_size(B, H, N, n_chunks) bytes, 256-byte aligned (may be
+ * NULL when that size is 0: one chunk, or an empty problem); contents
+ * unspecified on return.  Every argument and every call is validated before
+ * anything is enqueued.
+ */
+#define MLA_RING_ORDER 0     /* launch s is ring step s: chunk r meets KV chunk (r - s) mod P */
+#define MLA_RING_BALANCED 1  /* the same calls in equally full launches, the diagonals last */
+mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_t H, int64_t N,
+                        int32_t dq, int32_t dv, float scale, int32_t n_chunks, int32_t order,
+                        const mla_rows* out, const mla_rows* lse,
+                        void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+
+/* Bytes of the workspace mla_ring_fwd needs: B*H*N*512*4 for n_chunks > 1,
+ * 0 for one chunk or invalid sizes. */
+size_t mla_ring_workspace_size(int32_t B, int32_t H, int64_t N, int32_t n_chunks);
+
+/*
+ * mla_ring_schedule -- the launches mla_ring_fwd issues for P = n_chunks
+ * (host only; nothing is enqueued).  launch_of: host int32 array of
+ * P (P + 1) / 2 entries; entry r (r + 1) / 2 + k receives the launch index
+ * of the call of query chunk r on KV chunk k (k <= r).  *n_launches receives
+ * the number of launches (P).  A query chunk has at most one call per
+ * launch, and its calls fold in launch order.
+ *
+ * MLA_RING_ORDER: launch s is ring step s, as each device of a P-device
+ * ring runs it (P diagonal calls, then P - 1, ..., 1 full calls).
+ * MLA_RING_BALANCED: each query chunk's full calls (k < r), longest chains
+ * first, go to the r least-filled of the first P - 1 launches, and the P
+ * diagonal calls (half the work of a full call each) run together last;
+ * the launches are then equally full.
+ */
+mla_status mla_ring_schedule(int32_t n_chunks, int32_t order, int32_t* launch_of, int32_t* n_launches);
+
+/*
  * mla_merge_lse -- fold two partial results over disjoint key sets
  * (TensorRT-LLM mla.py, forward_context_with_chunked_prefill: partial outputs
  * merged with their softmax stats; Ascend RingMLAOperation prevOut/prevLse).

@@ -22,6 +22,9 @@ MLA_OUT_F32 = 2
 MLA_PREV_OUT_F32 = 4
 MLA_VALID_LENS = 8
 MLA_OUT_MX4 = 1  # mla_sparse_fwd
+MLA_RING_ORDER = 0
+MLA_RING_BALANCED = 1
+_RING_ORDERS = {"ring": MLA_RING_ORDER, "balanced": MLA_RING_BALANCED}
 
 
 class MlaRows(ctypes.Structure):
@@ -95,6 +98,15 @@ def _load():
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
     lib.mla_decode_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                               ctypes.c_int32]
+    lib.mla_ring_fwd.restype = ctypes.c_int
+    lib.mla_ring_fwd.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_ring_workspace_size.restype = ctypes.c_size_t
+    lib.mla_ring_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+    lib.mla_ring_schedule.restype = ctypes.c_int
+    lib.mla_ring_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                      ctypes.POINTER(ctypes.c_int32)]
     return lib
 
 
@@ -102,7 +114,8 @@ LIB = _load()
 LIB_PATH = _LIB_PATH
 
 EXPORTS = ("mla_fwd", "mla_fwd_group", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd", "mla_vup",
-           "mla_debug_gather", "mla_last_error", "mla_version", "mla_workspace_size", "mla_decode_workspace_size")
+           "mla_debug_gather", "mla_last_error", "mla_version", "mla_workspace_size", "mla_decode_workspace_size",
+           "mla_ring_fwd", "mla_ring_workspace_size", "mla_ring_schedule")
 
 
 class MlaError(RuntimeError):
@@ -519,42 +532,26 @@ def ring_order(r: int, n_chunks: int) -> Sequence[int]:
 
 
 def ring_schedule(n_chunks: int, order: str = "balanced") -> List[List[Tuple[int, int]]]:
-    """Launches of a one-device ring: a list of launches, each a list of
-    (query chunk r, KV chunk k) calls that run together.  Every pair k <= r
-    appears once; a query chunk has at most one call per launch, and its
-    calls run in launch order, each folding into the previous one's result.
-
-    "ring": launch s is ring step s, in which query chunk r meets KV chunk
-    (r - s) mod P, as each device of a P-device ring does at that step.  The
-    step launches hold P, P - 1, ..., 1 calls (the diagonals first).
-
-    "balanced": the same calls packed so that launches are equally full.
-    The fold is commutative (the result does not depend on the order in
-    which a query chunk meets its KV chunks), so each query chunk's full
-    calls (k < r) go to the least-filled of the first P - 1 launches, longest
-    chains first, and all diagonal calls (k = r, half the work of a full
-    call) run together in the last launch.  For P = 4 the launches hold 2,
-    2, 2 full calls and then the 4 diagonals, against 4 diagonals, 3, 2 and
-    1 full calls in ring order: with 128 workgroups a call, each launch then
-    fills the 256 compute units once instead of 1.5 or 0.5 times."""
-    if n_chunks < 1:
-        raise ValueError("n_chunks must be >= 1")
-    P = n_chunks
-    if order == "ring":
-        steps = [[] for _ in range(P)]
-        for r in range(P):
-            for s, k in enumerate(ring_order(r, P)):
-                steps[s].append((r, k))
-        return steps
-    if order != "balanced":
+    """The launches mla_ring_fwd issues (mla_ring_schedule): a list of
+    launches, each a list of (query chunk r, KV chunk k) calls that run
+    together.  Every pair k <= r appears once; a query chunk has at most one
+    call per launch, and its calls fold in launch order.  ``order``: "ring"
+    (launch s is ring step s: chunk r meets KV chunk (r - s) mod P) or
+    "balanced" (the same calls in equally full launches, the diagonals
+    last)."""
+    if order not in _RING_ORDERS:
         raise ValueError(f"unknown ring schedule {order!r}")
-    full = [[] for _ in range(max(P - 1, 0))]
-    for r in range(P - 1, 0, -1):
-        # the r least-filled launches (ties: the earlier one), in launch order
-        slots = sorted(sorted(range(P - 1), key=lambda j: (len(full[j]), j))[:r])
-        for k, j in enumerate(slots):
-            full[j].append((r, k))
-    return [l for l in full if l] + [[(r, r) for r in range(P)]]
+    P = int(n_chunks)
+    if P < 1:
+        raise ValueError("n_chunks must be >= 1")
+    launch_of = (ctypes.c_int32 * (P * (P + 1) // 2))()
+    n = ctypes.c_int32(0)
+    _check(LIB.mla_ring_schedule(P, _RING_ORDERS[order], launch_of, ctypes.byref(n)))
+    launches = [[] for _ in range(n.value)]
+    for r in range(P):
+        for k in range(r + 1):
+            launches[launch_of[r * (r + 1) // 2 + k]].append((r, k))
+    return launches
 
 
 def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
@@ -562,45 +559,34 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
              lse: Optional[torch.Tensor] = None,
              carry: Optional[torch.Tensor] = None,
              order: str = "balanced") -> Tuple[torch.Tensor, torch.Tensor]:
-    """Causal shared-latent attention of q [B,H,N,dk] over kv [B,1,N,dk]
-    processed as a ring of ``n_chunks`` contiguous chunks on one device.
-
-    Query chunk r meets each KV chunk k <= r (``order``: see ring_schedule;
-    "ring" visits them in ring order, "balanced", the default, packs the
-    launches evenly); every call passes
-    the global offsets (r*C, k*C), so the kernel applies the causal mask on
-    the diagonal chunk and none on earlier chunks, and every call after the
-    first folds its result into the running (out, lse) through the prev
-    arguments, in place (TensorRT-LLM mla.py forward_context_with_chunked_prefill;
-    Ascend RingMLAOperation calcType).  The running output between folds is
-    kept in float32 (``carry``, [n_chunks, B, H, C, dv], allocated if not
-    given) and only the last step of each query chunk writes bf16 ``out``.
-
-    The query chunks are independent of one another: each launch of the
-    schedule runs their calls together (mla_fwd_group, up to four calls a
-    launch), on the caller's stream."""
-    B, H, N, dk = q.shape
+    """Causal shared-latent attention of q [B,H,N,576] over kv [B,1,N,576]
+    processed as a ring of ``n_chunks`` contiguous chunks on one device
+    (mla_ring_fwd): query chunk r meets each KV chunk k <= r with global
+    offsets, and every call after the first folds into the running result
+    (TensorRT-LLM mla.py forward_context_with_chunked_prefill; Ascend
+    RingMLAOperation calcType).  ``order``: see ring_schedule.  ``carry``:
+    the float32 running result between folds, any contiguous GPU tensor of at
+    least mla_ring_workspace_size() bytes (allocated if not given)."""
+    if order not in _RING_ORDERS:
+        raise ValueError(f"unknown ring schedule {order!r}")
+    B, H, N, dq = q.shape
     if N % n_chunks:
         raise ValueError("sequence length must be a multiple of the chunk count")
-    C = N // n_chunks
     if out is None:
         out = torch.empty((B, H, N, head_dim_v), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if carry is None and n_chunks > 1:
-        carry = torch.empty((n_chunks, B, H, C, head_dim_v), dtype=torch.float32, device=q.device)
-    launches = ring_schedule(n_chunks, order)
-    done = [0] * n_chunks   # calls of each query chunk issued so far
-    for launch in launches:
-        calls = []
-        for r, k in launch:
-            qs = slice(r * C, (r + 1) * C)
-            first, last = done[r] == 0, done[r] == r   # query chunk r makes r + 1 calls
-            done[r] += 1
-            calls.append(dict(q=q[:, :, qs], kv=kv[:, :, k * C:(k + 1) * C], scale=scale,
-                              head_dim_v=head_dim_v, causal=True, q_offset=r * C, kv_offset=k * C,
-                              prev=None if first else (carry[r], lse[:, :, qs]),
-                              out=out[:, :, qs] if last else carry[r], lse=lse[:, :, qs]))
-        for i in range(0, len(calls), MAX_GROUP):
-            fwd_group(calls[i:i + MAX_GROUP])
+    need = int(LIB.mla_ring_workspace_size(B, H, N, n_chunks))
+    if carry is None and need:
+        carry = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws, ws_bytes = None, 0
+    if carry is not None:
+        if not carry.is_cuda or not carry.is_contiguous():
+            raise ValueError("carry: expected a contiguous GPU tensor")
+        ws, ws_bytes = carry.data_ptr(), carry.numel() * carry.element_size()
+    vq, vkv = _rows_bhtd(q, "q"), _rows_bhtd(kv, "kv")
+    vo, vl = _rows_bhtd(out, "out"), _lse_bht(lse, "lse")
+    _check(LIB.mla_ring_fwd(ctypes.byref(vq), ctypes.byref(vkv), B, H, N, dq, head_dim_v, float(scale),
+                            int(n_chunks), _RING_ORDERS[order], ctypes.byref(vo), ctypes.byref(vl),
+                            ws, ws_bytes, _stream(q.device)))
     return out, lse

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "mla_internal.h"
 
@@ -272,6 +273,74 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
               Hq, Hkv, dq, dr, dv, v ? "given" : "NULL", seq_lens ? "given" : "NULL");
 }
 
+// The calls of one mla_fwd_group launch, validated and prepared (nothing is
+// launched).  g->n == 0: nothing to launch.
+mla_status prepare_group(int32_t n, const mla_fwd_call* calls, mla::GroupParams* gp) {
+  mla::GroupParams& g = *gp;
+  g = mla::GroupParams{};
+  if (n < 0 || n > MLA_MAX_GROUP) return fail(MLA_ERR_INVALID_ARG, "n (%d) must lie in [0, %d]", n, MLA_MAX_GROUP);
+  if (n > 0 && !calls) return fail(MLA_ERR_INVALID_ARG, "calls: missing");
+  int64_t items = 0;
+  g.first[0] = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const mla_fwd_call& c = calls[i];
+    mla::AttnParams p;
+    int form = FORM_EMPTY;
+    if (mla_status st = prepare_fwd(c.q, c.q_rope, c.kv, c.k_rope, nullptr, c.B, c.Hq, 1, c.Nq, c.Nkv, c.dq, c.dr,
+                                    c.dv, nullptr, 0, c.scale, c.flags, c.q_offset, c.kv_offset, c.prev_out,
+                                    c.prev_lse, c.out, c.lse, nullptr, 0, &p, &form)) {
+      char buf[600];
+      snprintf(buf, sizeof(buf), "call %d: %s", i, g_last_error.c_str());
+      g_last_error = buf;
+      return st;
+    }
+    if (form == FORM_EMPTY) continue;
+    if (form != FORM_LATENT)
+      return fail(MLA_ERR_UNSUPPORTED, "call %d: a group holds shared-latent calls only", i);
+    items += (int64_t)p.n_qblk * p.n_hgrp * p.B;
+    if (items > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "group too large for one launch");
+    g.sub[g.n] = p;
+    g.first[++g.n] = (int32_t)items;
+  }
+  g.interleave = 1;
+  for (int k = 1; k < g.n; ++k)
+    if (g.first[k + 1] - g.first[k] != g.first[1]) g.interleave = 0;
+  return MLA_OK;
+}
+
+// One-device ring (the value width of the shared-latent form; the most chunks).
+constexpr int kRingDv = 512;
+constexpr int kMaxRingChunks = 64;
+
+// Launch index of each call (r, k), k <= r, at launch_of[r (r + 1) / 2 + k];
+// returns the number of launches.  MLA_RING_ORDER: launch s is ring step s,
+// in which query chunk r meets KV chunk (r - s) mod P (for s <= r that is
+// r - s; later steps bring chunks after r, which are skipped).
+// MLA_RING_BALANCED: each query chunk's full calls (k < r), longest chains
+// first, go to the r least-filled of the first P - 1 launches (ties: the
+// earlier launch), and every diagonal call (k = r) runs in the last launch.
+int ring_schedule(int P, int order, int32_t* launch_of) {
+  auto id = [](int r, int k) { return r * (r + 1) / 2 + k; };
+  if (order == MLA_RING_ORDER) {
+    for (int r = 0; r < P; ++r)
+      for (int s = 0; s <= r; ++s) launch_of[id(r, r - s)] = s;
+    return P;
+  }
+  int fill[kMaxRingChunks] = {0};
+  int order_of[kMaxRingChunks];
+  for (int r = P - 1; r >= 1; --r) {
+    for (int j = 0; j < P - 1; ++j) order_of[j] = j;
+    std::stable_sort(order_of, order_of + P - 1, [&](int a, int b) { return fill[a] < fill[b]; });
+    std::sort(order_of, order_of + r);  // the chosen launches, in launch order
+    for (int k = 0; k < r; ++k) {
+      launch_of[id(r, k)] = order_of[k];
+      ++fill[order_of[k]];
+    }
+  }
+  for (int r = 0; r < P; ++r) launch_of[id(r, r)] = P - 1;
+  return P;
+}
+
 }  // namespace
 
 extern "C" {
@@ -304,36 +373,118 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv
 
 mla_status mla_fwd_group(int32_t n, const mla_fwd_call* calls, void* stream) {
   g_last_error.clear();
-  if (n < 0 || n > MLA_MAX_GROUP) return fail(MLA_ERR_INVALID_ARG, "n (%d) must lie in [0, %d]", n, MLA_MAX_GROUP);
-  if (n > 0 && !calls) return fail(MLA_ERR_INVALID_ARG, "calls: missing");
-  mla::GroupParams g{};
-  int64_t items = 0;
-  g.first[0] = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    const mla_fwd_call& c = calls[i];
-    mla::AttnParams p;
-    int form = FORM_EMPTY;
-    if (mla_status st = prepare_fwd(c.q, c.q_rope, c.kv, c.k_rope, nullptr, c.B, c.Hq, 1, c.Nq, c.Nkv, c.dq, c.dr,
-                                    c.dv, nullptr, 0, c.scale, c.flags, c.q_offset, c.kv_offset, c.prev_out,
-                                    c.prev_lse, c.out, c.lse, nullptr, 0, &p, &form)) {
-      char buf[600];
-      snprintf(buf, sizeof(buf), "call %d: %s", i, g_last_error.c_str());
-      g_last_error = buf;
-      return st;
-    }
-    if (form == FORM_EMPTY) continue;
-    if (form != FORM_LATENT)
-      return fail(MLA_ERR_UNSUPPORTED, "call %d: a group holds shared-latent calls only", i);
-    items += (int64_t)p.n_qblk * p.n_hgrp * p.B;
-    if (items > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "group too large for one launch");
-    g.sub[g.n] = p;
-    g.first[++g.n] = (int32_t)items;
-  }
+  mla::GroupParams g;
+  if (mla_status st = prepare_group(n, calls, &g)) return st;
   if (g.n == 0) return MLA_OK;
-  g.interleave = 1;
-  for (int k = 1; k < g.n; ++k)
-    if (g.first[k + 1] - g.first[k] != g.first[1]) g.interleave = 0;
   return hip_status(mla::launch_latent_group(g, static_cast<hipStream_t>(stream)), "group attention launch");
+}
+
+mla_status mla_ring_schedule(int32_t n_chunks, int32_t order, int32_t* launch_of, int32_t* n_launches) {
+  g_last_error.clear();
+  if (n_chunks < 1 || n_chunks > kMaxRingChunks)
+    return fail(MLA_ERR_INVALID_ARG, "n_chunks (%d) must lie in [1, %d]", n_chunks, kMaxRingChunks);
+  if (order != MLA_RING_ORDER && order != MLA_RING_BALANCED)
+    return fail(MLA_ERR_INVALID_ARG, "order (%d) must be MLA_RING_ORDER or MLA_RING_BALANCED", order);
+  if (!launch_of || !n_launches) return fail(MLA_ERR_INVALID_ARG, "launch_of and n_launches must be given");
+  *n_launches = ring_schedule(n_chunks, order, launch_of);
+  return MLA_OK;
+}
+
+size_t mla_ring_workspace_size(int32_t B, int32_t H, int64_t N, int32_t n_chunks) {
+  if (B < 0 || H <= 0 || N < 0 || n_chunks < 1 || n_chunks > kMaxRingChunks || N % n_chunks) return 0;
+  if (n_chunks == 1) return 0;
+  return (size_t)B * H * N * kRingDv * sizeof(float);
+}
+
+mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_t H, int64_t N, int32_t dq,
+                        int32_t dv, float scale, int32_t n_chunks, int32_t order, const mla_rows* out,
+                        const mla_rows* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || H <= 0 || N < 0) return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, H > 0, N >= 0");
+  if (n_chunks < 1 || n_chunks > kMaxRingChunks)
+    return fail(MLA_ERR_INVALID_ARG, "n_chunks (%d) must lie in [1, %d]", n_chunks, kMaxRingChunks);
+  if (N % n_chunks) return fail(MLA_ERR_INVALID_ARG, "N (%lld) must be a multiple of n_chunks (%d)", (long long)N, n_chunks);
+  if (order != MLA_RING_ORDER && order != MLA_RING_BALANCED)
+    return fail(MLA_ERR_INVALID_ARG, "order (%d) must be MLA_RING_ORDER or MLA_RING_BALANCED", order);
+  if (dq != 576 || dv != kRingDv)
+    return fail(MLA_ERR_UNSUPPORTED, "the ring is built for dq = 576, dv = %d (got %d, %d)", kRingDv, dq, dv);
+  if (!q || !kv || !out || !lse) return fail(MLA_ERR_INVALID_ARG, "q, kv, out and lse must be given");
+  const size_t need = mla_ring_workspace_size(B, H, N, n_chunks);
+  if (need && !workspace) return fail(MLA_ERR_INVALID_ARG, "the ring needs a workspace of mla_ring_workspace_size() bytes");
+  if (need && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_INVALID_ARG, "workspace_bytes (%zu) is below mla_ring_workspace_size() (%zu)", workspace_bytes, need);
+  const int P = n_chunks;
+  const int64_t C = N / P;
+  int32_t launch_of[kMaxRingChunks * (kMaxRingChunks + 1) / 2];
+  const int n_launches = ring_schedule(P, order, launch_of);
+
+  // Views of every call (they must outlive the preparation below).  Query
+  // chunk r's running result between its calls: the float32 slice r of the
+  // workspace, [B, H, C, dv] contiguous.
+  const int n_calls = P * (P + 1) / 2;
+  std::vector<mla_rows> views(5 * (size_t)n_calls);
+  std::vector<mla_fwd_call> calls(n_calls);
+  std::vector<int> call_launch(n_calls);
+  std::vector<int> seen(P, 0);
+  auto shift = [](const mla_rows* r, int64_t t0, int elem) {
+    mla_rows v = *r;
+    if (v.data) v.data = static_cast<char*>(v.data) + t0 * r->stride_t * elem;
+    return v;
+  };
+  int ci = 0;
+  for (int L = 0; L < n_launches; ++L)
+    for (int r = 0; r < P; ++r)
+      for (int k = 0; k <= r; ++k) {
+        if (launch_of[r * (r + 1) / 2 + k] != L) continue;
+        const bool first = seen[r] == 0, last = seen[r] == r;  // query chunk r makes r + 1 calls
+        ++seen[r];
+        mla_rows* v = &views[5 * (size_t)ci];
+        v[0] = shift(q, r * C, 2);
+        v[1] = shift(kv, k * C, 2);
+        v[2] = shift(out, r * C, 2);
+        v[3] = shift(lse, r * C, 4);
+        float* carry_r = workspace ? static_cast<float*>(workspace) + (size_t)r * B * H * C * kRingDv : nullptr;
+        v[4] = mla_rows{carry_r, (int64_t)H * C * kRingDv, C * kRingDv, kRingDv};
+        mla_fwd_call& c = calls[ci];
+        c = mla_fwd_call{};
+        c.q = &v[0];
+        c.kv = &v[1];
+        c.B = B;
+        c.Hq = H;
+        c.Nq = C;
+        c.Nkv = C;
+        c.dq = dq;
+        c.dr = 0;
+        c.dv = dv;
+        c.scale = scale;
+        c.flags = MLA_CAUSAL | (last ? 0u : MLA_OUT_F32) | (first ? 0u : MLA_PREV_OUT_F32);
+        c.q_offset = r * C;
+        c.kv_offset = k * C;
+        c.prev_out = first ? nullptr : &v[4];
+        c.prev_lse = first ? nullptr : &v[3];
+        c.out = last ? &v[2] : &v[4];
+        c.lse = &v[3];
+        call_launch[ci] = L;
+        ++ci;
+      }
+  // Validate and prepare every group before anything is launched.
+  std::vector<mla::GroupParams> groups;
+  for (int L = 0, i = 0; L < n_launches; ++L) {
+    int j = i;
+    while (j < n_calls && call_launch[j] == L) ++j;
+    for (int g0 = i; g0 < j; g0 += MLA_MAX_GROUP) {
+      mla::GroupParams g;
+      if (mla_status st = prepare_group(std::min(MLA_MAX_GROUP, j - g0), &calls[g0], &g)) return st;
+      if (g.n) groups.push_back(g);
+    }
+    i = j;
+  }
+  for (const mla::GroupParams& g : groups)
+    if (mla_status st = hip_status(mla::launch_latent_group(g, static_cast<hipStream_t>(stream)), "ring launch"))
+      return st;
+  return MLA_OK;
 }
 
 mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a, const mla_rows* out_b,

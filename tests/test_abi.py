@@ -339,3 +339,75 @@ def test_generated_qk_chain_is_current():
     gen = os.path.join(ROOT, "ring_chunk_attention_amd", "csrc", "gen_qk_chain.py")
     r = subprocess.run(["python3", gen, "--check"], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+# ---------------------------------------------------------------------------
+# native ring driver (mla_ring_fwd, mla_ring_schedule)
+# ---------------------------------------------------------------------------
+def _balanced_reference(P):
+    """The balanced packing restated: each query chunk's full calls, longest
+    chains first, go to its r least-filled launches among the first P - 1
+    (ties: the earlier), the diagonals last."""
+    full = [[] for _ in range(max(P - 1, 0))]
+    for r in range(P - 1, 0, -1):
+        slots = sorted(sorted(range(P - 1), key=lambda j: (len(full[j]), j))[:r])
+        for k, j in enumerate(slots):
+            full[j].append((r, k))
+    return [l for l in full if l] + [[(r, r) for r in range(P)]]
+
+
+@pytest.mark.parametrize("P", range(1, 17))
+def test_native_balanced_schedule_matches_its_rule(P):
+    from ring_chunk_attention_amd import ring_schedule
+    got = [sorted(l) for l in ring_schedule(P, "balanced")]
+    want = [sorted(l) for l in _balanced_reference(P)]
+    assert got == want
+
+
+def call_ring(lib, q=None, kv=None, out=None, lse=None, B=1, H=16, N=4096, dq=576, dv=512, scale=0.072,
+              n_chunks=4, order=1, workspace=0x20000000, workspace_bytes=1 << 40):
+    from ring_chunk_attention_amd.binding import MlaRows
+    def conv(r):
+        return None if r is None else ctypes.byref(MlaRows(r.data, r.stride_b, r.stride_h, r.stride_t))
+    q = rows() if q is None else q
+    kv = rows() if kv is None else kv
+    out = rows(st=512) if out is None else out
+    lse = Rows(FAKE, 0, 4096, 1) if lse is None else lse
+    return lib.mla_ring_fwd(conv(q), conv(kv), B, H, N, dq, dv, scale, n_chunks, order, conv(out), conv(lse),
+                            workspace, workspace_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n_chunks=0), MLA_ERR_INVALID_ARG, "n_chunks"),
+    (dict(n_chunks=65), MLA_ERR_INVALID_ARG, "n_chunks"),
+    (dict(N=4095), MLA_ERR_INVALID_ARG, "multiple of n_chunks"),
+    (dict(order=2), MLA_ERR_INVALID_ARG, "order"),
+    (dict(dq=512), MLA_ERR_UNSUPPORTED, "dq = 576"),
+    (dict(H=0), MLA_ERR_INVALID_ARG, "sizes"),
+    (dict(workspace=None), MLA_ERR_INVALID_ARG, "needs a workspace"),
+    (dict(workspace=0x20000010), MLA_ERR_INVALID_ARG, "256-byte aligned"),
+    (dict(workspace_bytes=1024), MLA_ERR_INVALID_ARG, "mla_ring_workspace_size"),
+    (dict(scale=float("nan")), MLA_ERR_INVALID_ARG, "scale"),        # from the first call's checks
+    (dict(q=Rows(FAKE + 2, 0, 576, 576)), MLA_ERR_INVALID_ARG, "aligned"),
+])
+def test_ring_rejects_invalid_arguments(lib, kw, code, msg):
+    assert call_ring(lib, **kw) == code
+    assert msg in lib.mla_last_error().decode()
+
+
+def test_ring_workspace_size_and_empty_ring(lib):
+    assert lib.mla_ring_workspace_size(1, 16, 4096, 4) == 16 * 4096 * 512 * 4
+    assert lib.mla_ring_workspace_size(1, 16, 4096, 1) == 0
+    assert lib.mla_ring_workspace_size(1, 16, 4095, 4) == 0
+    # no rows: nothing is launched, and every view may be NULL
+    assert call_ring(lib, N=0, q=NULL_ROWS, kv=NULL_ROWS, out=NULL_ROWS, lse=NULL_ROWS, workspace=None,
+                     workspace_bytes=0) == MLA_OK
+
+
+def test_ring_schedule_rejects(lib):
+    arr = (ctypes.c_int32 * 10)()
+    n = ctypes.c_int32(0)
+    assert lib.mla_ring_schedule(4, 7, arr, ctypes.byref(n)) == MLA_ERR_INVALID_ARG
+    assert lib.mla_ring_schedule(0, 1, arr, ctypes.byref(n)) == MLA_ERR_INVALID_ARG
+    assert lib.mla_ring_schedule(4, 1, None, ctypes.byref(n)) == MLA_ERR_INVALID_ARG
+    assert lib.mla_ring_schedule(4, 1, arr, ctypes.byref(n)) == MLA_OK and n.value == 4
