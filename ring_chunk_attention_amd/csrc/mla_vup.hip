@@ -170,10 +170,12 @@ hipError_t launch_vup(const VupParams& p0, hipStream_t s) {
   VupParams p = p0;
   const int64_t nblk = ((int64_t)p.B * p.T + 31) / 32;
   if (nblk == 0 || p.H == 0) return hipSuccess;
-  // about two workgroups per CU over all heads, each with at least 16 row
-  // blocks (two per wave) so that the weight copy stays a small part
+  // about one workgroup per CU over all heads (a workgroup's 130 KB of LDS
+  // leaves room for one: a second round would stage every head's weight
+  // again; one round measured 2% faster than two), each with at least 16
+  // row blocks (two per wave) so that the weight copy stays a small part
   const int ncu = cu_count() > 0 ? cu_count() : 256;
-  int64_t parts = (2 * (int64_t)ncu + p.H - 1) / p.H;
+  int64_t parts = ((int64_t)ncu + p.H - 1) / p.H;
   parts = std::max<int64_t>(1, std::min<int64_t>(parts, (nblk + 15) / 16));
   p.blocks_per_part = (nblk + parts - 1) / parts;
   parts = (nblk + p.blocks_per_part - 1) / p.blocks_per_part;
