@@ -793,3 +793,20 @@ def test_ring_hip_graph_replays_match_eager(mla):
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
     assert report("graph ring O", host(out), o_ref) <= O_TOL
     assert report("graph ring LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_ring_two_batches_strided_q(mla):
+    """The native ring driver with B = 2 (batch strides through every chunk
+    view) and q a strided view (every other head of a larger tensor), both
+    schedules, against the unchunked oracle."""
+    c = W.dense_case(B=2, H=6, N=384, seed=98)
+    q_all = dev_bf16(c.q)
+    big = torch.zeros((2, 12, 384, 576), dtype=torch.bfloat16, device="cuda")
+    big[:, ::2] = q_all
+    q_view = big[:, ::2]                       # stride_h twice the contiguous one
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
+    for order in ("ring", "balanced"):
+        out, lse = mla.ring_fwd(q_view, dev_bf16(c.kv), 3, scale=c.scale, order=order)
+        torch.cuda.synchronize()
+        assert report(f"ring B=2 {order} O", host(out), o_ref) <= O_TOL
+        assert report(f"ring B=2 {order} LSE", host(lse), l_ref) <= LSE_TOL
