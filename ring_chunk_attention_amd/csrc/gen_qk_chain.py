@@ -206,7 +206,7 @@ def emit_function(name, with_softmax):
 # P.V MFMAs of tile t, their LDS reads, and the copies of tile t+3.
 # ---------------------------------------------------------------------------
 TS_NBUF = 4          # K fragment registers of the chain inside the step
-TS_BUDGET = 3.0      # VALU issue time per MFMA slot
+TS_BUDGET = 2.5      # VALU issue time per MFMA slot (3.0 and 3.5 measured ~0.5% slower)
 VFA, VFB = 216, 220  # the two V fragment tuples (v[216:219], v[220:223])
 N_PV = 32            # P.V MFMAs: 2 key halves x 4 value blocks x 4 row blocks
 
@@ -246,7 +246,7 @@ def ts_schedule(nslots):
     return step
 
 
-TS_COPY_EVERY = 2     # slots between the copies, from the start of the block
+TS_COPY_EVERY = 3     # slots between the copies, from the start of the block
 
 
 def ts_copy_slots(seq):
