@@ -205,6 +205,59 @@ def summarize_stats(folder, out_path, cmd):
     print("\n".join(lines))
 
 
+def summarize_counters(folders, kernel, out_path, cmds):
+    """Markdown summary of `rocprofv3 --pmc` csv runs (one folder per pass):
+    each counter's value summed over the dispatch's sampled units, for the last
+    dispatch of the kernel whose name contains `kernel`, and the ratios the
+    design cites (SIMD and CU busy fractions use the per-XCD GRBM_GUI_ACTIVE
+    as the clock count)."""
+    import csv
+    vals = {}
+    for folder in folders:
+        files = _csvs(folder, "counter_collection.csv")
+        if not files:
+            sys.exit(f"no *counter_collection.csv under {folder}")
+        per = {}
+        for r in csv.DictReader(open(files[0])):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if not per:
+            sys.exit(f"no dispatch of a kernel named like {kernel!r} in {folder}")
+        vals.update(per[max(per)])
+    lines = ["# Counters: " + os.path.basename(out_path).rsplit(".", 1)[0], "",
+             "Commands (from the repository root, on one MI355X; one pass each):", ""]
+    lines += ["    " + c for c in cmds]
+    lines += ["", f"Last dispatch of the kernel named like `{kernel}`; values summed over the units "
+              "rocprofv3 reports.", "", "| counter | value |", "|---|---:|"]
+    lines += [f"| `{k}` | {v:.4g} |" for k, v in sorted(vals.items())]
+    clk = vals.get("GRBM_GUI_ACTIVE", 0.0) / 8.0   # per XCD
+    derived = []
+    if clk:
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+            derived.append(("MFMA busy (per SIMD)", vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (clk * 1024)))
+        if "SQ_ACTIVE_INST_VALU" in vals:
+            derived.append(("VALU busy (per CU, 4-cycle issue)", vals["SQ_ACTIVE_INST_VALU"] / (clk * 256)))
+    if vals.get("SQ_WAVE_CYCLES"):
+        for k, label in (("SQ_WAIT_ANY", "waves waiting on a memory counter"),
+                         ("SQ_WAIT_INST_ANY", "waves waiting to issue")):
+            if k in vals:
+                derived.append((label, vals[k] / vals["SQ_WAVE_CYCLES"]))
+    if vals.get("TCC_HIT_sum") is not None and vals.get("TCC_MISS_sum"):
+        derived.append(("L2 hit rate", vals["TCC_HIT_sum"] / (vals["TCC_HIT_sum"] + vals["TCC_MISS_sum"])))
+    if vals.get("SQ_INSTS_MFMA"):
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
+            if k in vals:
+                derived.append((f"{k} per MFMA", vals[k] / vals["SQ_INSTS_MFMA"]))
+    if derived:
+        lines += ["", "| derived | value |", "|---|---:|"]
+        lines += [f"| {k} | {v:.3g} |" for k, v in derived]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _counter_means(folder, counter):
     """Mean value of `counter` per dispatch of each kernel (rocprofv3 csv)."""
     import csv
@@ -262,18 +315,26 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
+    ap.add_argument("--only-row", choices=["ring", "merge", "split", "sparse", "decode", "vup"],
+                    help="time this one row alone (no headline, no CPU baseline): for profiling a kernel")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one plain device copy of 1 GiB (HBM counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="write a markdown summary of a rocprofv3 --stats csv run to --out, then exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM traffic summary from FETCH_SIZE / WRITE_SIZE csv runs, then exit")
-    ap.add_argument("--out", help="output file of --summarize-stats")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="write a summary of rocprofv3 --pmc csv runs (one folder per pass) to --out, then exit")
+    ap.add_argument("--kernel", default="attn_fwd", help="kernel name substring for --summarize-counters")
+    ap.add_argument("--out", help="output file of --summarize-stats / --summarize-counters")
     ap.add_argument("--cmd", nargs="*", default=[],
                     help="the profiling command(s) the summary came from, recorded in it")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.out, " ".join(args.cmd))
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.kernel, args.out, args.cmd)
         return
     if args.summarize_traffic:
         cf, cw = (args.cmd + ["", ""])[:2]
@@ -290,6 +351,11 @@ def main():
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    if args.only_row:
+        rows = measure_rows(mla, W, to_dev, args.steps, args.warmup, only=args.only_row)
+        print(json.dumps({"row": args.only_row, **rows}), flush=True)
+        return
 
     print("bench: generating the DeepSeek-V3 prefill inputs", file=sys.stderr, flush=True)
     case = W.dsv3_prefill(0)
@@ -348,110 +414,121 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False):
+def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
     """Time the other steps of the path at their workload shapes."""
     import torch
     rows = {}
     steps = max(3, min(steps, 10))
 
-    # one-device ring: 16 heads, N = 4096 as 4 chunks of 1024, folds in place
-    print("bench: ring workload", file=sys.stderr, flush=True)
-    c = W.ring4(0)
-    q, kv = to_dev(c.q), to_dev(c.kv)
-    o = torch.empty((1, 16, 4096, 512), dtype=torch.bfloat16, device="cuda")
-    l = torch.empty((1, 16, 4096), dtype=torch.float32, device="cuda")
-    # balanced schedule (the default): full calls packed 2 + 2 + 2, then the
-    # 4 diagonals; ring order: 4 diagonals, then 3, 2 and 1 full calls
-    ms, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l), steps, warmup, per_launch=False)
-    ms_ring, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l, order="ring"),
-                                  steps, warmup, per_launch=False)
-    fl = 16 * causal_pairs(4096, 4096) * 2176
-    rows["ring_4x1024_h16"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
-                               "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-                               "calls": 10, "launches": 4, "folds_in_epilogue": 6,
-                               "schedule": "balanced", "ring_order_ms": round(ms_ring, 4)}
-    # the same workload unchunked, for the cost of chunking
-    ms1, _, _ = time_launches(lambda: mla.fwd(q, kv, scale=c.scale, out=o, lse=l), steps, warmup, per_launch=False)
-    rows["ring_4x1024_h16"]["unchunked_ms"] = round(ms1, 4)
-    # standalone merge of two [1, 16, 1024, 512] partials (HBM-bound)
-    a, b = o[:, :, :1024].contiguous(), o[:, :, 1024:2048].contiguous()
-    la, lb = l[:, :, :1024].contiguous(), l[:, :, 1024:2048].contiguous()
-    mo, ml = torch.empty_like(a), torch.empty_like(la)
-    ms, _, _ = time_launches(lambda: mla.merge(a, la, b, lb, out=mo, lse=ml), steps, warmup, hold=True,
-                             per_launch=False)
-    nbytes = 3 * a.numel() * 2 + 3 * la.numel() * 4
-    rows["merge_h16_1024x512"] = {"ms": round(ms, 4), "GBps": round(nbytes / ms / 1e6, 1),
-                                  "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
-    del q, kv, o, l, a, b, la, lb, mo, ml
+    if only in (None, "ring"):
+        # one-device ring: 16 heads, N = 4096 as 4 chunks of 1024, folds in place
+        print("bench: ring workload", file=sys.stderr, flush=True)
+        c = W.ring4(0)
+        q, kv = to_dev(c.q), to_dev(c.kv)
+        o = torch.empty((1, 16, 4096, 512), dtype=torch.bfloat16, device="cuda")
+        l = torch.empty((1, 16, 4096), dtype=torch.float32, device="cuda")
+        # balanced schedule (the default): full calls packed 2 + 2 + 2, then the
+        # 4 diagonals; ring order: 4 diagonals, then 3, 2 and 1 full calls
+        ms, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l), steps, warmup, per_launch=False)
+        ms_ring, _, _ = time_launches(lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l, order="ring"),
+                                      steps, warmup, per_launch=False)
+        fl = 16 * causal_pairs(4096, 4096) * 2176
+        rows["ring_4x1024_h16"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+                                   "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                                   "calls": 10, "launches": 4, "folds_in_epilogue": 6,
+                                   "schedule": "balanced", "ring_order_ms": round(ms_ring, 4)}
+        # the same workload unchunked, for the cost of chunking
+        ms1, _, _ = time_launches(lambda: mla.fwd(q, kv, scale=c.scale, out=o, lse=l), steps, warmup, per_launch=False)
+        rows["ring_4x1024_h16"]["unchunked_ms"] = round(ms1, 4)
+        del q, kv, o, l
+    if only in (None, "merge"):
+        # standalone merge of two [1, 16, 1024, 512] partials (HBM-bound): two
+        # chunks of the ring workload's result
+        c = W.ring4(0)
+        q, kv = to_dev(c.q), to_dev(c.kv)
+        o, l = mla.fwd(q, kv, scale=c.scale)
+        a, b = o[:, :, :1024].contiguous(), o[:, :, 1024:2048].contiguous()
+        la, lb = l[:, :, :1024].contiguous(), l[:, :, 1024:2048].contiguous()
+        mo, ml = torch.empty_like(a), torch.empty_like(la)
+        ms, _, _ = time_launches(lambda: mla.merge(a, la, b, lb, out=mo, lse=ml), steps, warmup, hold=True,
+                                 per_launch=False)
+        nbytes = 3 * a.numel() * 2 + 3 * la.numel() * 4
+        rows["merge_h16_1024x512"] = {"ms": round(ms, 4), "GBps": round(nbytes / ms / 1e6, 1),
+                                      "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+        del q, kv, o, l, a, b, la, lb, mo, ml
 
-    # split q/k varlen ring step: 8 sequences, 32 heads, prev fold
-    print("bench: split varlen workload", file=sys.stderr, flush=True)
-    c = W.split_ring_step(0)
-    args = [to_dev(x) for x in (c.q1, c.q2, c.k1, c.k2, c.v)]
-    sl = torch.from_numpy(c.seq_lens).cuda()
-    prev = (to_dev(c.prev_out), torch.from_numpy(c.prev_lse).cuda())
-    T = int(c.seq_lens.sum())
-    so = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
-    sL = torch.empty((32, T), dtype=torch.float32, device="cuda")
-    ms, _, _ = time_launches(lambda: mla.split_fwd(*args, scale=c.scale, seq_lens=sl, prev=prev,
-                                                   out=so, lse=sL), steps, warmup, per_launch=False)
-    fl = 32 * sum(causal_pairs(int(L), int(L)) for L in c.seq_lens) * (2 * 192 + 2 * 128)
-    rows["split_varlen_8seq_h32"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
-                                     "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-                                     "tokens": T}
-    del args, sl, prev, so, sL
+    if only in (None, "split"):
+        # split q/k varlen ring step: 8 sequences, 32 heads, prev fold
+        print("bench: split varlen workload", file=sys.stderr, flush=True)
+        c = W.split_ring_step(0)
+        args = [to_dev(x) for x in (c.q1, c.q2, c.k1, c.k2, c.v)]
+        sl = torch.from_numpy(c.seq_lens).cuda()
+        prev = (to_dev(c.prev_out), torch.from_numpy(c.prev_lse).cuda())
+        T = int(c.seq_lens.sum())
+        so = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
+        sL = torch.empty((32, T), dtype=torch.float32, device="cuda")
+        ms, _, _ = time_launches(lambda: mla.split_fwd(*args, scale=c.scale, seq_lens=sl, prev=prev,
+                                                       out=so, lse=sL), steps, warmup, per_launch=False)
+        fl = 32 * sum(causal_pairs(int(L), int(L)) for L in c.seq_lens) * (2 * 192 + 2 * 128)
+        rows["split_varlen_8seq_h32"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+                                         "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                                         "tokens": T}
+        del args, sl, prev, so, sL
 
-    # sparse top-k: 4096 queries x 128 heads x 2048 gathered rows
-    print("bench: sparse workload", file=sys.stderr, flush=True)
-    c = W.sparse_topk(0)
-    t = [to_dev(x) for x in (c.q_lift, c.q_pe, c.c_kv, c.k_pe)]
-    idx = torch.from_numpy(c.idx).cuda()
-    so = torch.empty((1, 4096, 128 * 512), dtype=torch.bfloat16, device="cuda")
-    sL = torch.empty((1, 4096, 128), dtype=torch.float32, device="cuda")
-    ms, _, _ = time_launches(lambda: mla.sparse_fwd(*t, idx, scale=c.scale, out=so, lse=sL), steps, warmup, per_launch=False)
-    fl = 4096 * 128 * 2048 * 2176
-    gathered = 4096 * 2048 * 1152
-    rows["sparse_topk_s4096_k2048_h128"] = {
-        "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
-        "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-        "gather_GBps": round(gathered / ms / 1e6, 1)}
-    del t, idx, so, sL
+    if only in (None, "sparse"):
+        # sparse top-k: 4096 queries x 128 heads x 2048 gathered rows
+        print("bench: sparse workload", file=sys.stderr, flush=True)
+        c = W.sparse_topk(0)
+        t = [to_dev(x) for x in (c.q_lift, c.q_pe, c.c_kv, c.k_pe)]
+        idx = torch.from_numpy(c.idx).cuda()
+        so = torch.empty((1, 4096, 128 * 512), dtype=torch.bfloat16, device="cuda")
+        sL = torch.empty((1, 4096, 128), dtype=torch.float32, device="cuda")
+        ms, _, _ = time_launches(lambda: mla.sparse_fwd(*t, idx, scale=c.scale, out=so, lse=sL), steps, warmup, per_launch=False)
+        fl = 4096 * 128 * 2048 * 2176
+        gathered = 4096 * 2048 * 1152
+        rows["sparse_topk_s4096_k2048_h128"] = {
+            "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+            "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "gather_GBps": round(gathered / ms / 1e6, 1)}
+        del t, idx, so, sL
 
-    # token generation: 64 sequences x 128 heads, 8192 cache rows each, the
-    # keys split across workgroups (4 ranges of 2048) and reduced through LSE
-    print("bench: decode workload", file=sys.stderr, flush=True)
-    c = W.dsv3_decode(0)
-    q, kv, lens = to_dev(c.q), to_dev(c.kv), torch.from_numpy(c.kv_lens).cuda()
-    B, H = c.q.shape[:2]
-    do = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
-    dl = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    ms, _, _ = time_launches(lambda: mla.decode_fwd(q, kv, scale=c.scale, kv_lens=lens, out=do, lse=dl),
-                             steps, warmup, per_launch=False)
-    keys = int(c.kv_lens.astype(np.int64).sum())
-    fl = H * keys * 2176
-    # algorithmic HBM bytes: each cache row once, the queries, outputs and LSEs
-    nbytes = keys * 576 * 2 + B * H * 576 * 2 + B * H * 512 * 2 + B * H * 4
-    rows["decode_b64_kv8192_h128"] = {
-        "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
-        "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-        "GBps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
-        "bytes": nbytes}
-    del q, kv, lens, do, dl
+    if only in (None, "decode"):
+        # token generation: 64 sequences x 128 heads, 8192 cache rows each, the
+        # keys split across workgroups (4 ranges of 2048) and reduced through LSE
+        print("bench: decode workload", file=sys.stderr, flush=True)
+        c = W.dsv3_decode(0)
+        q, kv, lens = to_dev(c.q), to_dev(c.kv), torch.from_numpy(c.kv_lens).cuda()
+        B, H = c.q.shape[:2]
+        do = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+        dl = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        ms, _, _ = time_launches(lambda: mla.decode_fwd(q, kv, scale=c.scale, kv_lens=lens, out=do, lse=dl),
+                                 steps, warmup, per_launch=False)
+        keys = int(c.kv_lens.astype(np.int64).sum())
+        fl = H * keys * 2176
+        # algorithmic HBM bytes: each cache row once, the queries, outputs and LSEs
+        nbytes = keys * 576 * 2 + B * H * 576 * 2 + B * H * 512 * 2 + B * H * 4
+        rows["decode_b64_kv8192_h128"] = {
+            "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+            "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "GBps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "bytes": nbytes}
+        del q, kv, lens, do, dl
 
-    # V-up projection of a prefill's latent output: [1, 128, 8192, 512] x
-    # per-head [128, 512] weights -> [8192, 128 * 128]; HBM-bound
-    print("bench: V-up workload", file=sys.stderr, flush=True)
-    c = W.dsv3_vup(0)
-    o, w = to_dev(c.o), to_dev(c.w_uv)
-    B, H, T, L = c.o.shape
-    vo = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
-    ms, _, _ = time_launches(lambda: mla.vup(o, w, out=vo), steps, warmup, per_launch=False)
-    fl = B * H * T * L * 128 * 2
-    nbytes = o.numel() * 2 + w.numel() * 2 + vo.numel() * 2   # each operand once
-    rows["vup_h128_t8192"] = {
-        "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
-        "GBps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
-        "bytes": nbytes}
+    if only in (None, "vup"):
+        # V-up projection of a prefill's latent output: [1, 128, 8192, 512] x
+        # per-head [128, 512] weights -> [8192, 128 * 128]; HBM-bound
+        print("bench: V-up workload", file=sys.stderr, flush=True)
+        c = W.dsv3_vup(0)
+        o, w = to_dev(c.o), to_dev(c.w_uv)
+        B, H, T, L = c.o.shape
+        vo = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
+        ms, _, _ = time_launches(lambda: mla.vup(o, w, out=vo), steps, warmup, per_launch=False)
+        fl = B * H * T * L * 128 * 2
+        nbytes = o.numel() * 2 + w.numel() * 2 + vo.numel() * 2   # each operand once
+        rows["vup_h128_t8192"] = {
+            "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+            "GBps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "bytes": nbytes}
     return rows
 
 
