@@ -205,10 +205,11 @@ mla_status mla_fwd_group(int32_t n, const mla_fwd_call* calls, void* stream /* h
  *
  * q [B, H, N, dq] and kv [B, 1, N, dq] (mla_rows views, the kv view's
  * stride_h ignored), dq = 576 (512 latent + 64 RoPE columns in one row),
- * value = the first dv = 512 columns of each kv row.  N must be a multiple
- * of n_chunks (1 .. 64); C = N / n_chunks.  Query chunk r attends each KV
- * chunk k <= r through one call equivalent to mla_fwd with q_offset = r*C
- * and kv_offset = k*C (so the diagonal chunk is causal, earlier ones full,
+ * value = the first dv = 512 columns of each kv row.  n_chunks: 1 .. 64;
+ * C = ceil(N / n_chunks), chunk r holds rows [r*C, min((r+1)*C, N)) (the last
+ * chunks may be shorter, or empty, when N is not a multiple: TT-NN ring_mla's
+ * logical length).  Query chunk r attends each KV chunk k <= r through one
+ * call equivalent to mla_fwd with q_offset = r*C and kv_offset = k*C (so the diagonal chunk is causal, earlier ones full,
  * later ones are never visited: their keys lie in the causal future), and
  * every call after a chunk's first folds into the running result.  The
  * running result between folds is float32, kept in the workspace; only each
@@ -231,8 +232,8 @@ mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_
                         const mla_rows* out, const mla_rows* lse,
                         void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
-/* Bytes of the workspace mla_ring_fwd needs: B*H*N*512*4 for n_chunks > 1,
- * 0 for one chunk or invalid sizes. */
+/* Bytes of the workspace mla_ring_fwd needs: B*H*n_chunks*C*512*4 with
+ * C = ceil(N / n_chunks) for n_chunks > 1; 0 for one chunk or invalid sizes. */
 size_t mla_ring_workspace_size(int32_t B, int32_t H, int64_t N, int32_t n_chunks);
 
 /*

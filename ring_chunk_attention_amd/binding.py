@@ -561,8 +561,9 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
              order: str = "balanced") -> Tuple[torch.Tensor, torch.Tensor]:
     """Causal shared-latent attention of q [B,H,N,576] over kv [B,1,N,576]
     processed as a ring of ``n_chunks`` contiguous chunks on one device
-    (mla_ring_fwd): query chunk r meets each KV chunk k <= r with global
-    offsets, and every call after the first folds into the running result
+    (mla_ring_fwd): chunks of ceil(N / n_chunks) rows (the last may be
+    shorter); query chunk r meets each KV chunk k <= r with global offsets,
+    and every call after the first folds into the running result
     (TensorRT-LLM mla.py forward_context_with_chunked_prefill; Ascend
     RingMLAOperation calcType).  ``order``: see ring_schedule.  ``carry``:
     the float32 running result between folds, any contiguous GPU tensor of at
@@ -570,8 +571,6 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
     if order not in _RING_ORDERS:
         raise ValueError(f"unknown ring schedule {order!r}")
     B, H, N, dq = q.shape
-    if N % n_chunks:
-        raise ValueError("sequence length must be a multiple of the chunk count")
     if out is None:
         out = torch.empty((B, H, N, head_dim_v), dtype=torch.bfloat16, device=q.device)
     if lse is None:

@@ -391,9 +391,10 @@ mla_status mla_ring_schedule(int32_t n_chunks, int32_t order, int32_t* launch_of
 }
 
 size_t mla_ring_workspace_size(int32_t B, int32_t H, int64_t N, int32_t n_chunks) {
-  if (B < 0 || H <= 0 || N < 0 || n_chunks < 1 || n_chunks > kMaxRingChunks || N % n_chunks) return 0;
+  if (B < 0 || H <= 0 || N < 0 || n_chunks < 1 || n_chunks > kMaxRingChunks) return 0;
   if (n_chunks == 1) return 0;
-  return (size_t)B * H * N * kRingDv * sizeof(float);
+  const int64_t C = (N + n_chunks - 1) / n_chunks;  // chunk length (the last may be shorter)
+  return (size_t)B * H * n_chunks * C * kRingDv * sizeof(float);
 }
 
 mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_t H, int64_t N, int32_t dq,
@@ -403,7 +404,6 @@ mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_
   if (B < 0 || H <= 0 || N < 0) return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, H > 0, N >= 0");
   if (n_chunks < 1 || n_chunks > kMaxRingChunks)
     return fail(MLA_ERR_INVALID_ARG, "n_chunks (%d) must lie in [1, %d]", n_chunks, kMaxRingChunks);
-  if (N % n_chunks) return fail(MLA_ERR_INVALID_ARG, "N (%lld) must be a multiple of n_chunks (%d)", (long long)N, n_chunks);
   if (order != MLA_RING_ORDER && order != MLA_RING_BALANCED)
     return fail(MLA_ERR_INVALID_ARG, "order (%d) must be MLA_RING_ORDER or MLA_RING_BALANCED", order);
   if (dq != 576 || dv != kRingDv)
@@ -416,7 +416,8 @@ mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_
   if (workspace_bytes < need)
     return fail(MLA_ERR_INVALID_ARG, "workspace_bytes (%zu) is below mla_ring_workspace_size() (%zu)", workspace_bytes, need);
   const int P = n_chunks;
-  const int64_t C = N / P;
+  const int64_t C = (N + P - 1) / P;  // chunk r holds rows [r C, min((r + 1) C, N))
+  auto len = [&](int r) { return std::max<int64_t>(0, std::min<int64_t>(C, N - r * C)); };
   int32_t launch_of[kMaxRingChunks * (kMaxRingChunks + 1) / 2];
   const int n_launches = ring_schedule(P, order, launch_of);
 
@@ -453,8 +454,8 @@ mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_
         c.kv = &v[1];
         c.B = B;
         c.Hq = H;
-        c.Nq = C;
-        c.Nkv = C;
+        c.Nq = len(r);
+        c.Nkv = len(k);
         c.dq = dq;
         c.dr = 0;
         c.dv = dv;

@@ -380,7 +380,6 @@ def call_ring(lib, q=None, kv=None, out=None, lse=None, B=1, H=16, N=4096, dq=57
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(n_chunks=0), MLA_ERR_INVALID_ARG, "n_chunks"),
     (dict(n_chunks=65), MLA_ERR_INVALID_ARG, "n_chunks"),
-    (dict(N=4095), MLA_ERR_INVALID_ARG, "multiple of n_chunks"),
     (dict(order=2), MLA_ERR_INVALID_ARG, "order"),
     (dict(dq=512), MLA_ERR_UNSUPPORTED, "dq = 576"),
     (dict(H=0), MLA_ERR_INVALID_ARG, "sizes"),
@@ -398,7 +397,8 @@ def test_ring_rejects_invalid_arguments(lib, kw, code, msg):
 def test_ring_workspace_size_and_empty_ring(lib):
     assert lib.mla_ring_workspace_size(1, 16, 4096, 4) == 16 * 4096 * 512 * 4
     assert lib.mla_ring_workspace_size(1, 16, 4096, 1) == 0
-    assert lib.mla_ring_workspace_size(1, 16, 4095, 4) == 0
+    # a ragged length: chunks of ceil(4095 / 4) = 1024 rows, the last 1023
+    assert lib.mla_ring_workspace_size(1, 16, 4095, 4) == 16 * 4 * 1024 * 512 * 4
     # no rows: nothing is launched, and every view may be NULL
     assert call_ring(lib, N=0, q=NULL_ROWS, kv=NULL_ROWS, out=NULL_ROWS, lse=NULL_ROWS, workspace=None,
                      workspace_bytes=0) == MLA_OK

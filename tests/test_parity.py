@@ -220,7 +220,9 @@ def test_merge_wide_rows_nan_side_and_empty_rows(mla):
 @pytest.mark.parametrize("order", ["ring", "balanced"])
 @pytest.mark.parametrize("H,N,P", [(4, 256, 4), (3, 192, 3), (2, 96, 1), (2, 640, 5),
                                    (2, 512, 8),       # 8 diagonals: two group launches
-                                   (2, 2048, 64)])    # the most chunks: 2080 calls in 64 launches
+                                   (2, 2048, 64),     # the most chunks: 2080 calls in 64 launches
+                                   (3, 250, 4),       # ragged: chunks of 63, the last 61
+                                   (2, 129, 8)])      # ragged: chunks of 17, the last 10
 def test_ring_small_equals_unchunked_oracle(mla, H, N, P, order):
     c = W.dense_case(B=1, H=H, N=N, seed=30 + P)
     out, lse = mla.ring_fwd(dev_bf16(c.q), dev_bf16(c.kv), P, scale=c.scale, order=order)
