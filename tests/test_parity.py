@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import LSE_TOL, O_TOL, dev, dev_bf16, host, report
+from gpu_util import LSE_TOL, O_TOL, dev, dev_bf16, host, report, report_o
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,7 @@ def test_tiny_config_full(mla):
     c = W.tiny(0)
     out, lse = _dense_gpu(mla, c)
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
-    assert report("tiny O", host(out), o_ref) <= O_TOL
+    assert report_o("tiny O", host(out), o_ref) <= 1.0
     assert report("tiny LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -60,7 +60,7 @@ def test_dense_ragged(mla, B, H, N, Nkv, q_off, kv_off, causal, seed):
     out, lse = _dense_gpu(mla, c)
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, causal=causal, q_offset=q_off,
                                     kv_offset=kv_off)
-    assert report("O", host(out), o_ref) <= O_TOL
+    assert report_o("O", host(out), o_ref) <= 1.0
     assert report("LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -89,7 +89,7 @@ def test_dense_fold_prev(mla):
     out, lse = _dense_gpu(mla, c, prev=(dev_bf16(prev_o), dev(prev_l)))
     fresh = oracle.dense_mla(c.q, c.kv, 512, c.scale, q_offset=0, kv_offset=32)
     o_ref, l_ref = oracle.merge(prev_o, prev_l, fresh[0], fresh[1])
-    assert report("fold O", host(out), o_ref) <= O_TOL
+    assert report_o("fold O", host(out), o_ref) <= 1.0
     assert report("fold LSE", host(lse), l_ref) <= LSE_TOL
     # rows 0..31 see no key (kv starts at 32): the previous values are kept bit
     # for bit, except row 5 whose previous LSE is -inf too, which gives (0, -inf)
@@ -110,7 +110,7 @@ def test_dense_fold_in_place(mla):
     torch.cuda.synchronize()
     fresh = oracle.dense_mla(c.q, c.kv, 512, c.scale)
     o_ref, l_ref = oracle.merge(prev_o, prev_l, fresh[0], fresh[1])
-    assert report("in-place O", host(o_t), o_ref) <= O_TOL
+    assert report_o("in-place O", host(o_t), o_ref) <= 1.0
     assert report("in-place LSE", host(l_t), l_ref) <= LSE_TOL
 
 
@@ -133,7 +133,7 @@ def test_dense_fp32_out_and_prev(mla):
     o2, l2 = mla.fwd(q, kv, scale=c.scale, prev=(dev(prev_o), dev(prev_l)))
     torch.cuda.synchronize()
     m_o, m_l = oracle.merge(prev_o, prev_l, o_ref, l_ref)
-    assert report("fp32 prev O", host(o2), m_o) <= O_TOL
+    assert report_o("fp32 prev O", host(o2), m_o) <= 1.0
     assert report("fp32 prev LSE", host(l2), m_l) <= LSE_TOL
 
 
@@ -155,7 +155,7 @@ def test_dsv3_full_size_sampled(mla):
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, rows=rows, heads=heads)
     o_got = host(out[:, heads][:, :, rows])
     l_got = host(lse[:, heads][:, :, rows])
-    assert report("dsv3 O", o_got, o_ref) <= O_TOL
+    assert report_o("dsv3 O", o_got, o_ref) <= 1.0
     assert report("dsv3 LSE", l_got, l_ref) <= LSE_TOL
     assert not torch.isnan(out).any() and torch.isfinite(lse).all()
 
@@ -174,7 +174,7 @@ def test_merge_kernel(mla):
     out, lse = mla.merge(dev_bf16(oa), dev(la), dev_bf16(ob), dev(lb))
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.merge(oa, la, ob, lb)
-    assert report("merge O", host(out), o_ref) <= O_TOL
+    assert report_o("merge O", host(out), o_ref) <= 1.0
     assert report("merge LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -188,7 +188,7 @@ def test_merge_in_place_dv128(mla):
     mla.merge(ta, tl, dev_bf16(ob), dev(lb), out=ta, lse=tl)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.merge(oa, la, ob, lb)
-    assert report("merge in place O", host(ta), o_ref) <= O_TOL
+    assert report_o("merge in place O", host(ta), o_ref) <= 1.0
     assert report("merge in place LSE", host(tl), l_ref) <= LSE_TOL
 
 
@@ -213,7 +213,7 @@ def test_merge_wide_rows_nan_side_and_empty_rows(mla):
     got_o, got_l = host(tb), host(tl)
     assert not np.isnan(got_o).any()
     assert (got_o[0, 0, 7:9] == 0).all() and np.isneginf(got_l[0, 0, 7:9]).all()
-    assert report("merge wide O", got_o, o_ref) <= O_TOL
+    assert report_o("merge wide O", got_o, o_ref) <= 1.0
     assert report("merge wide LSE", got_l, l_ref) <= LSE_TOL
 
 
@@ -228,7 +228,7 @@ def test_ring_small_equals_unchunked_oracle(mla, H, N, P, order):
     out, lse = mla.ring_fwd(dev_bf16(c.q), dev_bf16(c.kv), P, scale=c.scale, order=order)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
-    assert report("ring O", host(out), o_ref) <= O_TOL
+    assert report_o("ring O", host(out), o_ref) <= 1.0
     assert report("ring LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -243,7 +243,7 @@ def test_ring4_config_sampled(mla, order):
     heads = [0, 5, 10, 15]
     rows = np.array([0, 1, 511, 1023, 1024, 1025, 2047, 2048, 3071, 3072, 3073, 4094, 4095])
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, rows=rows, heads=heads)
-    assert report("ring4 O", host(out[:, heads][:, :, rows]), o_ref) <= O_TOL
+    assert report_o("ring4 O", host(out[:, heads][:, :, rows]), o_ref) <= 1.0
     assert report("ring4 LSE", host(lse[:, heads][:, :, rows]), l_ref) <= LSE_TOL
 
 
@@ -269,7 +269,7 @@ def test_split_small(mla, lens, H, Hkv, with_prev):
     o_ref, l_ref = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale,
                                     prev_out=c.prev_out if with_prev else None,
                                     prev_lse=c.prev_lse if with_prev else None)
-    assert report("split O", host(out), o_ref) <= O_TOL
+    assert report_o("split O", host(out), o_ref) <= 1.0
     assert report("split LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -289,9 +289,9 @@ def test_split_config_sampled(mla):
             k = np.concatenate([f(c.k1[t0:t0 + L, h]), f(c.k2[t0:t0 + L, h])], 1)
             o, l = oracle.attention(q, k, f(c.v[t0:t0 + L, h]), c.scale, True, rows, np.arange(L))
             o, l = oracle.merge(c.prev_out[t0 + rows, h], c.prev_lse[h, t0 + rows], o, l)
-            worst_o = max(worst_o, report(f"split s{s} h{h} O", host(out[t0 + rows, h]), o))
+            worst_o = max(worst_o, report_o(f"split s{s} h{h} O", host(out[t0 + rows, h]), o))
             worst_l = max(worst_l, report(f"split s{s} h{h} LSE", host(lse[h, t0 + rows]), l))
-    assert worst_o <= O_TOL and worst_l <= LSE_TOL
+    assert worst_o <= 1.0 and worst_l <= LSE_TOL
 
 
 # ---------------------------------------------------------------------------
@@ -312,7 +312,7 @@ def test_sparse_small(mla, H, K, seed):
     c = W.sparse_case(S=24, S_kv=max(3000, K + 100), pos0=max(2900, K + 50), H=H, K=K, seed=seed)
     out, lse = _sparse_gpu(mla, c)
     o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale)
-    assert report("sparse O", host(out), o_ref) <= O_TOL
+    assert report_o("sparse O", host(out), o_ref) <= 1.0
     assert report("sparse LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -326,7 +326,7 @@ def test_sparse_mx4_output_order(mla):
     o_nat, l_nat = mla.sparse_fwd(*args, scale=c.scale)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale)
-    assert report("mx4 O", host(o_mx), oracle.mx4_pack(o_ref, 512)) <= O_TOL
+    assert report_o("mx4 O", host(o_mx), oracle.mx4_pack(o_ref, 512)) <= 1.0
     assert report("mx4 LSE", host(l_mx), l_ref) <= LSE_TOL
     perm = oracle.mx4_pack(np.arange(512, dtype=np.float64), 512).astype(np.int64)
     nat = o_nat.view(torch.int16).view(1, 24, 128, 512).cpu().numpy()
@@ -345,7 +345,7 @@ def test_sparse_duplicates_and_invalid_indices(mla):
     idx[0, 3, :] = -1                        # nothing valid: O = 0, LSE = -inf
     out, lse = _sparse_gpu(mla, c, idx)
     o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, idx, c.scale)
-    assert report("sparse dup O", host(out), o_ref) <= O_TOL
+    assert report_o("sparse dup O", host(out), o_ref) <= 1.0
     assert report("sparse dup LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -386,7 +386,7 @@ def test_sparse_config_sampled(mla):
     out, lse = _sparse_gpu(mla, c)
     rows = [0, 1, 1000, 2047, 4094, 4095]
     o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale, rows=rows)
-    assert report("sparse cfg O", host(out[:, rows]), o_ref) <= O_TOL
+    assert report_o("sparse cfg O", host(out[:, rows]), o_ref) <= 1.0
     assert report("sparse cfg LSE", host(lse[:, rows]), l_ref) <= LSE_TOL
 
 
@@ -428,7 +428,7 @@ def test_dense_wide_range_second_pass(mla):
     assert _max_growth_log2(q64, k64, c.scale, vis) > 40.0
     out, lse = _dense_gpu(mla, c)
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
-    assert report("wide O", host(out), o_ref) <= O_TOL
+    assert report_o("wide O", host(out), o_ref) <= 1.0
     assert report("wide LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -444,7 +444,7 @@ def test_sparse_wide_range_second_pass(mla, K):
     assert _max_growth_log2(q64, k64, c.scale, np.ones((32, K), dtype=bool)) > 40.0
     out, lse = _sparse_gpu(mla, c)
     o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale)
-    assert report("wide sparse O", host(out), o_ref) <= O_TOL
+    assert report_o("wide sparse O", host(out), o_ref) <= 1.0
     assert report("wide sparse LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -459,7 +459,7 @@ def test_split_wide_range_second_pass(mla):
     out, lse = _split_gpu(mla, c, True)
     o_ref, l_ref = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale,
                                     prev_out=c.prev_out, prev_lse=c.prev_lse)
-    assert report("wide split O", host(out), o_ref) <= O_TOL
+    assert report_o("wide split O", host(out), o_ref) <= 1.0
     assert report("wide split LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -484,7 +484,7 @@ def test_dense_queue_bit_identical_to_launch_order(mla):
     b, heads, rows = 1, [0, 63], [0, 1000, 2047]
     for hh in heads:
         o_ref, l_ref = oracle.dense_mla(c.q[b:b + 1, hh:hh + 1], c.kv[b:b + 1], 512, c.scale, rows=rows)
-        assert report("queue O", host(o2[b:b + 1, hh:hh + 1, rows]), o_ref) <= O_TOL
+        assert report_o("queue O", host(o2[b:b + 1, hh:hh + 1, rows]), o_ref) <= 1.0
         assert report("queue LSE", host(l2[b:b + 1, hh:hh + 1, rows]), l_ref) <= LSE_TOL
 
 
@@ -519,7 +519,7 @@ def test_decode_small(mla, B, H, Nkv, lens, n_splits):
     c = W.decode_case(B=B, H=H, Nkv=Nkv, kv_lens=lens, seed=70 + B + Nkv)
     out, lse = _decode_gpu(mla, c, n_splits=n_splits)
     o_ref, l_ref = oracle.decode_mla(c.q, c.kv, c.kv_lens, 512, c.scale)
-    assert report("decode O", host(out), o_ref) <= O_TOL
+    assert report_o("decode O", host(out), o_ref) <= 1.0
     assert report("decode LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -544,7 +544,7 @@ def test_decode_config_sampled(mla):
     out, lse = _decode_gpu(mla, c)
     seqs = [0, 31, 63]
     o_ref, l_ref = oracle.decode_mla(c.q[seqs], c.kv[seqs], c.kv_lens[seqs], 512, c.scale)
-    assert report("decode cfg O", host(out[seqs]), o_ref) <= O_TOL
+    assert report_o("decode cfg O", host(out[seqs]), o_ref) <= 1.0
     assert report("decode cfg LSE", host(lse[seqs]), l_ref) <= LSE_TOL
 
 
@@ -611,7 +611,7 @@ def test_decode_indexed_cache_slots(mla):
                               kv_slots=dev(slots))
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.decode_mla(q, kv, lens, 512, W.SCALE_192, kv_slots=slots)
-    assert report("slots O", host(out), o_ref) <= O_TOL
+    assert report_o("slots O", host(out), o_ref) <= 1.0
     assert report("slots LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -650,7 +650,7 @@ def test_dense_valid_lens_padded_batch(mla, B, H, N, lens, seed):
         n = min(n, N)
         if n:
             o_ref, l_ref = oracle.dense_mla(c.q[b:b + 1, :, :n], c.kv[b:b + 1, :, :n], 512, c.scale)
-            assert report(f"b{b} O", o[b:b + 1, :, :n], o_ref) <= O_TOL
+            assert report_o(f"b{b} O", o[b:b + 1, :, :n], o_ref) <= 1.0
             assert report(f"b{b} LSE", l[b:b + 1, :, :n], l_ref) <= LSE_TOL
         assert np.all(o[b, :, n:] == 7.0) and np.all(l[b, :, n:] == 7.0)
 
@@ -759,7 +759,7 @@ def test_decode_longest_cache(mla):
     out, lse = mla.decode_fwd(dev_bf16(c.q), dev_bf16(c.kv), scale=c.scale, kv_lens=dev(c.kv_lens))
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.decode_mla(c.q, c.kv, c.kv_lens, 512, c.scale)
-    assert report("decode 131072 O", host(out), o_ref) <= O_TOL
+    assert report_o("decode 131072 O", host(out), o_ref) <= 1.0
     assert report("decode 131072 LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -793,7 +793,7 @@ def test_ring_hip_graph_replays_match_eager(mla):
         assert torch.equal(out, o_eager), f"replay {rep}: O differs from eager"
         assert torch.equal(lse, l_eager), f"replay {rep}: LSE differs from eager"
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
-    assert report("graph ring O", host(out), o_ref) <= O_TOL
+    assert report_o("graph ring O", host(out), o_ref) <= 1.0
     assert report("graph ring LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -810,5 +810,55 @@ def test_ring_two_batches_strided_q(mla):
     for order in ("ring", "balanced"):
         out, lse = mla.ring_fwd(q_view, dev_bf16(c.kv), 3, scale=c.scale, order=order)
         torch.cuda.synchronize()
-        assert report(f"ring B=2 {order} O", host(out), o_ref) <= O_TOL
+        assert report_o(f"ring B=2 {order} O", host(out), o_ref) <= 1.0
         assert report(f"ring B=2 {order} LSE", host(lse), l_ref) <= LSE_TOL
+
+
+# ---------------------------------------------------------------------------
+# randomized shapes (fixed seeds): every form against the oracle
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_all_forms(mla, seed):
+    """Random sizes, offsets, masks, head groupings, sequence lengths (zero
+    included), prev folds and decode valid lengths, drawn from a fixed seed:
+    the dense, sparse, split and decode forms against the oracle."""
+    r = np.random.default_rng(1000 + seed)
+    # dense: batches, heads, query and key counts, offsets, mask
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 10))
+    N, Nkv = int(r.integers(1, 300)), int(r.integers(1, 400))
+    causal = bool(r.integers(0, 2))
+    qo, ko = int(r.integers(0, 300)), int(r.integers(0, 200))
+    c = W.dense_case(B=B, H=H, N=N, Nkv=Nkv, seed=seed, causal=causal, q_offset=qo, kv_offset=ko)
+    o, l = mla.fwd(dev_bf16(c.q), dev_bf16(c.kv), scale=c.scale, causal=causal, q_offset=qo, kv_offset=ko)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, causal=causal, q_offset=qo, kv_offset=ko)
+    assert report_o("random dense O", host(o), o_ref) <= 1.0
+    assert report("random dense LSE", host(l), l_ref) <= LSE_TOL
+    # sparse: queries, list length, heads
+    S, K, Hs = int(r.integers(1, 20)), int(r.integers(1, 700)), int(r.integers(1, 129))
+    cs = W.sparse_case(S=S, S_kv=K + 200, pos0=K + 50, H=Hs, K=K, seed=seed)
+    o, l = _sparse_gpu(mla, cs)
+    o_ref, l_ref = oracle.sparse_mla(cs.q_lift, cs.q_pe, cs.c_kv, cs.k_pe, cs.idx, cs.scale)
+    assert report_o("random sparse O", host(o), o_ref) <= 1.0
+    assert report("random sparse LSE", host(l), l_ref) <= LSE_TOL
+    # split: sequence lengths (zero allowed), head grouping, prev fold
+    lens = [int(x) for x in r.integers(0, 300, int(r.integers(1, 5)))]
+    if sum(lens) == 0:
+        lens[0] = 1
+    Hsp = int(r.choice([2, 4, 8]))
+    Hkv = int(r.choice([h for h in (1, 2, Hsp) if Hsp % h == 0]))
+    cp = W.split_case(seq_lens=lens, H=Hsp, Hkv=Hkv, seed=seed, with_prev=bool(r.integers(0, 2)))
+    o, l = _split_gpu(mla, cp)
+    o_ref, l_ref = oracle.split_mla(cp.q1, cp.q2, cp.k1, cp.k2, cp.v, cp.seq_lens, cp.scale, causal=True,
+                                    prev_out=cp.prev_out, prev_lse=cp.prev_lse)
+    assert report_o("random split O", host(o), o_ref) <= 1.0
+    assert report("random split LSE", host(l), l_ref) <= LSE_TOL
+    # decode: sequences, heads, cache rows, valid lengths (zero allowed)
+    Bd, Hd, Nd = int(r.integers(1, 6)), int(r.integers(1, 129)), int(r.integers(1, 5000))
+    kl = [int(x) for x in r.integers(0, Nd + 1, Bd)]
+    cd = W.decode_case(B=Bd, H=Hd, Nkv=Nd, kv_lens=kl, seed=seed)
+    o, l = mla.decode_fwd(dev_bf16(cd.q), dev_bf16(cd.kv), scale=cd.scale, kv_lens=dev(cd.kv_lens))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode_mla(cd.q, cd.kv, cd.kv_lens, 512, cd.scale)
+    assert report_o("random decode O", host(o), o_ref) <= 1.0
+    assert report("random decode LSE", host(l), l_ref) <= LSE_TOL
