@@ -233,7 +233,9 @@ mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_
                         void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
 /* Bytes of the workspace mla_ring_fwd needs: B*H*n_chunks*C*512*4 with
- * C = ceil(N / n_chunks) for n_chunks > 1; 0 for one chunk or invalid sizes. */
+ * C = ceil(N / n_chunks) for n_chunks > 1; 0 for one chunk or invalid sizes;
+ * SIZE_MAX when the product overflows (mla_ring_fwd then fails with
+ * MLA_ERR_UNSUPPORTED). */
 size_t mla_ring_workspace_size(int32_t B, int32_t H, int64_t N, int32_t n_chunks);
 
 /*

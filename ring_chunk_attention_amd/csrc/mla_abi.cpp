@@ -7,8 +7,10 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -147,6 +149,15 @@ bool same_view(const mla_rows* a, const mla_rows* b) {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int64_t kMaxGrid = 0x7fffffff;
 
+// The product of non-negative sizes is at most kMaxGrid, with no overflow on
+// the way (sizes come from the caller and may be anything).
+bool fits_grid(std::initializer_list<int64_t> factors) {
+  int64_t prod = 1;
+  for (int64_t f : factors)
+    if (__builtin_mul_overflow(prod, f, &prod)) return false;
+  return prod <= kMaxGrid;
+}
+
 }  // namespace
 
 namespace {
@@ -253,16 +264,18 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
       p.kb.p = p.ka.p ? p.ka.p + (dq - 64) : nullptr;
       p.da = dq - 64;
     }
-    const int64_t n_qblk = (Nq + 31) / 32, n_hgrp = (Hq + 3) / 4;
-    if (n_qblk * n_hgrp * B > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+    const int64_t n_qblk = Nq / 32 + (Nq % 32 != 0), n_hgrp = (Hq + 3) / 4;
+    if (!fits_grid({n_qblk, n_hgrp, B})) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
     p.n_qblk = (int32_t)n_qblk;
     p.n_hgrp = (int32_t)n_hgrp;
     *form = Nq == 0 || B == 0 ? FORM_EMPTY : FORM_LATENT;
     return MLA_OK;
   }
   if (split) {
-    const int64_t qb = seq_lens ? (Nq + 127) / 128 + n_seqs : (Nq + 127) / 128 * B;
-    if (qb * Hq > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+    const int64_t nb = Nq / 128 + (Nq % 128 != 0);
+    if (!fits_grid({nb, B})) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+    const int64_t qb = seq_lens ? nb + n_seqs : nb * B;
+    if (!fits_grid({qb, Hq})) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
     *form = Nq == 0 || B == 0 ? FORM_EMPTY : FORM_SPLIT;
     return MLA_OK;
   }
@@ -393,8 +406,11 @@ mla_status mla_ring_schedule(int32_t n_chunks, int32_t order, int32_t* launch_of
 size_t mla_ring_workspace_size(int32_t B, int32_t H, int64_t N, int32_t n_chunks) {
   if (B < 0 || H <= 0 || N < 0 || n_chunks < 1 || n_chunks > kMaxRingChunks) return 0;
   if (n_chunks == 1) return 0;
-  const int64_t C = (N + n_chunks - 1) / n_chunks;  // chunk length (the last may be shorter)
-  return (size_t)B * H * n_chunks * C * kRingDv * sizeof(float);
+  const uint64_t C = (uint64_t)N / n_chunks + ((uint64_t)N % n_chunks != 0);  // chunk length (the last may be shorter)
+  uint64_t bytes = (uint64_t)B;
+  for (uint64_t f : {(uint64_t)H, (uint64_t)n_chunks, C, (uint64_t)kRingDv, (uint64_t)sizeof(float)})
+    if (__builtin_mul_overflow(bytes, f, &bytes)) return SIZE_MAX;  // no buffer can be that large
+  return (size_t)bytes;
 }
 
 mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_t H, int64_t N, int32_t dq,
@@ -413,6 +429,7 @@ mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_
   if (need && !workspace) return fail(MLA_ERR_INVALID_ARG, "the ring needs a workspace of mla_ring_workspace_size() bytes");
   if (need && (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (need == SIZE_MAX) return fail(MLA_ERR_UNSUPPORTED, "the ring's workspace size overflows (N = %lld)", (long long)N);
   if (workspace_bytes < need)
     return fail(MLA_ERR_INVALID_ARG, "workspace_bytes (%zu) is below mla_ring_workspace_size() (%zu)", workspace_bytes, need);
   const int P = n_chunks;
@@ -506,8 +523,7 @@ mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a, const mla
     return fail(MLA_ERR_INVALID_ARG, "out may alias out_a/out_b only as the identical view");
   if (lse && ((lse->data == lse_a->data && !same_view(lse, lse_a)) || (lse->data == lse_b->data && !same_view(lse, lse_b))))
     return fail(MLA_ERR_INVALID_ARG, "lse may alias lse_a/lse_b only as the identical view");
-  const int64_t rows = (int64_t)B * H * N;
-  if ((rows + 3) / 4 > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (!fits_grid({B, H, N / 4 + (N % 4 != 0)})) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
   mla::MergeParams p{};
   p.oa = rc(out_a);
   p.ob = rc(out_b);
@@ -548,7 +564,7 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
   if (lse && (st = check_lse(lse, "lse", no_q))) return st;
   if (no_q) return MLA_OK;
   if ((int64_t)B * S > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
-  if (S_kv * c_kv->stride_t * 2 > kMaxGrid || S_kv * k_pe->stride_t * 2 > kMaxGrid)
+  if (!fits_grid({S_kv, c_kv->stride_t, 2}) || !fits_grid({S_kv, k_pe->stride_t, 2}))
     return fail(MLA_ERR_UNSUPPORTED, "one batch of the cache must span less than 2 GiB (row offsets are 32-bit)");
   mla::AttnParams p{};
   p.qa = rc(q_lift);
@@ -612,7 +628,7 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_r
     return fail(MLA_ERR_INVALID_ARG, "kv_slots must be 4-byte aligned");
   if (kv_slots ? n_slots <= 0 : n_slots != 0 && n_slots < B)
     return fail(MLA_ERR_INVALID_ARG, "n_slots: need n_slots > 0 with kv_slots, else 0 or at least B");
-  if (Nkv * kv->stride_t * 2 > kMaxGrid || (k_rope && Nkv * k_rope->stride_t * 2 > kMaxGrid))
+  if (!fits_grid({Nkv, kv->stride_t, 2}) || (k_rope && !fits_grid({Nkv, k_rope->stride_t, 2})))
     return fail(MLA_ERR_UNSUPPORTED, "one sequence of the cache must span less than 2 GiB (row offsets are 32-bit)");
   int32_t S = 0, chunk = 0;
   if (!decode_split(B, Nkv, n_splits, &S, &chunk))
@@ -715,7 +731,7 @@ mla_status mla_debug_gather(const mla_rows* c_kv, const mla_rows* k_pe, const in
   if ((st = check_rows(c_kv, "c_kv", false)) || (st = check_rows(k_pe, "k_pe", false))) return st;
   if (!idx || (reinterpret_cast<uintptr_t>(idx) & 3u)) return fail(MLA_ERR_INVALID_ARG, "idx: missing or misaligned");
   if (!rows_out || !aligned16(rows_out)) return fail(MLA_ERR_INVALID_ARG, "rows_out: missing or not 16-byte aligned");
-  if (S_kv * c_kv->stride_t * 2 > kMaxGrid || S_kv * k_pe->stride_t * 2 > kMaxGrid)
+  if (!fits_grid({S_kv, c_kv->stride_t, 2}) || !fits_grid({S_kv, k_pe->stride_t, 2}))
     return fail(MLA_ERR_UNSUPPORTED, "one batch of the cache must span less than 2 GiB (row offsets are 32-bit)");
   mla::GatherParams p{};
   p.ka = rc(c_kv);

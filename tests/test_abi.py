@@ -411,3 +411,20 @@ def test_ring_schedule_rejects(lib):
     assert lib.mla_ring_schedule(0, 1, arr, ctypes.byref(n)) == MLA_ERR_INVALID_ARG
     assert lib.mla_ring_schedule(4, 1, None, ctypes.byref(n)) == MLA_ERR_INVALID_ARG
     assert lib.mla_ring_schedule(4, 1, arr, ctypes.byref(n)) == MLA_OK and n.value == 4
+
+
+def test_sizes_whose_products_overflow_are_rejected(lib):
+    """Row counts near the int64 range make the grid and workspace products
+    wrap; validation must still refuse them rather than pass a wrapped size."""
+    from ring_chunk_attention_amd.binding import MlaRows
+    big = 1 << 62
+    assert lib.mla_ring_workspace_size(1 << 30, 1 << 30, big, 2) == (1 << 64) - 1
+    assert call_ring(lib, N=big, workspace_bytes=1 << 40) == MLA_ERR_UNSUPPORTED
+    assert "overflows" in lib.mla_last_error().decode()
+    st = call_fwd(lib, B=1 << 30, Nq=big, Nkv=big, lse=Rows(FAKE + (1 << 20), 0, 0, 1))
+    assert st == MLA_ERR_UNSUPPORTED and "too large" in lib.mla_last_error().decode()
+    a, b, o = (MlaRows(FAKE + i * (1 << 24), 0, 512, 512) for i in range(3))
+    la, lb, lo = (MlaRows(FAKE + (3 + i) * (1 << 24), 0, 0, 1) for i in range(3))
+    st = lib.mla_merge_lse(ctypes.byref(a), ctypes.byref(la), ctypes.byref(b), ctypes.byref(lb),
+                           1 << 30, 128, big, 512, ctypes.byref(o), ctypes.byref(lo), None)
+    assert st == MLA_ERR_UNSUPPORTED and "too large" in lib.mla_last_error().decode()
