@@ -563,7 +563,7 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
     return fail(MLA_ERR_INVALID_ARG, "topk_idx: missing or not 4-byte aligned");
   if (lse && (st = check_lse(lse, "lse", no_q))) return st;
   if (no_q) return MLA_OK;
-  if ((int64_t)B * S > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (!fits_grid({B, S})) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
   if (!fits_grid({S_kv, c_kv->stride_t, 2}) || !fits_grid({S_kv, k_pe->stride_t, 2}))
     return fail(MLA_ERR_UNSUPPORTED, "one batch of the cache must span less than 2 GiB (row offsets are 32-bit)");
   mla::AttnParams p{};

@@ -428,3 +428,13 @@ def test_sizes_whose_products_overflow_are_rejected(lib):
     st = lib.mla_merge_lse(ctypes.byref(a), ctypes.byref(la), ctypes.byref(b), ctypes.byref(lb),
                            1 << 30, 128, big, 512, ctypes.byref(o), ctypes.byref(lo), None)
     assert st == MLA_ERR_UNSUPPORTED and "too large" in lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("B,S,S_kv,msg", [(1 << 30, 1 << 40, 1024, "too large"),
+                                          (1, 16, 1 << 62, "2 GiB")])
+def test_sparse_sizes_whose_products_overflow_are_rejected(lib, B, S, S_kv, msg):
+    from ring_chunk_attention_amd.binding import MlaRows
+    q, qp, ckv, kpe, o = (MlaRows(FAKE + i * (1 << 24), 0, 512, 512) for i in range(5))
+    st = lib.mla_sparse_fwd(ctypes.byref(q), ctypes.byref(qp), ctypes.byref(ckv), ctypes.byref(kpe), FAKE,
+                            B, S, S_kv, 128, 512, 64, 128, 0.07, 0, ctypes.byref(o), None, None, 0, None)
+    assert st == MLA_ERR_UNSUPPORTED and msg in lib.mla_last_error().decode()
