@@ -113,7 +113,8 @@ def _load():
 LIB = _load()
 LIB_PATH = _LIB_PATH
 
-EXPORTS = ("mla_fwd", "mla_fwd_group", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd", "mla_vup",
+EXPORTS = ("mla_fwd", "mla_fwd_group", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd",
+           "mla_vup",
            "mla_debug_gather", "mla_last_error", "mla_version", "mla_workspace_size", "mla_decode_workspace_size",
            "mla_ring_fwd", "mla_ring_workspace_size", "mla_ring_schedule")
 
@@ -145,6 +146,16 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
         raise ValueError(f"{name}: must be a GPU tensor")
 
 
+def _shape(t: torch.Tensor, name: str, shape: Tuple[int, ...], device: torch.device) -> None:
+    """The library sees only pointers and the sizes passed beside them, so a
+    tensor whose shape or device does not match those sizes would be read or
+    written out of bounds: such a call is refused here, before the ABI."""
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: expected shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device} (all tensors of a call on one device)")
+
+
 def _rows_bhtd(t: torch.Tensor, name: str, dtype: torch.dtype = torch.bfloat16) -> MlaRows:
     """[B, H, T, D] (inner dim contiguous) -> view."""
     _need(t, name, dtype)
@@ -153,9 +164,9 @@ def _rows_bhtd(t: torch.Tensor, name: str, dtype: torch.dtype = torch.bfloat16) 
     return MlaRows(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
-def _rows_thd(t: torch.Tensor, name: str) -> MlaRows:
+def _rows_thd(t: torch.Tensor, name: str, dtype: torch.dtype = torch.bfloat16) -> MlaRows:
     """[T, H, D] (tokens outermost) -> view with b = 0."""
-    _need(t, name, torch.bfloat16)
+    _need(t, name, dtype)
     if t.dim() != 3 or t.stride(2) != 1:
         raise ValueError(f"{name}: expected [T, H, D] with a contiguous last dim")
     return MlaRows(t.data_ptr(), 0, t.stride(1), t.stride(0))
@@ -214,14 +225,38 @@ def _workspace(device: torch.device, workspace) -> Tuple[Optional[int], int]:
 def _fwd_args(q, kv, scale, head_dim_v, causal, q_offset, kv_offset, q_rope, k_rope, v, prev, out,
               lse, want_lse):
     """Views and sizes of one mla_fwd call (outputs allocated if not given)."""
+    for t, n in ((q, "q"), (kv, "kv")):
+        _need(t, n, torch.bfloat16)
+        if t.dim() != 4:
+            raise ValueError(f"{n}: expected [B, H, N, D]")
     B, Hq, Nq, dq = q.shape
-    _, Hkv, Nkv, _ = kv.shape
+    Hkv, Nkv = kv.shape[1], kv.shape[2]
+    dev_ = q.device
+    _shape(kv, "kv", (B, Hkv, Nkv, dq), dev_)
+    if (q_rope is None) != (k_rope is None):
+        raise ValueError("q_rope and k_rope: give both or neither")
     dr = 0 if q_rope is None else q_rope.shape[-1]
+    if q_rope is not None:
+        _need(q_rope, "q_rope", torch.bfloat16)
+        _need(k_rope, "k_rope", torch.bfloat16)
+        _shape(q_rope, "q_rope", (B, Hq, Nq, dr), dev_)
+        _shape(k_rope, "k_rope", (B, Hkv, Nkv, dr), dev_)
     dv = head_dim_v if v is None else v.shape[-1]
+    if v is not None:
+        _need(v, "v", torch.bfloat16)
+        _shape(v, "v", (B, Hkv, Nkv, dv), dev_)
     if out is None:
-        out = torch.empty((B, Hq, Nq, dv), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, Hq, Nq, dv), dtype=torch.bfloat16, device=dev_)
     if lse is None and (want_lse or prev is not None):
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev_)
+    _shape(out, "out", (B, Hq, Nq, dv), dev_)
+    if lse is not None:
+        _shape(lse, "lse", (B, Hq, Nq), dev_)
+    if prev is not None:
+        if len(prev) != 2:
+            raise ValueError("prev: expected (prev_out, prev_lse)")
+        _shape(prev[0], "prev_out", (B, Hq, Nq, dv), dev_)
+        _shape(prev[1], "prev_lse", (B, Hq, Nq), dev_)
     out_f32 = out.dtype == torch.float32
     prev_f32 = prev is not None and prev[0].dtype == torch.float32
     a = dict(
@@ -270,8 +305,10 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 51
     lens_ptr, flags = None, a["flags"]
     if valid_lens is not None:
         _need(valid_lens, "valid_lens", torch.int32)
-        if valid_lens.shape != (a["B"],) or not valid_lens.is_contiguous():
+        if tuple(valid_lens.shape) != (a["B"],) or not valid_lens.is_contiguous():
             raise ValueError("valid_lens: expected a contiguous [B] tensor")
+        if valid_lens.device != q.device:
+            raise ValueError(f"valid_lens: on {valid_lens.device}, expected {q.device}")
         lens_ptr, flags = valid_lens.data_ptr(), flags | MLA_VALID_LENS
     _check(LIB.mla_fwd(ctypes.byref(a["q"]), _ref(a["q_rope"]), ctypes.byref(a["kv"]), _ref(a["k_rope"]),
                        _ref(a["v"]), a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["dq"], a["dr"], a["dv"],
@@ -323,32 +360,58 @@ def split_fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Te
     RingMLAOperation layout): q1 [T, H, 128], q2 [T, H, 64], k1 [T, Hkv, 128],
     k2 [T, Hkv, 64], v [T, Hkv, 128]; seq_lens int32 [batch] on the GPU;
     prev = (prev_out [T, H, 128], prev_lse [H, T]).  Returns out [T, H, 128]
-    and lse [H, T].  ``workspace`` as for fwd."""
+    and lse [H, T].  ``out`` and ``prev_out`` may be float32 tensors (their
+    dtype selects MLA_OUT_F32 / MLA_PREV_OUT_F32).  ``workspace`` as for
+    fwd."""
+    for t, n in ((q1, "q1"), (q2, "q2"), (k1, "k1"), (k2, "k2"), (v, "v")):
+        _need(t, n, torch.bfloat16)
+        if t.dim() != 3:
+            raise ValueError(f"{n}: expected [T, H, D]")
     T, H, dq = q1.shape
     Hkv = k1.shape[1]
     dr = q2.shape[2]
     dv = v.shape[2]
+    dev_ = q1.device
+    _shape(q2, "q2", (T, H, dr), dev_)
+    _shape(k1, "k1", (T, Hkv, dq), dev_)
+    _shape(k2, "k2", (T, Hkv, dr), dev_)
+    _shape(v, "v", (T, Hkv, dv), dev_)
     if out is None:
-        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=q1.device)
+        out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev_)
     if lse is None:
-        lse = torch.empty((H, T), dtype=torch.float32, device=q1.device)
+        lse = torch.empty((H, T), dtype=torch.float32, device=dev_)
+    _shape(out, "out", (T, H, dv), dev_)
+    _shape(lse, "lse", (H, T), dev_)
     if seq_lens is not None:
         _need(seq_lens, "seq_lens", torch.int32)
         if seq_lens.dim() != 1 or not seq_lens.is_contiguous():
             raise ValueError("seq_lens: expected a contiguous [batch] tensor")
+        if seq_lens.device != dev_:
+            raise ValueError(f"seq_lens: on {seq_lens.device}, expected {dev_}")
+    out_f32 = out.dtype == torch.float32
+    prev_f32 = prev is not None and prev[0].dtype == torch.float32
     views = [_rows_thd(q1, "q1"), _rows_thd(q2, "q2"), _rows_thd(k1, "k1"), _rows_thd(k2, "k2"),
              _rows_thd(v, "v")]
-    vpo = _rows_thd(prev[0], "prev_out") if prev is not None else None
-    vpl = _lse_ht(prev[1], "prev_lse") if prev is not None else None
-    vout, vl = _rows_thd(out, "out"), _lse_ht(lse, "lse")
+    vpo = vpl = None
+    if prev is not None:
+        if len(prev) != 2:
+            raise ValueError("prev: expected (prev_out, prev_lse)")
+        _shape(prev[0], "prev_out", (T, H, dv), dev_)
+        _shape(prev[1], "prev_lse", (H, T), dev_)
+        vpo = _rows_thd(prev[0], "prev_out", torch.float32 if prev_f32 else torch.bfloat16)
+        vpl = _lse_ht(prev[1], "prev_lse")
+    vout = _rows_thd(out, "out", torch.float32 if out_f32 else torch.bfloat16)
+    vl = _lse_ht(lse, "lse")
+    flags = ((MLA_CAUSAL if causal else 0) | (MLA_OUT_F32 if out_f32 else 0)
+             | (MLA_PREV_OUT_F32 if prev_f32 else 0))
     _check(LIB.mla_fwd(ctypes.byref(views[0]), ctypes.byref(views[1]), ctypes.byref(views[2]),
                        ctypes.byref(views[3]), ctypes.byref(views[4]),
                        1, H, Hkv, T, T, dq, dr, dv,
                        seq_lens.data_ptr() if seq_lens is not None else None,
                        seq_lens.numel() if seq_lens is not None else 0,
-                       float(scale), MLA_CAUSAL if causal else 0, 0, 0,
+                       float(scale), flags, 0, 0,
                        _ref(vpo), _ref(vpl), ctypes.byref(vout), ctypes.byref(vl),
-                       *_workspace(q1.device, workspace), _stream(q1.device)))
+                       *_workspace(dev_, workspace), _stream(dev_)))
     return out, lse
 
 
@@ -356,15 +419,23 @@ def merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor, lse_b: 
           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
           ) -> Tuple[torch.Tensor, torch.Tensor]:
     """LSE merge of two [B, H, N, dv] partial results (mla_merge_lse)."""
+    _need(out_a, "out_a", torch.bfloat16)
+    if out_a.dim() != 4:
+        raise ValueError("out_a: expected [B, H, N, dv]")
     B, H, N, dv = out_a.shape
+    dev_ = out_a.device
     if out is None:
         out = torch.empty_like(out_a)
     if lse is None:
-        lse = torch.empty_like(lse_a)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev_)
+    for t, n in ((out_b, "out_b"), (out, "out")):
+        _shape(t, n, (B, H, N, dv), dev_)
+    for t, n in ((lse_a, "lse_a"), (lse_b, "lse_b"), (lse, "lse")):
+        _shape(t, n, (B, H, N), dev_)
     va, vb, vo = _rows_bhtd(out_a, "out_a"), _rows_bhtd(out_b, "out_b"), _rows_bhtd(out, "out")
     la, lb, lo = _lse_bht(lse_a, "lse_a"), _lse_bht(lse_b, "lse_b"), _lse_bht(lse, "lse")
     _check(LIB.mla_merge_lse(ctypes.byref(va), ctypes.byref(la), ctypes.byref(vb), ctypes.byref(lb),
-                             B, H, N, dv, ctypes.byref(vo), ctypes.byref(lo), _stream(out_a.device)))
+                             B, H, N, dv, ctypes.byref(vo), ctypes.byref(lo), _stream(dev_)))
     return out, lse
 
 
@@ -375,11 +446,9 @@ def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
     """Top-k sparse latent attention (mla_sparse_fwd): q_lift [B,S,H,L],
     q_pe [B,S,H,R], c_kv [B,S_kv,L], k_pe [B,S_kv,R], topk_idx int32
     [B,S,K] -> out [B, S, H*L] bf16 and lse [B, S, H] fp32.  ``workspace`` as
-    for fwd.  ``mx4``: each head's columns in MX 4-pack order (MLA_OUT_MX4)."""
-    B, S, H, L = q_lift.shape
-    R = q_pe.shape[3]
-    S_kv = c_kv.shape[1]
-    K = topk_idx.shape[2]
+    for fwd.  ``mx4``: each head's columns in MX 4-pack order (MLA_OUT_MX4).
+    A float32 ``out`` selects MLA_OUT_F32 (the result before its bf16
+    rounding)."""
     for t, n in ((q_lift, "q_lift"), (q_pe, "q_pe")):
         _need(t, n, torch.bfloat16)
         if t.dim() != 4 or t.stride(3) != 1:
@@ -388,16 +457,30 @@ def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
         _need(t, n, torch.bfloat16)
         if t.dim() != 3 or t.stride(2) != 1:
             raise ValueError(f"{n}: expected [B, S_kv, D] with a contiguous last dim")
+    B, S, H, L = q_lift.shape
+    R = q_pe.shape[3]
+    S_kv = c_kv.shape[1]
+    dev_ = q_lift.device
+    _shape(q_pe, "q_pe", (B, S, H, R), dev_)
+    _shape(c_kv, "c_kv", (B, S_kv, L), dev_)
+    _shape(k_pe, "k_pe", (B, S_kv, R), dev_)
     _need(topk_idx, "topk_idx", torch.int32)
-    if not topk_idx.is_contiguous() or topk_idx.shape[:2] != (B, S):
+    if topk_idx.dim() != 3 or not topk_idx.is_contiguous() or tuple(topk_idx.shape[:2]) != (B, S):
         raise ValueError("topk_idx: expected a contiguous [B, S, K] tensor")
+    if topk_idx.device != dev_:
+        raise ValueError(f"topk_idx: on {topk_idx.device}, expected {dev_}")
+    K = topk_idx.shape[2]
     if out is None:
-        out = torch.empty((B, S, H * L), dtype=torch.bfloat16, device=q_lift.device)
+        out = torch.empty((B, S, H * L), dtype=torch.bfloat16, device=dev_)
     if lse is None and want_lse:
-        lse = torch.empty((B, S, H), dtype=torch.float32, device=q_lift.device)
-    _need(out, "out", torch.bfloat16)
-    if out.shape != (B, S, H * L) or out.stride(2) != 1:
+        lse = torch.empty((B, S, H), dtype=torch.float32, device=dev_)
+    out_f32 = out.dtype == torch.float32
+    _need(out, "out", torch.float32 if out_f32 else torch.bfloat16)
+    _shape(out, "out", (B, S, H * L), dev_)
+    if out.stride(2) != 1:
         raise ValueError("out: expected [B, S, H*L] with a contiguous last dim")
+    if lse is not None:
+        _shape(lse, "lse", (B, S, H), dev_)
     v_ql = MlaRows(q_lift.data_ptr(), q_lift.stride(0), q_lift.stride(2), q_lift.stride(1))
     v_qp = MlaRows(q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(2), q_pe.stride(1))
     v_ck = MlaRows(c_kv.data_ptr(), c_kv.stride(0), 0, c_kv.stride(1))
@@ -409,7 +492,8 @@ def sparse_fwd(q_lift: torch.Tensor, q_pe: torch.Tensor, c_kv: torch.Tensor, k_p
         v_l = MlaRows(lse.data_ptr(), lse.stride(0), lse.stride(2), lse.stride(1))
     _check(LIB.mla_sparse_fwd(ctypes.byref(v_ql), ctypes.byref(v_qp), ctypes.byref(v_ck),
                               ctypes.byref(v_kp), topk_idx.data_ptr(), B, S, S_kv, H, L, R, K,
-                              float(scale), MLA_OUT_MX4 if mx4 else 0, ctypes.byref(v_o), _ref(v_l),
+                              float(scale), (MLA_OUT_MX4 if mx4 else 0) | (MLA_OUT_F32 if out_f32 else 0),
+                              ctypes.byref(v_o), _ref(v_l),
                               *_workspace(q_lift.device, workspace), _stream(q_lift.device)))
     return out, lse
 
@@ -422,15 +506,19 @@ def vup(o: torch.Tensor, w_uv: torch.Tensor, *, out: Optional[torch.Tensor] = No
     ``out.unsqueeze(2)``), w_uv bf16 [H, 128, 512] contiguous.  Returns out
     [B, T, H, 128] bf16 (o_proj's input row per token), or writes the given
     ``out`` of that shape.  ``mx4``: o's columns are in MX 4-pack order."""
+    _need(o, "o", torch.bfloat16)
+    if o.dim() != 4:
+        raise ValueError("o: expected [B, H, T, L]")
     B, H, T, L = o.shape
     _need(w_uv, "w_uv", torch.bfloat16)
     if w_uv.dim() != 3 or w_uv.shape[0] != H or w_uv.shape[2] != L or not w_uv.is_contiguous():
         raise ValueError("w_uv: expected a contiguous [H, dvh, L] tensor")
+    if w_uv.device != o.device:
+        raise ValueError(f"w_uv: on {w_uv.device}, expected {o.device}")
     dvh = w_uv.shape[1]
     if out is None:
         out = torch.empty((B, T, H, dvh), dtype=torch.bfloat16, device=o.device)
-    if out.shape != (B, T, H, dvh):
-        raise ValueError("out: expected [B, T, H, dvh]")
+    _shape(out, "out", (B, T, H, dvh), o.device)
     vo = _rows_bhtd(out.transpose(1, 2), "out")
     _check(LIB.mla_vup(ctypes.byref(_rows_bhtd(o, "o")), w_uv.data_ptr(), B, H, T, L, dvh,
                        MLA_OUT_MX4 if mx4 else 0, ctypes.byref(vo), _stream(o.device)))
@@ -456,25 +544,50 @@ def decode_fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float,
     of each sequence; None = slot b).  Returns (out [B, H, dv] bf16, lse [B, H] fp32 or
     None).  n_splits = 0 lets the library split the keys; ``workspace`` (a
     uint8 GPU tensor) defaults to a cached per-stream buffer."""
+    if (q_rope is None) != (k_rope is None):
+        raise ValueError("q_rope and k_rope: give both or neither")
+    for t, n in ((q, "q"), (kv, "kv")) + (((q_rope, "q_rope"), (k_rope, "k_rope")) if q_rope is not None else ()):
+        _need(t, n, torch.bfloat16)
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{n}: expected a 3-D tensor with a contiguous last dim")
     B, H, dq = q.shape
     Nkv = kv.shape[1]
     dr = 0 if q_rope is None else q_rope.shape[-1]
     dv = head_dim_v
-    for t, n in ((q, "q"), (kv, "kv")) + (((q_rope, "q_rope"), (k_rope, "k_rope")) if dr else ()):
-        _need(t, n, torch.bfloat16)
-        if t.dim() != 3 or t.stride(2) != 1:
-            raise ValueError(f"{n}: expected a 3-D tensor with a contiguous last dim")
+    dev_ = q.device
+    _shape(kv, "kv", (kv.shape[0], Nkv, dq), dev_)
+    if kv_slots is None and kv.shape[0] < B and Nkv > 0:
+        raise ValueError(f"kv: {kv.shape[0]} cache slots for {B} sequences (sequence b reads slot b)")
+    if q_rope is not None:
+        _shape(q_rope, "q_rope", (B, H, dr), dev_)
+        _shape(k_rope, "k_rope", (kv.shape[0], Nkv, dr), dev_)
     if out is None:
-        out = torch.empty((B, H, dv), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev_)
     if lse is None and want_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev_)
     _need(out, "out", torch.bfloat16)
+    _shape(out, "out", (B, H, dv), dev_)
+    if lse is not None:
+        _shape(lse, "lse", (B, H), dev_)
     for t, n in ((kv_lens, "kv_lens"), (kv_slots, "kv_slots")):
         if t is not None:
             _need(t, n, torch.int32)
-            if t.shape != (B,) or not t.is_contiguous():
+            if tuple(t.shape) != (B,) or not t.is_contiguous():
                 raise ValueError(f"{n}: expected a contiguous [B] tensor")
+            if t.device != dev_:
+                raise ValueError(f"{n}: on {t.device}, expected {dev_}")
     n_slots = kv.shape[0] if kv_slots is not None else 0
+    vq = MlaRows(q.data_ptr(), q.stride(0), q.stride(1), 0)
+    vkv = MlaRows(kv.data_ptr(), kv.stride(0), 0, kv.stride(1))
+    vqr = MlaRows(q_rope.data_ptr(), q_rope.stride(0), q_rope.stride(1), 0) if dr else None
+    vkr = MlaRows(k_rope.data_ptr(), k_rope.stride(0), 0, k_rope.stride(1)) if dr else None
+    vo = MlaRows(out.data_ptr(), out.stride(0), out.stride(1), 0)
+    vl = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+        vl = MlaRows(lse.data_ptr(), lse.stride(0), lse.stride(1), 0)
+    lens_p = kv_lens.data_ptr() if kv_lens is not None else None
+    slots_p = kv_slots.data_ptr() if kv_slots is not None else None
     need = int(LIB.mla_decode_workspace_size(B, H, Nkv, n_splits))
     if need == 0:
         raise MlaError(2, f"no key split fits Nkv={Nkv} with n_splits={n_splits}")
@@ -486,18 +599,8 @@ def decode_fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float,
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             _DECODE_WS[key] = workspace
     _need(workspace, "workspace", torch.uint8)
-    vq = MlaRows(q.data_ptr(), q.stride(0), q.stride(1), 0)
-    vkv = MlaRows(kv.data_ptr(), kv.stride(0), 0, kv.stride(1))
-    vqr = MlaRows(q_rope.data_ptr(), q_rope.stride(0), q_rope.stride(1), 0) if dr else None
-    vkr = MlaRows(k_rope.data_ptr(), k_rope.stride(0), 0, k_rope.stride(1)) if dr else None
-    vo = MlaRows(out.data_ptr(), out.stride(0), out.stride(1), 0)
-    vl = None
-    if lse is not None:
-        _need(lse, "lse", torch.float32)
-        vl = MlaRows(lse.data_ptr(), lse.stride(0), lse.stride(1), 0)
     _check(LIB.mla_decode_fwd(ctypes.byref(vq), _ref(vqr), ctypes.byref(vkv), _ref(vkr),
-                              kv_lens.data_ptr() if kv_lens is not None else None,
-                              kv_slots.data_ptr() if kv_slots is not None else None, n_slots,
+                              lens_p, slots_p, n_slots,
                               B, H, Nkv, dq, dr, dv, float(scale), n_splits,
                               ctypes.byref(vo), _ref(vl), workspace.data_ptr(), workspace.numel(),
                               _stream(q.device)))
@@ -512,7 +615,14 @@ def debug_gather(c_kv: torch.Tensor, k_pe: torch.Tensor, idx: torch.Tensor, b: i
     _need(idx, "idx", torch.int32)
     if idx.dim() != 1 or not idx.is_contiguous():
         raise ValueError("idx: expected a contiguous 1-D int32 tensor")
+    if c_kv.dim() != 3 or k_pe.dim() != 3:
+        raise ValueError("c_kv, k_pe: expected [B, S_kv, D]")
     L, R = c_kv.shape[2], k_pe.shape[2]
+    _shape(k_pe, "k_pe", (c_kv.shape[0], c_kv.shape[1], R), c_kv.device)
+    if idx.device != c_kv.device:
+        raise ValueError(f"idx: on {idx.device}, expected {c_kv.device}")
+    if not 0 <= b < c_kv.shape[0]:
+        raise ValueError(f"b = {b} outside the cache's {c_kv.shape[0]} batches")
     K = idx.numel()
     rows = torch.empty((K, L + R), dtype=torch.bfloat16, device=c_kv.device)
     v_ck = MlaRows(c_kv.data_ptr(), c_kv.stride(0), 0, c_kv.stride(1))
@@ -570,11 +680,18 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
     least mla_ring_workspace_size() bytes (allocated if not given)."""
     if order not in _RING_ORDERS:
         raise ValueError(f"unknown ring schedule {order!r}")
+    for t, n in ((q, "q"), (kv, "kv")):
+        _need(t, n, torch.bfloat16)
+        if t.dim() != 4:
+            raise ValueError(f"{n}: expected [B, H, N, D]")
     B, H, N, dq = q.shape
+    _shape(kv, "kv", (B, 1, N, dq), q.device)
     if out is None:
         out = torch.empty((B, H, N, head_dim_v), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _shape(out, "out", (B, H, N, head_dim_v), q.device)
+    _shape(lse, "lse", (B, H, N), q.device)
     need = int(LIB.mla_ring_workspace_size(B, H, N, n_chunks))
     if carry is None and need:
         carry = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -582,6 +699,8 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
     if carry is not None:
         if not carry.is_cuda or not carry.is_contiguous():
             raise ValueError("carry: expected a contiguous GPU tensor")
+        if carry.device != q.device:
+            raise ValueError(f"carry: on {carry.device}, expected {q.device}")
         ws, ws_bytes = carry.data_ptr(), carry.numel() * carry.element_size()
     vq, vkv = _rows_bhtd(q, "q"), _rows_bhtd(kv, "kv")
     vo, vl = _rows_bhtd(out, "out"), _lse_bht(lse, "lse")

@@ -552,11 +552,15 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
   if (K > mla::kSparseMaxTopk)
     return fail(MLA_ERR_UNSUPPORTED, "sparse kernel handles up to %d indices per query (got %d)", mla::kSparseMaxTopk, K);
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
-  if (flags & ~MLA_OUT_MX4) return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~MLA_OUT_MX4);
+  if (flags & ~(MLA_OUT_MX4 | MLA_OUT_F32))
+    return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~(MLA_OUT_MX4 | MLA_OUT_F32));
+  const bool out_f32 = flags & MLA_OUT_F32;
+  if (out_f32 && (flags & MLA_OUT_MX4))
+    return fail(MLA_ERR_UNSUPPORTED, "MLA_OUT_MX4 is built for bf16 output only (not with MLA_OUT_F32)");
   if ((st = check_workspace(workspace, workspace_bytes))) return st;
   const bool no_q = B == 0 || S == 0;  // no queries: the query-side views may be NULL
   if ((st = check_rows(q_lift, "q_lift", true, no_q)) || (st = check_rows(q_pe, "q_pe", true, no_q)) ||
-      (st = check_rows(out, "out", true, no_q)))
+      (st = out_f32 ? check_rows_f32(out, "out", no_q) : check_rows(out, "out", true, no_q)))
     return st;
   if ((st = check_rows(c_kv, "c_kv", false, B == 0)) || (st = check_rows(k_pe, "k_pe", false, B == 0))) return st;
   if ((!topk_idx && !no_q) || (reinterpret_cast<uintptr_t>(topk_idx) & 3u))
@@ -583,6 +587,7 @@ mla_status mla_sparse_fwd(const mla_rows* q_lift, const mla_rows* q_pe, const ml
   p.topk = K;
   p.scale_log2 = scale * kLog2e;
   p.mx4 = (flags & MLA_OUT_MX4) ? 1 : 0;
+  p.out_f32 = out_f32 ? 1 : 0;
   p.queue = static_cast<unsigned*>(workspace);
   if (S == 0 || B == 0) return MLA_OK;
   return hip_status(mla::launch_latent_sparse(p, static_cast<hipStream_t>(stream)), "sparse attention launch");

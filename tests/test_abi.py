@@ -230,12 +230,16 @@ def test_fwd_valid_lens_split_form_unsupported(lib):
     assert st == MLA_ERR_UNSUPPORTED
 
 
-def test_sparse_rejects_unknown_flags(lib):
+@pytest.mark.parametrize("flags,code,msg", [(4, MLA_ERR_INVALID_ARG, "flag"), (6, MLA_ERR_INVALID_ARG, "flag"),
+                                            (3, MLA_ERR_UNSUPPORTED, "MX4")])
+def test_sparse_rejects_unknown_flags(lib, flags, code, msg):
+    """Bits other than MLA_OUT_MX4 and MLA_OUT_F32 are refused, and the two
+    are not combined."""
     from ring_chunk_attention_amd.binding import MlaRows
     r = MlaRows(FAKE, 0, 512, 512)
     st = lib.mla_sparse_fwd(ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), ctypes.byref(r), FAKE,
-                            1, 16, 1024, 128, 512, 64, 128, 0.07, 2, ctypes.byref(r), None, None, 0, None)
-    assert st == MLA_ERR_INVALID_ARG and "flag" in lib.mla_last_error().decode()
+                            1, 16, 1024, 128, 512, 64, 128, 0.07, flags, ctypes.byref(r), None, None, 0, None)
+    assert st == code and msg in lib.mla_last_error().decode()
 
 
 @pytest.mark.parametrize("args,code,msg", [
@@ -438,3 +442,4 @@ def test_sparse_sizes_whose_products_overflow_are_rejected(lib, B, S, S_kv, msg)
     st = lib.mla_sparse_fwd(ctypes.byref(q), ctypes.byref(qp), ctypes.byref(ckv), ctypes.byref(kpe), FAKE,
                             B, S, S_kv, 128, 512, 64, 128, 0.07, 0, ctypes.byref(o), None, None, 0, None)
     assert st == MLA_ERR_UNSUPPORTED and msg in lib.mla_last_error().decode()
+

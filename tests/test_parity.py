@@ -2,10 +2,16 @@
 
 Every case draws seeded inputs from ``workloads``, runs them through
 ``ring_chunk_attention_amd`` on the GPU and compares element by element with
-the oracle: bf16 outputs to 1e-2 and fp32 LSE to 1e-3 max-abs; gathers and
-the repeated-row case bit-exact.  Small cases compare every element; the
-full-size workloads (the launch configurations the benchmark times) compare
-sampled rows that the oracle computes one by one.
+the oracle: bf16 outputs to 1e-2 max-abs where |O| < 2 and, from |O| = 2
+on, to half an ulp plus 1e-2 (the rounding of a value within 1e-2), fp32 LSE
+to 1e-3 max-abs; gathers and the repeated-row case bit-exact.  Cases whose outputs
+reach |O| >= 2 (folds with a previous result, wide score ranges, rows that
+see few keys) also run with a float32 output: that result, the kernel's
+arithmetic before the last rounding, must lie within 1e-2 of the oracle
+everywhere, and the bf16 result must be bit for bit its round-to-nearest-even.
+Small cases compare every element; the full-size workloads (the launch
+configurations the benchmark times) compare sampled rows that the oracle
+computes one by one.
 """
 import math
 
@@ -14,7 +20,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import LSE_TOL, O_TOL, dev, dev_bf16, host, report, report_o
+from gpu_util import LSE_TOL, O_TOL, assert_rne_of, dev, dev_bf16, host, report, report_o
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +31,22 @@ torch = pytest.importorskip("torch")
 def mla():
     import ring_chunk_attention_amd as m
     return m
+
+
+def _twin(name, o_bf16, o_f32, o_ref, got_bf16=None, got_f32=None):
+    """A call's bf16 and float32 outputs against the oracle: the float32 one
+    within max-abs 1e-2 everywhere, the bf16 one its rounding bit for bit and
+    within the bf16 bound.  got_*: the host values to compare with o_ref (the
+    sampled rows), when not the whole tensors."""
+    assert_rne_of(name, o_bf16, o_f32)
+    g16 = host(o_bf16) if got_bf16 is None else got_bf16
+    g32 = host(o_f32) if got_f32 is None else got_f32
+    assert report(f"{name} fp32 O", g32, o_ref) <= O_TOL
+    assert report_o(f"{name} O", g16, o_ref) <= 1.0
+
+
+def _f32(t):
+    return torch.empty(t.shape, dtype=torch.float32, device=t.device)
 
 
 # ---------------------------------------------------------------------------
@@ -39,12 +61,15 @@ def _dense_gpu(mla, c, **kw):
 
 
 def test_tiny_config_full(mla):
-    """B=1, 4 heads, N=128, dk=576/dv=512, seed 0: every element."""
+    """B=1, 4 heads, N=128, dk=576/dv=512, seed 0: every element, with the
+    float32-output twin (early rows see few keys and reach |O| > 2)."""
     c = W.tiny(0)
     out, lse = _dense_gpu(mla, c)
+    o32, l32 = _dense_gpu(mla, c, out=_f32(out))
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
-    assert report_o("tiny O", host(out), o_ref) <= 1.0
+    _twin("tiny", out, o32, o_ref)
     assert report("tiny LSE", host(lse), l_ref) <= LSE_TOL
+    assert torch.equal(lse, l32)
 
 
 @pytest.mark.parametrize("B,H,N,Nkv,q_off,kv_off,causal,seed", [
@@ -58,9 +83,10 @@ def test_dense_ragged(mla, B, H, N, Nkv, q_off, kv_off, causal, seed):
     c = W.dense_case(B=B, H=H, N=N, Nkv=Nkv, seed=seed, causal=causal, q_offset=q_off,
                      kv_offset=kv_off)
     out, lse = _dense_gpu(mla, c)
+    o32, _ = _dense_gpu(mla, c, out=_f32(out))
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, causal=causal, q_offset=q_off,
                                     kv_offset=kv_off)
-    assert report_o("O", host(out), o_ref) <= 1.0
+    _twin("ragged", out, o32, o_ref)
     assert report("LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -87,10 +113,12 @@ def test_dense_fold_prev(mla):
     prev_l = rng.uniform(0, 8, (1, 4, 96)).astype(np.float32)
     prev_l[:, :, 5] = -np.inf
     out, lse = _dense_gpu(mla, c, prev=(dev_bf16(prev_o), dev(prev_l)))
+    o32, l32 = _dense_gpu(mla, c, prev=(dev_bf16(prev_o), dev(prev_l)), out=_f32(out))
     fresh = oracle.dense_mla(c.q, c.kv, 512, c.scale, q_offset=0, kv_offset=32)
     o_ref, l_ref = oracle.merge(prev_o, prev_l, fresh[0], fresh[1])
-    assert report_o("fold O", host(out), o_ref) <= 1.0
+    _twin("fold", out, o32, o_ref)
     assert report("fold LSE", host(lse), l_ref) <= LSE_TOL
+    assert torch.equal(lse, l32)
     # rows 0..31 see no key (kv starts at 32): the previous values are kept bit
     # for bit, except row 5 whose previous LSE is -inf too, which gives (0, -inf)
     keep = [i for i in range(32) if i != 5]
@@ -107,11 +135,15 @@ def test_dense_fold_in_place(mla):
     o_t, l_t = dev_bf16(prev_o), dev(prev_l)
     q, kv = dev_bf16(c.q), dev_bf16(c.kv)
     mla.fwd(q, kv, scale=c.scale, prev=(o_t, l_t), out=o_t, lse=l_t)
+    # the float32 twin, in place over a float32 copy of the same previous result
+    o_f, l_f = dev_bf16(prev_o).float(), dev(prev_l)
+    mla.fwd(q, kv, scale=c.scale, prev=(o_f, l_f), out=o_f, lse=l_f)
     torch.cuda.synchronize()
     fresh = oracle.dense_mla(c.q, c.kv, 512, c.scale)
     o_ref, l_ref = oracle.merge(prev_o, prev_l, fresh[0], fresh[1])
-    assert report_o("in-place O", host(o_t), o_ref) <= 1.0
+    _twin("in-place", o_t, o_f, o_ref)
     assert report("in-place LSE", host(l_t), l_ref) <= LSE_TOL
+    assert torch.equal(l_t, l_f)
 
 
 def test_dense_fp32_out_and_prev(mla):
@@ -158,6 +190,11 @@ def test_dsv3_full_size_sampled(mla):
     assert report_o("dsv3 O", o_got, o_ref) <= 1.0
     assert report("dsv3 LSE", l_got, l_ref) <= LSE_TOL
     assert not torch.isnan(out).any() and torch.isfinite(lse).all()
+    # the float32 twin: the whole output is its rounding, the sampled rows within 1e-2
+    o32, l32 = _dense_gpu(mla, c, out=_f32(out))
+    assert torch.equal(lse, l32)
+    assert_rne_of("dsv3", out, o32)
+    assert report("dsv3 fp32 O", host(o32[:, heads][:, :, rows]), o_ref) <= O_TOL
 
 
 # ---------------------------------------------------------------------------
@@ -250,12 +287,23 @@ def test_ring4_config_sampled(mla, order):
 # ---------------------------------------------------------------------------
 # split q/k varlen ring step
 # ---------------------------------------------------------------------------
-def _split_gpu(mla, c, with_prev=True):
+def _split_gpu(mla, c, with_prev=True, f32=False, causal=True, scale=None):
     args = [dev_bf16(x) for x in (c.q1, c.q2, c.k1, c.k2, c.v)]
     prev = (dev_bf16(c.prev_out), dev(c.prev_lse)) if (with_prev and c.prev_out is not None) else None
-    out, lse = mla.split_fwd(*args, scale=c.scale, seq_lens=dev(c.seq_lens), prev=prev)
+    T, H = c.q1.shape[:2]
+    out = torch.empty((T, H, c.v.shape[2]), dtype=torch.float32, device="cuda") if f32 else None
+    out, lse = mla.split_fwd(*args, scale=c.scale if scale is None else scale, seq_lens=dev(c.seq_lens),
+                             prev=prev, out=out, causal=causal)
     torch.cuda.synchronize()
     return out, lse
+
+
+def _split_twin(mla, c, with_prev=True, **kw):
+    """The bf16 and float32 outputs of the same split call (same LSE)."""
+    out, lse = _split_gpu(mla, c, with_prev, **kw)
+    o32, l32 = _split_gpu(mla, c, with_prev, f32=True, **kw)
+    assert torch.equal(lse, l32)
+    return out, o32, lse
 
 
 @pytest.mark.parametrize("lens,H,Hkv,with_prev", [
@@ -265,42 +313,57 @@ def _split_gpu(mla, c, with_prev=True):
 ])
 def test_split_small(mla, lens, H, Hkv, with_prev):
     c = W.split_case(seq_lens=lens, H=H, Hkv=Hkv, seed=sum(lens), with_prev=with_prev)
-    out, lse = _split_gpu(mla, c, with_prev)
+    out, o32, lse = _split_twin(mla, c, with_prev)
     o_ref, l_ref = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale,
                                     prev_out=c.prev_out if with_prev else None,
                                     prev_lse=c.prev_lse if with_prev else None)
-    assert report_o("split O", host(out), o_ref) <= 1.0
+    _twin("split", out, o32, o_ref)
     assert report("split LSE", host(lse), l_ref) <= LSE_TOL
+
+
+@pytest.mark.parametrize("with_prev", [False, True])
+def test_split_non_causal(mla, with_prev):
+    """Without the mask every token of a sequence sees every key of its own
+    sequence (and none of the others)."""
+    c = W.split_case(seq_lens=[70, 200, 1, 130], H=4, Hkv=2, seed=77, with_prev=with_prev)
+    out, o32, lse = _split_twin(mla, c, with_prev, causal=False)
+    o_ref, l_ref = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale, causal=False,
+                                    prev_out=c.prev_out if with_prev else None,
+                                    prev_lse=c.prev_lse if with_prev else None)
+    _twin("split non-causal", out, o32, o_ref)
+    assert report("split non-causal LSE", host(lse), l_ref) <= LSE_TOL
 
 
 def test_split_config_sampled(mla):
     """8 sequences (seed-0 lengths, T = 27610), 32 heads, prev fold: sampled
     tokens of each sequence for four heads against the oracle."""
     c = W.split_ring_step(0)
-    out, lse = _split_gpu(mla, c)
+    out, o32, lse = _split_twin(mla, c)
+    assert_rne_of("split cfg", out, o32)          # every element of the step
     cu = np.concatenate([[0], np.cumsum(c.seq_lens)])
     f = W.bf16_bits_to_f64
-    worst_o = worst_l = 0.0
+    worst_o = worst_o32 = worst_l = 0.0
     for s in range(len(c.seq_lens)):
         t0, L = int(cu[s]), int(c.seq_lens[s])
-        rows = np.unique(np.array([0, 1, 127, 128, L // 2, L - 2, L - 1]).clip(0, L - 1))
+        rows = np.unique(np.array([0, 1, 2, 3, 127, 128, L // 2, L - 2, L - 1]).clip(0, L - 1))
         for h in (0, 9, 22, 31):
             q = np.concatenate([f(c.q1[t0 + rows, h]), f(c.q2[t0 + rows, h])], 1)
             k = np.concatenate([f(c.k1[t0:t0 + L, h]), f(c.k2[t0:t0 + L, h])], 1)
             o, l = oracle.attention(q, k, f(c.v[t0:t0 + L, h]), c.scale, True, rows, np.arange(L))
             o, l = oracle.merge(c.prev_out[t0 + rows, h], c.prev_lse[h, t0 + rows], o, l)
             worst_o = max(worst_o, report_o(f"split s{s} h{h} O", host(out[t0 + rows, h]), o))
+            worst_o32 = max(worst_o32, report(f"split s{s} h{h} fp32 O", host(o32[t0 + rows, h]), o))
             worst_l = max(worst_l, report(f"split s{s} h{h} LSE", host(lse[h, t0 + rows]), l))
-    assert worst_o <= 1.0 and worst_l <= LSE_TOL
+    assert worst_o <= 1.0 and worst_o32 <= O_TOL and worst_l <= LSE_TOL
 
 
 # ---------------------------------------------------------------------------
 # sparse top-k
 # ---------------------------------------------------------------------------
-def _sparse_gpu(mla, c, idx=None):
+def _sparse_gpu(mla, c, idx=None, out=None):
     idx = c.idx if idx is None else idx
     out, lse = mla.sparse_fwd(dev_bf16(c.q_lift), dev_bf16(c.q_pe), dev_bf16(c.c_kv),
-                              dev_bf16(c.k_pe), dev(idx), scale=c.scale)
+                              dev_bf16(c.k_pe), dev(idx), scale=c.scale, out=out)
     torch.cuda.synchronize()
     return out, lse
 
@@ -311,8 +374,9 @@ def _sparse_gpu(mla, c, idx=None):
 def test_sparse_small(mla, H, K, seed):
     c = W.sparse_case(S=24, S_kv=max(3000, K + 100), pos0=max(2900, K + 50), H=H, K=K, seed=seed)
     out, lse = _sparse_gpu(mla, c)
+    o32, _ = _sparse_gpu(mla, c, out=_f32(out))
     o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale)
-    assert report_o("sparse O", host(out), o_ref) <= 1.0
+    _twin("sparse", out, o32, o_ref)
     assert report("sparse LSE", host(lse), l_ref) <= LSE_TOL
 
 
@@ -396,9 +460,7 @@ def test_sparse_config_sampled(mla):
 # exact-max pass.  The 64 RoPE columns of queries and keys are scaled by 8
 # (exact in bf16), which gives scores of about 37 nats standard deviation.
 # The weights are then close to one-hot, so an output is close to one value
-# row; the value columns are halved so that outputs stay below 4 in
-# magnitude, where rounding to bf16 costs at most 2^-8 (between 4 and 8 it
-# would cost up to 2^-7, past the 1e-2 bound).
+# row and reaches |O| > 4; the float32 twins hold the arithmetic to 1e-2.
 # ---------------------------------------------------------------------------
 def _times_pow2(bits, f, cols=slice(None)):
     """bf16 bits with the columns `cols` of the last axis times a power of two
@@ -422,14 +484,16 @@ def _max_growth_log2(q, k, scale, vis):
 def test_dense_wide_range_second_pass(mla):
     c = W.dense_case(B=1, H=6, N=200, seed=8)
     c.q = _times_pow2(c.q, 8.0, slice(512, None))
-    c.kv = _times_pow2(_times_pow2(c.kv, 8.0, slice(512, None)), 0.5, slice(0, 512))
+    c.kv = _times_pow2(c.kv, 8.0, slice(512, None))
     q64, k64 = W.bf16_bits_to_f64(c.q[0, 0]), W.bf16_bits_to_f64(c.kv[0, 0])
     vis = np.tril(np.ones((200, 200), dtype=bool))
     assert _max_growth_log2(q64, k64, c.scale, vis) > 40.0
     out, lse = _dense_gpu(mla, c)
+    o32, l32 = _dense_gpu(mla, c, out=_f32(out))
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale)
-    assert report_o("wide O", host(out), o_ref) <= 1.0
+    _twin("wide", out, o32, o_ref)
     assert report("wide LSE", host(lse), l_ref) <= LSE_TOL
+    assert torch.equal(lse, l32)
 
 
 @pytest.mark.parametrize("K", [300, 2400])
@@ -437,30 +501,59 @@ def test_sparse_wide_range_second_pass(mla, K):
     c = W.sparse_case(S=8, S_kv=3000, pos0=2900, H=32, K=K, seed=50 + K)
     c.q_pe = _times_pow2(c.q_pe, 8.0)
     c.k_pe = _times_pow2(c.k_pe, 8.0)
-    c.c_kv = _times_pow2(c.c_kv, 0.5)
     q64 = np.concatenate([W.bf16_bits_to_f64(c.q_lift[0, 0]), W.bf16_bits_to_f64(c.q_pe[0, 0])], axis=1)
     rows = np.concatenate([W.bf16_bits_to_f64(c.c_kv[0]), W.bf16_bits_to_f64(c.k_pe[0])], axis=1)
     k64 = rows[c.idx[0, 0]]
     assert _max_growth_log2(q64, k64, c.scale, np.ones((32, K), dtype=bool)) > 40.0
     out, lse = _sparse_gpu(mla, c)
+    o32, l32 = _sparse_gpu(mla, c, out=torch.empty(out.shape, dtype=torch.float32, device="cuda"))
     o_ref, l_ref = oracle.sparse_mla(c.q_lift, c.q_pe, c.c_kv, c.k_pe, c.idx, c.scale)
-    assert report_o("wide sparse O", host(out), o_ref) <= 1.0
+    _twin("wide sparse", out, o32, o_ref)
     assert report("wide sparse LSE", host(lse), l_ref) <= LSE_TOL
+    assert torch.equal(lse, l32)
 
 
 def test_split_wide_range_second_pass(mla):
     c = W.split_case(seq_lens=[300, 77], H=4, Hkv=2, seed=9, with_prev=True)
     c.q2 = _times_pow2(c.q2, 8.0)
     c.k2 = _times_pow2(c.k2, 8.0)
-    c.v = _times_pow2(c.v, 0.5)
     q64 = np.concatenate([W.bf16_bits_to_f64(c.q1[:300, 0]), W.bf16_bits_to_f64(c.q2[:300, 0])], axis=1)
     k64 = np.concatenate([W.bf16_bits_to_f64(c.k1[:300, 0]), W.bf16_bits_to_f64(c.k2[:300, 0])], axis=1)
     assert _max_growth_log2(q64, k64, c.scale, np.tril(np.ones((300, 300), dtype=bool))) > 40.0
-    out, lse = _split_gpu(mla, c, True)
+    out, o32, lse = _split_twin(mla, c, True)
     o_ref, l_ref = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale,
                                     prev_out=c.prev_out, prev_lse=c.prev_lse)
-    assert report_o("wide split O", host(out), o_ref) <= 1.0
+    _twin("wide split", out, o32, o_ref)
     assert report("wide split LSE", host(lse), l_ref) <= LSE_TOL
+
+
+# ---------------------------------------------------------------------------
+# scale <= 0: the kernels scale and mask the scores before the softmax
+# (rather than folding the scale into the exponent), so that the row max is
+# taken on the scaled values; scale 0 gives uniform weights over the visible
+# keys (the prefix mean of V, LSE = ln #visible)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("scale", [0.0, -0.05])
+def test_non_positive_scale_all_forms(mla, scale):
+    c = W.dense_case(B=1, H=5, N=150, Nkv=170, seed=60, q_offset=20)
+    out, lse = mla.fwd(dev_bf16(c.q), dev_bf16(c.kv), scale=scale, q_offset=20)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, scale, q_offset=20)
+    assert report_o(f"scale {scale} dense O", host(out), o_ref) <= 1.0
+    assert report(f"scale {scale} dense LSE", host(lse), l_ref) <= LSE_TOL
+    cs = W.sparse_case(S=6, S_kv=900, pos0=700, H=16, K=300, seed=61)
+    o, l = mla.sparse_fwd(*[dev_bf16(x) for x in (cs.q_lift, cs.q_pe, cs.c_kv, cs.k_pe)], dev(cs.idx),
+                          scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.sparse_mla(cs.q_lift, cs.q_pe, cs.c_kv, cs.k_pe, cs.idx, scale)
+    assert report_o(f"scale {scale} sparse O", host(o), o_ref) <= 1.0
+    assert report(f"scale {scale} sparse LSE", host(l), l_ref) <= LSE_TOL
+    cp = W.split_case(seq_lens=[90, 160], H=4, Hkv=2, seed=62, with_prev=True)
+    out, o32, lse = _split_twin(mla, cp, True, scale=scale)
+    o_ref, l_ref = oracle.split_mla(cp.q1, cp.q2, cp.k1, cp.k2, cp.v, cp.seq_lens, scale,
+                                    prev_out=cp.prev_out, prev_lse=cp.prev_lse)
+    _twin(f"scale {scale} split", out, o32, o_ref)
+    assert report(f"scale {scale} split LSE", host(lse), l_ref) <= LSE_TOL
 
 
 # ---------------------------------------------------------------------------
@@ -635,24 +728,27 @@ def test_split_workspace_bit_identical(mla):
 def test_dense_valid_lens_padded_batch(mla, B, H, N, lens, seed):
     """Padded batch with per-batch valid lengths (MLA_VALID_LENS): batch b
     equals the oracle on its first lens[b] rows; rows past it are untouched.
-    Value columns are halved (exact) so that |O| < 2: over 128 heads x 1037
-    rows, a few rows that see only a few keys reach |O| > 2 otherwise, where
-    the bf16 output's half ulp (2^-7) alone takes most of the 1e-2 bound."""
+    Rows that see only a few keys reach |O| > 2, so the float32 twin runs
+    too."""
     c = W.dense_case(B=B, H=H, N=N, seed=seed)
-    c.kv = _times_pow2(c.kv, 0.5, slice(0, 512))
     q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    vl = dev(np.array(lens, dtype=np.int32))
     out = torch.full((B, H, N, 512), 7.0, dtype=torch.bfloat16, device="cuda")
     lse = torch.full((B, H, N), 7.0, dtype=torch.float32, device="cuda")
-    mla.fwd(q, kv, scale=c.scale, out=out, lse=lse, valid_lens=dev(np.array(lens, dtype=np.int32)))
+    mla.fwd(q, kv, scale=c.scale, out=out, lse=lse, valid_lens=vl)
+    o32 = torch.full((B, H, N, 512), 7.0, dtype=torch.float32, device="cuda")
+    mla.fwd(q, kv, scale=c.scale, out=o32, lse=torch.empty_like(lse), valid_lens=vl)
     torch.cuda.synchronize()
-    o, l = host(out), host(lse)
+    assert_rne_of("valid lens", out, o32)
+    o, o_f, l = host(out), host(o32), host(lse)
     for b, n in enumerate(lens):
         n = min(n, N)
         if n:
             o_ref, l_ref = oracle.dense_mla(c.q[b:b + 1, :, :n], c.kv[b:b + 1, :, :n], 512, c.scale)
+            assert report(f"b{b} fp32 O", o_f[b:b + 1, :, :n], o_ref) <= O_TOL
             assert report_o(f"b{b} O", o[b:b + 1, :, :n], o_ref) <= 1.0
             assert report(f"b{b} LSE", l[b:b + 1, :, :n], l_ref) <= LSE_TOL
-        assert np.all(o[b, :, n:] == 7.0) and np.all(l[b, :, n:] == 7.0)
+        assert np.all(o[b, :, n:] == 7.0) and np.all(l[b, :, n:] == 7.0) and np.all(o_f[b, :, n:] == 7.0)
 
 
 # ---------------------------------------------------------------------------
@@ -830,16 +926,19 @@ def test_random_shapes_all_forms(mla, seed):
     qo, ko = int(r.integers(0, 300)), int(r.integers(0, 200))
     c = W.dense_case(B=B, H=H, N=N, Nkv=Nkv, seed=seed, causal=causal, q_offset=qo, kv_offset=ko)
     o, l = mla.fwd(dev_bf16(c.q), dev_bf16(c.kv), scale=c.scale, causal=causal, q_offset=qo, kv_offset=ko)
+    o32, _ = mla.fwd(dev_bf16(c.q), dev_bf16(c.kv), scale=c.scale, causal=causal, q_offset=qo, kv_offset=ko,
+                     out=_f32(o))
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, causal=causal, q_offset=qo, kv_offset=ko)
-    assert report_o("random dense O", host(o), o_ref) <= 1.0
+    _twin("random dense", o, o32, o_ref)
     assert report("random dense LSE", host(l), l_ref) <= LSE_TOL
     # sparse: queries, list length, heads
     S, K, Hs = int(r.integers(1, 20)), int(r.integers(1, 700)), int(r.integers(1, 129))
     cs = W.sparse_case(S=S, S_kv=K + 200, pos0=K + 50, H=Hs, K=K, seed=seed)
     o, l = _sparse_gpu(mla, cs)
+    o32, _ = _sparse_gpu(mla, cs, out=_f32(o))
     o_ref, l_ref = oracle.sparse_mla(cs.q_lift, cs.q_pe, cs.c_kv, cs.k_pe, cs.idx, cs.scale)
-    assert report_o("random sparse O", host(o), o_ref) <= 1.0
+    _twin("random sparse", o, o32, o_ref)
     assert report("random sparse LSE", host(l), l_ref) <= LSE_TOL
     # split: sequence lengths (zero allowed), head grouping, prev fold
     lens = [int(x) for x in r.integers(0, 300, int(r.integers(1, 5)))]
@@ -848,10 +947,10 @@ def test_random_shapes_all_forms(mla, seed):
     Hsp = int(r.choice([2, 4, 8]))
     Hkv = int(r.choice([h for h in (1, 2, Hsp) if Hsp % h == 0]))
     cp = W.split_case(seq_lens=lens, H=Hsp, Hkv=Hkv, seed=seed, with_prev=bool(r.integers(0, 2)))
-    o, l = _split_gpu(mla, cp)
+    o, o32, l = _split_twin(mla, cp)
     o_ref, l_ref = oracle.split_mla(cp.q1, cp.q2, cp.k1, cp.k2, cp.v, cp.seq_lens, cp.scale, causal=True,
                                     prev_out=cp.prev_out, prev_lse=cp.prev_lse)
-    assert report_o("random split O", host(o), o_ref) <= 1.0
+    _twin("random split", o, o32, o_ref)
     assert report("random split LSE", host(l), l_ref) <= LSE_TOL
     # decode: sequences, heads, cache rows, valid lengths (zero allowed)
     Bd, Hd, Nd = int(r.integers(1, 6)), int(r.integers(1, 129)), int(r.integers(1, 5000))
