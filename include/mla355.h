@@ -374,6 +374,37 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope,
 size_t mla_decode_workspace_size(int32_t B, int32_t H, int64_t Nkv, int32_t n_splits);
 
 /*
+ * mla_decode_fwd_noalloc -- mla_decode_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, the same kernels and the same
+ * results bit for bit, but no workspace argument.  The partial results and
+ * the item queue's counter live in a static device array of the library,
+ * MLA_DECODE_SCRATCH_BYTES on each GPU it runs on, held until the process
+ * ends; the call itself allocates and frees nothing.  Sizes whose workspace
+ * (mla_decode_workspace_size) exceeds MLA_DECODE_SCRATCH_BYTES return
+ * MLA_ERR_UNSUPPORTED and enqueue nothing.  The workspace is 256 bytes plus,
+ * with more than one key range, (dv + 1) * 4 bytes per (sequence, range,
+ * head), rounded up: at H = 128 up to 319 (sequence, range) pairs fit, e.g.
+ * 64 sequences of 8192 rows in 4 ranges each; a call with one range per
+ * sequence always fits.  Every call on one GPU shares that
+ * GPU's array and leaves its contents behind (each call resets what must
+ * start at zero): calls that may overlap on one GPU (different streams
+ * without ordering between them) race and must not be issued.  The first
+ * call on each device looks the array's address up (hipGetSymbolAddress);
+ * a failure there returns MLA_ERR_HIP.
+ */
+#define MLA_DECODE_SCRATCH_BYTES (80u << 20)
+mla_status mla_decode_fwd_noalloc(const mla_rows* q, const mla_rows* q_rope,
+                                  const mla_rows* kv, const mla_rows* k_rope,
+                                  const int32_t* kv_lens,
+                                  const int32_t* kv_slots, int32_t n_slots,
+                                  int32_t B, int32_t H, int64_t Nkv,
+                                  int32_t dq, int32_t dr, int32_t dv, float scale,
+                                  int32_t n_splits,
+                                  const mla_rows* out, const mla_rows* lse,
+                                  void* stream /* hipStream_t */);
+
+/*
  * mla_vup -- V-up projection of the latent attention output (TensorRT-LLM
  * mla.py, forward_absorption_context and forward_absorption_generation: the
  * per-head product [heads, tokens, kv_lora_rank] x [heads, kv_lora_rank,

@@ -95,6 +95,11 @@ def _load():
     lib.mla_vup.restype = ctypes.c_int
     lib.mla_vup.argtypes = [_P, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                             ctypes.c_int32, ctypes.c_uint32, _P, ctypes.c_void_p]
+    lib.mla_decode_fwd_noalloc.restype = ctypes.c_int
+    lib.mla_decode_fwd_noalloc.argtypes = [_P, _P, _P, _P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_float, ctypes.c_int32, _P, _P, ctypes.c_void_p]
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
     lib.mla_decode_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                               ctypes.c_int32]
@@ -114,7 +119,7 @@ LIB = _load()
 LIB_PATH = _LIB_PATH
 
 EXPORTS = ("mla_fwd", "mla_fwd_group", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd",
-           "mla_vup",
+           "mla_decode_fwd_noalloc", "mla_vup",
            "mla_debug_gather", "mla_last_error", "mla_version", "mla_workspace_size", "mla_decode_workspace_size",
            "mla_ring_fwd", "mla_ring_workspace_size", "mla_ring_schedule")
 
@@ -535,7 +540,7 @@ def decode_fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float,
                q_rope: Optional[torch.Tensor] = None, k_rope: Optional[torch.Tensor] = None,
                n_splits: int = 0, out: Optional[torch.Tensor] = None,
                lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-               workspace: Optional[torch.Tensor] = None
+               workspace: Optional[torch.Tensor] = None, noalloc: bool = False
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Token generation (mla_decode_fwd): q [B, H, dq] (the newest token of
     each sequence), kv [n_slots, Nkv, dq] (the latent cache), optional q_rope
@@ -543,7 +548,10 @@ def decode_fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float,
     (valid rows; None = Nkv), kv_slots int32 [B] on the GPU (the cache slot
     of each sequence; None = slot b).  Returns (out [B, H, dv] bf16, lse [B, H] fp32 or
     None).  n_splits = 0 lets the library split the keys; ``workspace`` (a
-    uint8 GPU tensor) defaults to a cached per-stream buffer."""
+    uint8 GPU tensor) defaults to a cached per-stream buffer.  ``noalloc``:
+    call mla_decode_fwd_noalloc instead, which takes no workspace (the
+    library's static device scratch; ``out``/``lse`` should then be given, so
+    that nothing is allocated here either)."""
     if (q_rope is None) != (k_rope is None):
         raise ValueError("q_rope and k_rope: give both or neither")
     for t, n in ((q, "q"), (kv, "kv")) + (((q_rope, "q_rope"), (k_rope, "k_rope")) if q_rope is not None else ()):
@@ -588,6 +596,13 @@ def decode_fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float,
         vl = MlaRows(lse.data_ptr(), lse.stride(0), lse.stride(1), 0)
     lens_p = kv_lens.data_ptr() if kv_lens is not None else None
     slots_p = kv_slots.data_ptr() if kv_slots is not None else None
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc: the call takes no workspace")
+        _check(LIB.mla_decode_fwd_noalloc(ctypes.byref(vq), _ref(vqr), ctypes.byref(vkv), _ref(vkr), lens_p,
+                                          slots_p, n_slots, B, H, Nkv, dq, dr, dv, float(scale), n_splits,
+                                          ctypes.byref(vo), _ref(vl), _stream(dev_)))
+        return out, lse
     need = int(LIB.mla_decode_workspace_size(B, H, Nkv, n_splits))
     if need == 0:
         raise MlaError(2, f"no key split fits Nkv={Nkv} with n_splits={n_splits}")

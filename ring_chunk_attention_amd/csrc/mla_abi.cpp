@@ -600,13 +600,17 @@ size_t mla_decode_workspace_size(int32_t B, int32_t H, int64_t Nkv, int32_t n_sp
   return decode_ws_bytes(B, H, S, 512, &ol, &oo);
 }
 
-mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
-                          const mla_rows* k_rope, const int32_t* kv_lens, const int32_t* kv_slots,
-                          int32_t n_slots, int32_t B, int32_t H,
-                          int64_t Nkv, int32_t dq, int32_t dr, int32_t dv, float scale,
-                          int32_t n_splits, const mla_rows* out, const mla_rows* lse,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// mla_decode_fwd with its workspace: `scratch` true when the workspace is the
+// library's static one (mla_decode_fwd_noalloc), which bounds the sizes.
+mla_status decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv, const mla_rows* k_rope,
+                      const int32_t* kv_lens, const int32_t* kv_slots, int32_t n_slots, int32_t B, int32_t H,
+                      int64_t Nkv, int32_t dq, int32_t dr, int32_t dv, float scale, int32_t n_splits,
+                      const mla_rows* out, const mla_rows* lse, void* workspace, size_t workspace_bytes,
+                      bool scratch, void* stream) {
   mla_status st;
   if (B < 0 || H <= 0 || Nkv < 0 || n_splits < 0)
     return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, H > 0, Nkv >= 0, n_splits >= 0");
@@ -642,13 +646,25 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_r
                 (long long)Nkv, n_splits);
   size_t off_l, off_o;
   const size_t need = decode_ws_bytes(B, H, S, dv, &off_l, &off_o);
-  if (!workspace) return fail(MLA_ERR_INVALID_ARG, "decode needs a workspace of mla_decode_workspace_size() bytes");
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-    return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < need)
-    return fail(MLA_ERR_INVALID_ARG, "workspace_bytes (%zu) is below mla_decode_workspace_size() (%zu)",
-                workspace_bytes, need);
   if ((int64_t)B * S > kMaxGrid) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (scratch) {
+    if (need > mla::kDecodeScratchBytes)
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "decode without allocation: %d sequences x %d heads x %d key ranges need %zu bytes of "
+                  "partial results, above the library's %zu-byte device scratch (use mla_decode_fwd with a "
+                  "workspace, or fewer sequences or ranges)",
+                  B, H, S, need, (size_t)mla::kDecodeScratchBytes);
+    if (B == 0) return MLA_OK;
+    if ((st = hip_status(mla::decode_scratch(&workspace), "decode scratch lookup"))) return st;
+    workspace_bytes = mla::kDecodeScratchBytes;
+  } else {
+    if (!workspace) return fail(MLA_ERR_INVALID_ARG, "decode needs a workspace of mla_decode_workspace_size() bytes");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MLA_ERR_INVALID_ARG, "workspace_bytes (%zu) is below mla_decode_workspace_size() (%zu)",
+                  workspace_bytes, need);
+  }
   if (B == 0) return MLA_OK;
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -700,6 +716,31 @@ mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_r
   c.out = o_final;
   c.lse = l_final;
   return hip_status(mla::launch_combine(c, s), "decode combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
+                          const mla_rows* k_rope, const int32_t* kv_lens, const int32_t* kv_slots,
+                          int32_t n_slots, int32_t B, int32_t H,
+                          int64_t Nkv, int32_t dq, int32_t dr, int32_t dv, float scale,
+                          int32_t n_splits, const mla_rows* out, const mla_rows* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return decode_fwd(q, q_rope, kv, k_rope, kv_lens, kv_slots, n_slots, B, H, Nkv, dq, dr, dv, scale, n_splits,
+                    out, lse, workspace, workspace_bytes, false, stream);
+}
+
+mla_status mla_decode_fwd_noalloc(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv,
+                                  const mla_rows* k_rope, const int32_t* kv_lens, const int32_t* kv_slots,
+                                  int32_t n_slots, int32_t B, int32_t H,
+                                  int64_t Nkv, int32_t dq, int32_t dr, int32_t dv, float scale,
+                                  int32_t n_splits, const mla_rows* out, const mla_rows* lse, void* stream) {
+  g_last_error.clear();
+  return decode_fwd(q, q_rope, kv, k_rope, kv_lens, kv_slots, n_slots, B, H, Nkv, dq, dr, dv, scale, n_splits,
+                    out, lse, nullptr, 0, true, stream);
 }
 
 mla_status mla_vup(const mla_rows* o, const void* w_uv, int32_t B, int32_t H, int64_t T, int32_t L, int32_t dvh,

@@ -137,4 +137,11 @@ hipError_t launch_vup(const VupParams& p, hipStream_t s);
 // Compute units of the current device, cached per device (0 if unknown).
 int cu_count();
 
+// The decode workspace that mla_decode_fwd_noalloc uses in place of a
+// caller-provided one: a static device array of kDecodeScratchBytes per GPU
+// (mla_scratch.hip).  decode_scratch() returns the current device's copy,
+// looked up on the first call on that device.
+constexpr size_t kDecodeScratchBytes = (size_t)80 << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace mla

@@ -443,3 +443,20 @@ def test_sparse_sizes_whose_products_overflow_are_rejected(lib, B, S, S_kv, msg)
                             B, S, S_kv, 128, 512, 64, 128, 0.07, 0, ctypes.byref(o), None, None, 0, None)
     assert st == MLA_ERR_UNSUPPORTED and msg in lib.mla_last_error().decode()
 
+
+def test_decode_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """64 sequences of 131,072 rows need 64 ranges each: 4096 partial results
+    per head, far past the static scratch.  Refused on the host with a
+    message naming the scratch, before any device call."""
+    from ring_chunk_attention_amd.binding import MlaRows
+    q = MlaRows(FAKE, 128 * 576, 576, 0)
+    kv = MlaRows(FAKE, 131072 * 576, 0, 576)
+    out = MlaRows(FAKE, 128 * 512, 512, 0)
+    st = lib.mla_decode_fwd_noalloc(ctypes.byref(q), None, ctypes.byref(kv), None, None, None, 0,
+                                    64, 128, 131072, 576, 0, 512, 0.072, 0, ctypes.byref(out), None, None)
+    assert st == MLA_ERR_UNSUPPORTED
+    msg = lib.mla_last_error().decode()
+    assert "scratch" in msg and "83886080" in msg, msg
+    # the same sizes with a caller's workspace are a matter of workspace size only
+    need = lib.mla_decode_workspace_size(64, 128, 131072, 0)
+    assert need > 83886080
