@@ -45,13 +45,21 @@ Functions and the passages they follow:
 * :func:`decode_mla`  -- token generation: each sequence's newest query over
   its valid cache rows (Mojo ``mha_single_batch_pipelined``: seq_len = 1,
   ``num_keys``; split-K with a separate reduction).
+* :func:`e4m3_decode`, :func:`dense_mla_fp8` -- the FP8 form: e4m3 codes
+  decoded from the OCP FP8 definition, dequantised by their per-tensor scales
+  and attended as :func:`dense_mla` (TensorRT-LLM ``mla.py``,
+  ``forward_absorption_context`` with the fused FP8 query and the FP8 latent
+  cache; the output stays bf16).  :func:`attention_weights` returns the exact
+  softmax weights from which the tests bound the effect of the kernel's FP8
+  P.V product.
 
 Every function is pinned by ``tests/test_oracle.py`` against brute force on
 tiny inputs, ``torch.nn.functional.scaled_dot_product_attention`` in float64,
 closed forms, hand-worked values and the chunking invariants.
 """
+from .mla_fp8 import attention_weights, dense_mla_fp8, e4m3_decode
 from .mla_ref import (attention, decode_mla, dense_mla, merge, mx4_pack, ring, ring_order, split_mla,
                       sparse_mla, vup)
 
-__all__ = ["attention", "decode_mla", "dense_mla", "merge", "mx4_pack", "ring", "ring_order", "split_mla",
-           "sparse_mla", "vup"]
+__all__ = ["attention", "attention_weights", "decode_mla", "dense_mla", "dense_mla_fp8", "e4m3_decode", "merge",
+           "mx4_pack", "ring", "ring_order", "split_mla", "sparse_mla", "vup"]

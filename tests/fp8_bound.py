@@ -1,0 +1,71 @@
+"""Tolerance of the FP8 form's output, derived from its arithmetic.
+
+The kernel's P.V product runs in FP8: each softmax weight, taken against the
+row's reference max mu (log2 units; mu <= the row max m, and m - mu <= 8),
+is p_j = 2^(s_j - mu) <= 256 and is rounded to e4m3 (round to nearest even):
+  * normal range (p >= 2^-6): |p~ - p| <= 2^-4 p  (3 mantissa bits),
+  * below it (subnormal spacing 2^-9, and flush to zero): |p~ - p| <= 2^-10.
+O is the sum of p~_j v_j over the sum of p~_j (the weights as the product
+sees them).  With the exact normalised weights w_j and the row sum Z =
+sum_j exp(s_j - m) >= 1, D_j = max(2^-4 w_j, 2^-10 / Z) bounds
+|p~_j - p_j| / sum p (because sum p = 2^(m - mu) Z >= Z), and
+
+  O_kernel - O = sum_j Delta_j (v_j - O) / (1 + sum_j Delta_j),  |Delta_j| <= D_j.
+
+Per element c the bound is the smaller of the worst case sum_j D_j |v_jc - O_c|
+and 7 standard deviations of the rounding errors modelled as independent and
+uniform within their bounds (sqrt(sum_j D_j^2 (v_jc - O_c)^2 / 3)), over
+1 - sum_j D_j, plus 1e-3 for the fp32 accumulation and the exponentials and,
+for a bf16 output, half an ulp of the result.  For up to 16 keys the worst
+case is the smaller term (a sum of n bounded terms is at most sqrt(3 n) of
+their standard deviation); for long rows the errors of many independent
+roundings add like a random walk.  The LSE takes the exact fp32 sum of the
+weights before any rounding and keeps the 1e-3 bound of the bf16 form.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+U = 2.0 ** -4        # relative rounding of an e4m3 normal value
+SUB = 2.0 ** -10     # absolute rounding below the e4m3 normal range (in units of 2^(s - mu))
+K_SIGMA = 7.0
+FIXED = 1e-3
+
+
+def o_bound(w: np.ndarray, Z: np.ndarray, v: np.ndarray, o_ref: np.ndarray, bf16: bool = True) -> np.ndarray:
+    """Per-element bound on |O_kernel - O_ref|.  w [R, n] exact weights, Z [R]
+    row sums relative to the row max, v [n, dv] value rows, o_ref [R, dv]."""
+    w = np.asarray(w, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    out = np.empty_like(o_ref)
+    for r in range(w.shape[0]):
+        live = w[r] > 0
+        if not live.any():
+            out[r] = FIXED
+            continue
+        D = np.maximum(U * w[r, live], SUB / Z[r])          # [n_live]
+        dev = np.abs(v[live] - o_ref[r][None, :])           # [n_live, dv]
+        worst = D @ dev
+        rms = np.sqrt((D * D) @ (dev * dev) / 3.0)
+        den = max(1.0 - float(D.sum()), 0.5)
+        out[r] = np.minimum(worst, K_SIGMA * rms) / den + FIXED
+    if bf16:
+        a = np.abs(o_ref)
+        out += 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 8)
+    return out
+
+
+def check(name: str, got: np.ndarray, o_ref: np.ndarray, bound: np.ndarray) -> float:
+    """Largest ratio of |got - o_ref| to the bound (passes at <= 1); prints the
+    worst element and the median ratio."""
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == o_ref.shape, (name, got.shape, o_ref.shape)
+    assert not np.isnan(got).any(), f"{name}: NaN in result"
+    err = np.abs(got - o_ref)
+    ratio = err / bound
+    i = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    print(f"{name}: max abs err {err.max():.3e}, mean {err.mean():.3e}; worst against the fp8 bound "
+          f"{ratio[i]:.3f} at {tuple(int(x) for x in i)} (ref {o_ref[i]:.4f}, err {err[i]:.3e}, bound "
+          f"{bound[i]:.3e}); median ratio {np.median(ratio):.3f}", flush=True)
+    return float(ratio[i])

@@ -244,3 +244,81 @@ def dsv3_vup(seed: int = 0) -> VupCase:
 def dsv3_decode(seed: int = 0) -> DecodeCase:
     return decode_case(B=64, H=128, Nkv=8192, seed=seed,
                        name="DeepSeek-V3 absorbed MLA decode B=64 H=128 KV=8192")
+
+
+# ---------------------------------------------------------------------------
+# FP8 inputs (TensorRT-LLM mla.py, forward_absorption_context: the fused FP8
+# query [tokens, heads, kv_lora_rank + qk_rope_head_dim] in float8_e4m3fn
+# written at unit scale, and the FP8 latent cache with its dequantisation
+# scale).  The codes are the OCP FP8 E4M3 format ("e4m3fn": 1 sign bit, 4
+# exponent bits of bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN,
+# largest finite value 448).  Quantising a draw to a code is input
+# preparation, like the bf16 rounding above; no attention arithmetic.
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float32 -> e4m3fn code (uint8), round to nearest even, saturating at
+    +-448 (the draws are finite)."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << np.uint8(7)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    # exponent of the binade (the subnormals share the smallest normal's spacing 2^-9)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -7)))
+    e = np.maximum(e, -6.0)
+    spacing = 2.0 ** (e - 3)
+    n = np.round(a / spacing)                 # numpy rounds halves to even
+    v = n * spacing                           # representable: n <= 16 carries into the next binade
+    ev = np.floor(np.log2(np.maximum(v, 2.0 ** -7)))
+    normal = v >= 2.0 ** -6
+    exp_bits = np.where(normal, ev + 7, 0).astype(np.int64)
+    man = np.where(normal, v / 2.0 ** (ev - 3) - 8, v / 2.0 ** -9)
+    code = (exp_bits << 3) | np.rint(man).astype(np.int64)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def normal_e4m3(rng: np.random.Generator, shape, std: float = 1.0, chunk: int = 1 << 26) -> np.ndarray:
+    """Draw N(0, std^2) float32 and store it as e4m3 codes at unit scale, in
+    bounded chunks."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = to_e4m3_codes(rng.standard_normal(e - s, dtype=np.float32) * np.float32(std))
+    return out.reshape(shape)
+
+
+@dataclass
+class Fp8DenseCase:
+    """Shared-latent causal attention over FP8 inputs: q8 [B,H,N,576] and kv8
+    [B,1,Nkv,576] e4m3 codes, dequantised as code * q_scale and
+    code * kv_scale."""
+    q8: np.ndarray
+    kv8: np.ndarray
+    q_scale: float
+    kv_scale: float
+    head_dim_v: int
+    scale: float
+    causal: bool = True
+    q_offset: int = 0
+    kv_offset: int = 0
+    name: str = ""
+
+
+def fp8_dense_case(B: int = 1, H: int = 4, N: int = 128, Nkv: Optional[int] = None, dk: int = 576,
+                   dv: int = 512, seed: int = 0, scale: float = SCALE_192, q_scale: float = 1.0,
+                   kv_scale: float = 1.0, causal: bool = True, q_offset: int = 0, kv_offset: int = 0,
+                   name: str = "") -> Fp8DenseCase:
+    """q8 then kv8, each N(0, 1) / its scale quantised to e4m3 (so that the
+    dequantised values are about N(0, 1) whatever the scales)."""
+    rng = np.random.default_rng(seed)
+    Nkv = N if Nkv is None else Nkv
+    q8 = normal_e4m3(rng, (B, H, N, dk), std=1.0 / q_scale)
+    kv8 = normal_e4m3(rng, (B, 1, Nkv, dk), std=1.0 / kv_scale)
+    return Fp8DenseCase(q8, kv8, q_scale, kv_scale, dv, scale, causal, q_offset, kv_offset, name)
+
+
+def dsv3_prefill_fp8(seed: int = 0) -> Fp8DenseCase:
+    return fp8_dense_case(B=1, H=128, N=8192, seed=seed,
+                          name="DeepSeek-V3 absorbed MLA prefill, FP8 e4m3 Q and KV, H=128 N=8192")
