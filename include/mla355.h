@@ -163,6 +163,38 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope,
                    void* stream /* hipStream_t */);
 
 /*
+ * mla_fwd_fp8 -- the shared-latent attention over FP8 inputs (TensorRT-LLM
+ * mla.py, forward_absorption_context: the fused FP8 query and the FP8 latent
+ * cache in float8_e4m3fn with the BMM1 and BMM2 scales; the output stays
+ * bf16).
+ *
+ * q8 [B, Hq, Nq, 576] and kv8 [B, 1, Nkv, 576]: OCP FP8 E4M3 codes (one byte
+ * per element; mla_rows views with strides in bytes, data and strides
+ * multiples of 16, the kv8 view's stride_h ignored), dequantised as
+ * code * q_scale and code * kv_scale (positive, finite; 1 for the page's
+ * unit-scale fused query).  The score is scale * q . kv over all 576 columns,
+ * the value the first 512 dequantised columns of the kv row; masking and
+ * offsets as mla_fwd (flags: 0 or MLA_CAUSAL).
+ *
+ * Arithmetic: both products run on 8-bit MFMA with fp32 accumulation; the
+ * softmax weights are rounded to e4m3 for the P.V product, each taken
+ * against its row's reference max (so a weight is at most 2^8); O is divided
+ * by the sum of the rounded weights, and lse (natural log, fp32) uses the
+ * exact sum.  An e4m3 weight carries 3 mantissa bits, so O differs from the
+ * exact attention of the dequantised inputs by up to a few percent of the
+ * spread of the values on rows dominated by few keys (less on long rows);
+ * the LSE is as exact as in the bf16 form.
+ *
+ * out [B, Hq, Nq, 512] bf16 (round to nearest even); lse [B, Hq, Nq] or NULL.
+ * workspace: as mla_fwd (the item queue's counter).  Kernels exist for
+ * dk == 576, dv == 512; other shapes return MLA_ERR_UNSUPPORTED.
+ */
+mla_status mla_fwd_fp8(const mla_rows* q8, const mla_rows* kv8, int32_t B, int32_t Hq, int64_t Nq, int64_t Nkv,
+                       int32_t dk, int32_t dv, float scale, float q_scale, float kv_scale, uint32_t flags,
+                       int64_t q_offset, int64_t kv_offset, const mla_rows* out, const mla_rows* lse,
+                       void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+
+/*
  * mla_fwd_group -- up to MLA_MAX_GROUP shared-latent mla_fwd calls in one
  * launch: one ring step for every query chunk at once (TT-NN ring_mla, the
  * ring's steps; Ascend RingMLAOperation, one call per ring step).  Each call

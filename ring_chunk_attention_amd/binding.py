@@ -66,6 +66,11 @@ def _load():
         ctypes.c_void_p, ctypes.c_int32,
         ctypes.c_float, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64,
         _P, _P, _P, _P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mla_fwd_fp8.restype = ctypes.c_int
+    lib.mla_fwd_fp8.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_void_p,
+                                ctypes.c_size_t, ctypes.c_void_p]
     lib.mla_fwd_group.restype = ctypes.c_int
     lib.mla_fwd_group.argtypes = [ctypes.c_int32, ctypes.POINTER(MlaFwdCall), ctypes.c_void_p]
     lib.mla_merge_lse.restype = ctypes.c_int
@@ -118,7 +123,7 @@ def _load():
 LIB = _load()
 LIB_PATH = _LIB_PATH
 
-EXPORTS = ("mla_fwd", "mla_fwd_group", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd",
+EXPORTS = ("mla_fwd", "mla_fwd_fp8", "mla_fwd_group", "mla_merge_lse", "mla_sparse_fwd", "mla_decode_fwd",
            "mla_decode_fwd_noalloc", "mla_vup",
            "mla_debug_gather", "mla_last_error", "mla_version", "mla_workspace_size", "mla_decode_workspace_size",
            "mla_ring_fwd", "mla_ring_workspace_size", "mla_ring_schedule")
@@ -320,6 +325,43 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, *, scale: float, head_dim_v: int = 51
                        lens_ptr, a["B"] if lens_ptr else 0, a["scale"], flags, a["q_offset"], a["kv_offset"],
                        _ref(a["prev_out"]), _ref(a["prev_lse"]), ctypes.byref(a["out"]), _ref(a["lse"]),
                        ws, ws_bytes, _stream(q.device)))
+    return out, lse
+
+
+def fwd_fp8(q8: torch.Tensor, kv8: torch.Tensor, *, scale: float, q_scale: float = 1.0, kv_scale: float = 1.0,
+            causal: bool = True, q_offset: int = 0, kv_offset: int = 0, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, want_lse: bool = True, workspace="auto"
+            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Shared-latent attention over FP8 e4m3 inputs (mla_fwd_fp8): q8
+    [B, H, N, 576] and kv8 [B, 1, Nkv, 576] as torch.float8_e4m3fn (or uint8
+    codes), dequantised by q_scale and kv_scale.  Returns (out [B, H, N, 512]
+    bf16, lse [B, H, N] fp32 or None).  ``workspace`` as for fwd."""
+    for t, n in ((q8, "q8"), (kv8, "kv8")):
+        if not isinstance(t, torch.Tensor) or t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError(f"{n}: expected a float8_e4m3fn (or uint8 code) tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{n}: must be a GPU tensor")
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{n}: expected [B, H, N, D] with a contiguous last dim")
+    B, H, N, dk = q8.shape
+    Nkv = kv8.shape[2]
+    dev_ = q8.device
+    _shape(kv8, "kv8", (B, 1, Nkv, dk), dev_)
+    if out is None:
+        out = torch.empty((B, H, N, 512), dtype=torch.bfloat16, device=dev_)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev_)
+    _shape(out, "out", (B, H, N, 512), dev_)
+    if lse is not None:
+        _shape(lse, "lse", (B, H, N), dev_)
+    vq = MlaRows(q8.data_ptr(), q8.stride(0), q8.stride(1), q8.stride(2))
+    vkv = MlaRows(kv8.data_ptr(), kv8.stride(0), kv8.stride(1), kv8.stride(2))
+    vo = _rows_bhtd(out, "out")
+    vl = _lse_bht(lse, "lse") if lse is not None else None
+    ws, ws_bytes = _workspace(dev_, workspace)
+    _check(LIB.mla_fwd_fp8(ctypes.byref(vq), ctypes.byref(vkv), B, H, N, Nkv, dk, 512, float(scale),
+                           float(q_scale), float(kv_scale), MLA_CAUSAL if causal else 0, int(q_offset),
+                           int(kv_offset), ctypes.byref(vo), _ref(vl), ws, ws_bytes, _stream(dev_)))
     return out, lse
 
 

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla355.so")
 
-SOURCES = ["mla_attn.hip", "mla_attn_split.hip", "mla_merge.hip", "mla_vup.hip", "mla_scratch.hip", "mla_abi.cpp"]
+SOURCES = ["mla_attn.hip", "mla_attn_split.hip", "mla_attn_fp8.hip", "mla_merge.hip", "mla_vup.hip", "mla_scratch.hip",
+           "mla_abi.cpp"]
 
 # Per-source device flags: the split form keeps its MFMA accumulators in
 # VGPRs (an LLVM option, given to the device compile only).

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "mla_internal.h"
@@ -382,6 +383,62 @@ mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows* kv
   if (form == FORM_LATENT) return hip_status(mla::launch_latent_dense(p, s), "latent attention launch");
   if (form == FORM_SPLIT) return hip_status(mla::launch_split(p, s), "split attention launch");
   return MLA_OK;
+}
+
+mla_status mla_fwd_fp8(const mla_rows* q8, const mla_rows* kv8, int32_t B, int32_t Hq, int64_t Nq, int64_t Nkv,
+                       int32_t dk, int32_t dv, float scale, float q_scale, float kv_scale, uint32_t flags,
+                       int64_t q_offset, int64_t kv_offset, const mla_rows* out, const mla_rows* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mla_status st;
+  if (B < 0 || Hq <= 0 || Nq < 0 || Nkv < 0)
+    return fail(MLA_ERR_INVALID_ARG, "sizes: need B >= 0, Hq > 0, Nq >= 0, Nkv >= 0");
+  if (dk != 576 || dv != 512)
+    return fail(MLA_ERR_UNSUPPORTED, "the FP8 form is built for dk = 576 (512 latent + 64 RoPE), dv = 512 (got %d, %d)",
+                dk, dv);
+  if (flags & ~MLA_CAUSAL) return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags & ~MLA_CAUSAL);
+  if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
+  if (!(std::isfinite(q_scale) && q_scale > 0.f) || !(std::isfinite(kv_scale) && kv_scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "q_scale and kv_scale must be finite and positive");
+  if (!std::isfinite(scale * q_scale * kv_scale * kLog2e))
+    return fail(MLA_ERR_INVALID_ARG, "scale * q_scale * kv_scale overflows float");
+  if ((st = check_workspace(workspace, workspace_bytes))) return st;
+  const bool no_q = B == 0 || Nq == 0, no_kv = B == 0 || Nkv == 0;
+  // e4m3 rows: one byte per element, rows 16-byte aligned
+  for (auto [r, name, empty] : {std::tuple{q8, "q8", no_q}, std::tuple{kv8, "kv8", no_kv}}) {
+    if (!r) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+    if (!r->data && !empty) return fail(MLA_ERR_INVALID_ARG, "%s: missing", name);
+    if (!aligned16(r->data)) return fail(MLA_ERR_INVALID_ARG, "%s: data pointer must be 16-byte aligned", name);
+    if (r->stride_b < 0 || r->stride_h < 0 || r->stride_t < 0)
+      return fail(MLA_ERR_INVALID_ARG, "%s: negative stride", name);
+    if (r->stride_b % 16 || r->stride_h % 16 || r->stride_t % 16)
+      return fail(MLA_ERR_INVALID_ARG, "%s: strides must be multiples of 16 bytes", name);
+  }
+  if ((st = check_rows(out, "out", true, no_q))) return st;
+  if (lse && (st = check_lse(lse, "lse", no_q))) return st;
+  if (kv8->stride_t > (1 << 24)) return fail(MLA_ERR_UNSUPPORTED, "kv8 rows must lie less than 16 MiB apart");
+  const int64_t n_qblk = Nq / 32 + (Nq % 32 != 0), n_hgrp = (Hq + 3) / 4;
+  if (!fits_grid({n_qblk, n_hgrp, B})) return fail(MLA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (no_q) return MLA_OK;
+  mla::AttnParams p{};
+  p.qa = mla::RowsC{static_cast<const uint16_t*>(q8->data), q8->stride_b, q8->stride_h, q8->stride_t};
+  p.ka = mla::RowsC{static_cast<const uint16_t*>(kv8->data), kv8->stride_b, kv8->stride_h, kv8->stride_t};
+  p.out = rm(out);
+  p.lse = lm(lse);
+  p.B = B;
+  p.Hq = Hq;
+  p.group = Hq;
+  p.Nq = Nq;
+  p.Nkv = Nkv;
+  p.q_offset = q_offset;
+  p.kv_offset = kv_offset;
+  p.scale_log2 = scale * q_scale * kv_scale * kLog2e;
+  p.v_scale = kv_scale;
+  p.causal = (flags & MLA_CAUSAL) ? 1 : 0;
+  p.n_qblk = (int32_t)n_qblk;
+  p.n_hgrp = (int32_t)n_hgrp;
+  p.queue = static_cast<unsigned*>(workspace);
+  return hip_status(mla::launch_latent_fp8(p, static_cast<hipStream_t>(stream)), "FP8 attention launch");
 }
 
 mla_status mla_fwd_group(int32_t n, const mla_fwd_call* calls, void* stream) {

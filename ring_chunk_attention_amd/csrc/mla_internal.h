@@ -68,6 +68,7 @@ struct AttnParams {
   const int32_t* kv_lens;   // decode: valid rows per sequence [B], or nullptr (Nkv)
   const int32_t* kv_slots;  // decode: cache slot of each sequence [B], or nullptr (slot b)
   int32_t n_slots;          // decode: slots of the cache
+  float v_scale;            // FP8 form: dequantisation scale of the value rows (applied to O)
 };
 
 // Several shared-latent calls in one launch (a ring step for all query
@@ -133,6 +134,7 @@ hipError_t launch_decode(const AttnParams& p, int64_t items, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_debug_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_vup(const VupParams& p, hipStream_t s);
+hipError_t launch_latent_fp8(const AttnParams& p, hipStream_t s);
 
 // Compute units of the current device, cached per device (0 if unknown).
 int cu_count();
