@@ -12,7 +12,7 @@ Rank 0 prints ONE JSON line with the headline, its roofline against the
 dense bf16 MFMA peak, the fp64 CPU oracle timed on a bounded sample of the
 same workload, and measured lines for the other steps of the path (one-device
 ring with LSE folds, split varlen ring step, sparse top-k, standalone merge,
-token-generation decode, V-up projection).
+token-generation decode, V-up projection, and the headline shape in FP8).
 """
 from __future__ import annotations
 
@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA: 256 CU x 8192 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "causal MLA prefill TFLOP/s and % of bf16 MFMA peak on 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_latent_dsv3_prefill_hbm_traffic.json")
@@ -315,7 +316,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
-    ap.add_argument("--only-row", choices=["ring", "merge", "split", "sparse", "decode", "vup"],
+    ap.add_argument("--only-row", choices=["ring", "merge", "split", "sparse", "decode", "vup", "fp8"],
                     help="time this one row alone (no headline, no CPU baseline): for profiling a kernel")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one plain device copy of 1 GiB (HBM counter calibration)")
@@ -529,6 +530,26 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
             "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
             "GBps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
             "bytes": nbytes}
+        del o, w, vo
+
+    if only in (None, "fp8"):
+        # the headline workload with FP8 e4m3 Q and KV (unit scales), both
+        # products on 8-bit MFMA, bf16 output and fp32 LSE
+        print("bench: FP8 prefill workload", file=sys.stderr, flush=True)
+        c = W.dsv3_prefill_fp8(0)
+        q8 = torch.from_numpy(c.q8).cuda().view(torch.float8_e4m3fn)
+        kv8 = torch.from_numpy(c.kv8).cuda().view(torch.float8_e4m3fn)
+        B, H, N, _ = c.q8.shape
+        fo = torch.empty((B, H, N, 512), dtype=torch.bfloat16, device="cuda")
+        fl_ = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        ms, _, _ = time_launches(lambda: mla.fwd_fp8(q8, kv8, scale=c.scale, out=fo, lse=fl_), steps, warmup,
+                                 per_launch=False)
+        fl = B * H * causal_pairs(N, N) * 2176
+        rows["prefill_fp8_dsv3_h128_n8192"] = {
+            "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
+            "pct_of_fp8_peak": round(100 * fl / ms / 1e9 / PEAK_FP8_TFLOPS, 2),
+            "peak_tflops": PEAK_FP8_TFLOPS, "dtype": "e4m3 inputs and P, fp32 accumulation, bf16 out"}
+        del q8, kv8, fo, fl_
     return rows
 
 

@@ -260,22 +260,17 @@ E4M3_MAX = 448.0
 
 def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
     """float32 -> e4m3fn code (uint8), round to nearest even, saturating at
-    +-448 (the draws are finite)."""
-    x = np.asarray(x, dtype=np.float64)
-    sign = (np.signbit(x)).astype(np.uint8) << np.uint8(7)
-    a = np.minimum(np.abs(x), E4M3_MAX)
-    # exponent of the binade (the subnormals share the smallest normal's spacing 2^-9)
-    e = np.floor(np.log2(np.maximum(a, 2.0 ** -7)))
-    e = np.maximum(e, -6.0)
-    spacing = 2.0 ** (e - 3)
-    n = np.round(a / spacing)                 # numpy rounds halves to even
-    v = n * spacing                           # representable: n <= 16 carries into the next binade
-    ev = np.floor(np.log2(np.maximum(v, 2.0 ** -7)))
-    normal = v >= 2.0 ** -6
-    exp_bits = np.where(normal, ev + 7, 0).astype(np.int64)
-    man = np.where(normal, v / 2.0 ** (ev - 3) - 8, v / 2.0 ** -9)
-    code = (exp_bits << 3) | np.rint(man).astype(np.int64)
-    return (code.astype(np.uint8) | sign).astype(np.uint8)
+    +-448 (the draws are finite).  On the float32 bit patterns: in the normal
+    range the 20 mantissa bits e4m3 drops are rounded off and the exponent
+    is rebiased from 127 to 7; below 2^-6 the value is a multiple of 2^-9."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    sign = ((u >> np.uint32(24)) & np.uint32(0x80)).astype(np.uint8)
+    a = u & np.uint32(0x7FFFFFFF)
+    r = (a + np.uint32(0x7FFFF) + ((a >> np.uint32(20)) & np.uint32(1))) >> np.uint32(20)
+    code = np.minimum(r.astype(np.int64) - ((127 - 7) << 3), 0x7E)          # 0x7E = 448
+    small = a < np.uint32(0x3C800000)                                         # |x| < 2^-6
+    code[small] = np.rint(a[small].view(np.float32) * np.float32(512.0)).astype(np.int64)
+    return code.astype(np.uint8) | sign
 
 
 def normal_e4m3(rng: np.random.Generator, shape, std: float = 1.0, chunk: int = 1 << 26) -> np.ndarray:
