@@ -117,6 +117,73 @@ def time_launches(fn, steps: int, warmup: int, hold: bool = False, per_launch: b
     return region, float(np.mean(per)), float(np.min(per))
 
 
+SCLK_FILES = ("/sys/class/drm/card0/device/pp_dpm_sclk",)
+
+
+class ClockSampler:
+    """Samples the GPU engine clock while work runs: the driver's
+    pp_dpm_sclk lists the clock levels and marks the current one with '*'
+    (the current engine clock in MHz).  Used as a context manager around a
+    timed region; `mhz` is the list of samples."""
+
+    def __init__(self, period_s: float = 0.002):
+        import threading
+        self.period = period_s
+        self.mhz = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self.path = next((p for p in SCLK_FILES if os.path.exists(p)), None)
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*[Mm]hz", line)
+                    if m:
+                        return int(m.group(1))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except OSError:
+                return
+            if v:
+                self.mhz.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def summary(self):
+        """Median of the samples taken above idle (a busy engine runs above
+        1 GHz; idle gaps between launches read a few hundred MHz)."""
+        busy = sorted(v for v in self.mhz if v >= 1000)
+        if not busy:
+            return None
+        return {"median_mhz": busy[len(busy) // 2], "min_mhz": busy[0], "max_mhz": busy[-1],
+                "samples": len(busy), "source": self.path}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, budget_s: float = 12.0):
     """The fp64 oracle on whole heads of the same workload until the budget is
     spent; throughput on the same algorithmic flop count."""
@@ -136,21 +203,28 @@ def cpu_baseline(case, budget_s: float = 12.0):
         heads += 1
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "logical_cpus_visible": len(os.sched_getaffinity(0)),
             "sample": f"fp64 NumPy oracle on heads 0..{heads - 1} of {H} (all {N} causal rows each), "
                       f"{dt:.1f} s wall, same flop count per head as the GPU"}
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+ROW_TRAFFIC = {   # row -> (kernel name substring, committed traffic summary)
+    "sparse": ("LatentCfg, 3>", os.path.join(ROOT, "profiles", "attn_fwd_sparse_topk_s4096_k2048_hbm_traffic.json")),
+    "decode": ("LatentCfg, 3>", os.path.join(ROOT, "profiles", "attn_fwd_decode_b64_kv8192_hbm_traffic.json")),
+}
+
+
+def measured_traffic(path=TRAFFIC_FILE, full=False):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (``full``: the whole summary)."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_sha256_16") != kernel_hash():
         return None
-    return t.get("bytes_per_launch")
+    return t if full else t.get("bytes_per_launch")
 
 
 ATTN_KERNEL = "attn_fwd_kernel<mla::(anonymous namespace)::LatentCfg"
@@ -259,8 +333,9 @@ def summarize_counters(folders, kernel, out_path, cmds):
     print("\n".join(lines))
 
 
-def _counter_means(folder, counter):
-    """Mean value of `counter` per dispatch of each kernel (rocprofv3 csv)."""
+def _counter_means(folder, counter, reduce=None):
+    """Mean value of `counter` per dispatch of each kernel (rocprofv3 csv), or
+    another reduction over the dispatches (``reduce``, e.g. max)."""
     import csv
     files = _csvs(folder, "counter_collection.csv")
     if not files:
@@ -274,28 +349,34 @@ def _counter_means(folder, counter):
     means = {}
     for (name, _), v in per.items():
         means.setdefault(name, []).append(v)
-    return {k: sum(v) / len(v) for k, v in means.items()}
+    return {k: (reduce(v) if reduce else sum(v) / len(v)) for k, v in means.items()}
 
 
-def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
-    """HBM bytes per launch of the attention kernel: FETCH_SIZE and WRITE_SIZE
-    (KiB per dispatch) scaled by what they read for a plain 1 GiB device copy
-    in the same run; written with the hash of the kernel source it was taken
-    on, so that a later kernel change makes bench.py report null."""
+def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write, kernel=ATTN_KERNEL, out=TRAFFIC_FILE,
+                      label="attn_fwd_kernel<LatentCfg, LATENT>",
+                      workload="DeepSeek-V3-shaped absorbed MLA prefill, causal, B=1 H=128 N=8192"):
+    """HBM bytes per launch of a kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch, averaged over its dispatches) scaled by what they read for a
+    plain 1 GiB device copy in the same run; written with the hash of the
+    kernel source it was taken on, so that a later kernel change makes
+    bench.py report null."""
     def pick(means, key):
         hits = [v for k, v in means.items() if key in k]
         if not hits:
             sys.exit(f"kernel {key!r} not found; kernels: {list(means)}")
         return hits[0]
     fm, wm = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
-    f_attn, w_attn = pick(fm, ATTN_KERNEL), pick(wm, ATTN_KERNEL)
-    f_copy, w_copy = pick(fm, COPY_KERNEL), pick(wm, COPY_KERNEL)
+    f_attn, w_attn = pick(fm, kernel), pick(wm, kernel)
+    # the calibration copy is the largest copy dispatch (small blits of the
+    # inputs' upload may share the kernel)
+    f_copy = pick(_counter_means(fetch_dir, "FETCH_SIZE", max), COPY_KERNEL)
+    w_copy = pick(_counter_means(write_dir, "WRITE_SIZE", max), COPY_KERNEL)
     f_scale = COPY_BYTES / (f_copy * 1024.0)   # the copy reads COPY_BYTES
     w_scale = COPY_BYTES / (w_copy * 1024.0)   # and writes COPY_BYTES
     fetch_b = f_attn * 1024.0 * f_scale
     write_b = w_attn * 1024.0 * w_scale
-    res = {"kernel": "attn_fwd_kernel<LatentCfg, LATENT>",
-           "workload": "DeepSeek-V3-shaped absorbed MLA prefill, causal, B=1 H=128 N=8192",
+    res = {"kernel": label,
+           "workload": workload,
            "kernel_sha256_16": kernel_hash(),
            "fetch_kib_raw": round(f_attn, 1), "write_kib_raw": round(w_attn, 1),
            "copy_1GiB_fetch_kib_raw": round(f_copy, 1), "copy_1GiB_write_kib_raw": round(w_copy, 1),
@@ -303,10 +384,19 @@ def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
            "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
            "bytes_per_launch": int(fetch_b + write_b),
            "cmd_fetch": cmd_fetch, "cmd_write": cmd_write}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(out, "w") as f:
         json.dump(res, f, indent=1)
         f.write("\n")
     print(json.dumps(res, indent=1))
+
+
+def copy_calibration():
+    """One plain device copy of 1 GiB: the HBM counters' calibration."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -327,6 +417,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="write a summary of rocprofv3 --pmc csv runs (one folder per pass) to --out, then exit")
     ap.add_argument("--kernel", default="attn_fwd", help="kernel name substring for --summarize-counters")
+    ap.add_argument("--traffic-row", choices=sorted(ROW_TRAFFIC),
+                    help="--summarize-traffic for this row's kernel (written to the row's summary file)")
     ap.add_argument("--out", help="output file of --summarize-stats / --summarize-counters")
     ap.add_argument("--cmd", nargs="*", default=[],
                     help="the profiling command(s) the summary came from, recorded in it")
@@ -339,7 +431,14 @@ def main():
         return
     if args.summarize_traffic:
         cf, cw = (args.cmd + ["", ""])[:2]
-        summarize_traffic(*args.summarize_traffic, cf, cw)
+        if args.traffic_row:
+            kern, path = ROW_TRAFFIC[args.traffic_row]
+            wl = {"sparse": "sparse top-k latent MLA, S=4096 S_kv=16384 H=128 K=2048 (drawn, unsorted lists)",
+                  "decode": "MLA decode, B=64 sequences x 8192 cache rows, H=128 (4 key ranges of 2048)"}
+            summarize_traffic(*args.summarize_traffic, cf, cw, kernel=kern, out=path,
+                              label="attn_fwd_kernel<LatentCfg, SPARSE_PIPE>", workload=wl[args.traffic_row])
+        else:
+            summarize_traffic(*args.summarize_traffic, cf, cw)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
@@ -355,6 +454,8 @@ def main():
 
     if args.only_row:
         rows = measure_rows(mla, W, to_dev, args.steps, args.warmup, only=args.only_row)
+        if args.copy_calib:
+            copy_calibration()
         print(json.dumps({"row": args.only_row, **rows}), flush=True)
         return
 
@@ -369,17 +470,16 @@ def main():
         mla.fwd(q, kv, scale=case.scale, head_dim_v=512, causal=True, out=out, lse=lse)
 
     print("bench: timing", file=sys.stderr, flush=True)
-    region_ms, launch_ms, launch_min_ms = time_launches(step, args.steps, args.warmup)
+    with ClockSampler() as clk:
+        region_ms, launch_ms, launch_min_ms = time_launches(step, args.steps, args.warmup)
     flops = B * H * causal_pairs(N, N) * (2 * dk + 2 * 512)
     value = flops / (region_ms * 1e-3) / 1e12
     achieved = flops / (launch_ms * 1e-3) / 1e12
     traffic = measured_traffic()
+    clock = clk.summary()
 
     if args.copy_calib:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration()
 
     result = {
         "metric": METRIC,
@@ -403,7 +503,13 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "attn_fwd_kernel<LatentCfg, LATENT>",
                      "launch_ms_mean": round(launch_ms, 4), "launch_ms_min": round(launch_min_ms, 4)},
+        "engine_clock": clock,
     }
+    if clock:
+        # the same achieved rate against the peak at the clock the engine ran at
+        peak_at = PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0
+        result["roofline"]["frac_at_measured_clock"] = round(achieved / peak_at, 4)
+        result["roofline"]["peak_at_measured_clock"] = round(peak_at, 1)
     del q, kv, out, lse
     torch.cuda.empty_cache()
 
@@ -490,7 +596,14 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
         rows["sparse_topk_s4096_k2048_h128"] = {
             "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
             "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-            "gather_GBps": round(gathered / ms / 1e6, 1)}
+            "gather_GBps": round(gathered / ms / 1e6, 1),
+            "compulsory_bytes": sum(x.numel() * x.element_size() for x in (*t, idx, so, sL)),
+            "gathered_bytes": gathered}
+        tr = measured_traffic(ROW_TRAFFIC["sparse"][1], full=True)
+        if tr:
+            rows["sparse_topk_s4096_k2048_h128"].update(
+                hbm_bytes_measured=tr["bytes_per_launch"], hbm_fetch_bytes=tr["fetch_bytes"],
+                hbm_GBps_measured=round(tr["bytes_per_launch"] / ms / 1e6, 1))
         del t, idx, so, sL
 
     if only in (None, "decode"):
@@ -513,6 +626,10 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
             "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
             "GBps": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
             "bytes": nbytes}
+        tr = measured_traffic(ROW_TRAFFIC["decode"][1], full=True)
+        if tr:
+            rows["decode_b64_kv8192_h128"].update(
+                hbm_bytes_measured_attention_kernel=tr["bytes_per_launch"], hbm_fetch_bytes=tr["fetch_bytes"])
         del q, kv, lens, do, dl
 
     if only in (None, "vup"):

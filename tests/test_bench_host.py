@@ -52,3 +52,24 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_clock_sampler_reads_the_marked_level(tmp_path, monkeypatch):
+    """The engine clock is the level pp_dpm_sclk marks with '*'; samples
+    below 1 GHz (idle gaps) are left out of the summary."""
+    import time
+    import bench
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1834Mhz *\n2: 2400Mhz\n")
+    monkeypatch.setattr(bench, "SCLK_FILES", (str(f),))
+    with bench.ClockSampler(period_s=0.001) as clk:
+        time.sleep(0.02)
+        f.write_text("0: 500Mhz\n1: 189Mhz *\n2: 2400Mhz\n")
+        time.sleep(0.02)
+    s = clk.summary()
+    assert s["median_mhz"] == 1834 and s["min_mhz"] == 1834 and s["samples"] >= 2
+    assert 189 in clk.mhz
+    monkeypatch.setattr(bench, "SCLK_FILES", (str(tmp_path / "missing"),))
+    with bench.ClockSampler() as clk:
+        pass
+    assert clk.summary() is None
