@@ -188,11 +188,20 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) vaddr[j][q] = vb ^ (uint32_t)(32 * j + 16 * q);
   }
-  const uint32_t lds_p = lds_addr(&sm.p[0][0][0][0]);
+  const uint32_t lds_pl = lds_addr(&sm.p[0][0][0][0]) + (uint32_t)lane * 16u;  // this lane's slot of the P operands
 
-  // S^T halves of tile `buf` (lane: query row lr; keys 32kh + 8(r/4) + 4h + r%4)
+  // S^T halves of tile `buf` (lane: query row lr; keys 32kh + 8(r/4) + 4h + r%4).
+  // The lane's fragment bases are formed once per tile; the k-step and key
+  // half become instruction offsets.
   auto qk = [&](int buf, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
     const uint32_t tb = lds_t + (uint32_t)buf * F8_TILE;
+    uint32_t kb[2][2], kr[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      kb[e][0] = tb + koff[e][0];
+      kb[e][1] = tb + koff[e][1];
+      kr[e] = tb + kropw[e];
+    }
 #pragma unroll
     for (int c = 0; c < F8_KS; ++c) {
       i32x8 a[2];
@@ -200,12 +209,11 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
       for (int kh = 0; kh < 2; ++kh) {
         i32x4 x0, x1;
         if (c < 8) {
-          const uint32_t o = tb + (uint32_t)(c >> 1) * 1024u + (uint32_t)kh * 16384u;
-          x0 = lds16(o + koff[0][c & 1]);
-          x1 = lds16(o + koff[1][c & 1]);
+          x0 = lds16(kb[0][c & 1] + (uint32_t)((c >> 1) * 1024 + kh * 16384));
+          x1 = lds16(kb[1][c & 1] + (uint32_t)((c >> 1) * 1024 + kh * 16384));
         } else {
-          x0 = lds16(tb + kropw[0] + (uint32_t)kh * 2048u);
-          x1 = lds16(tb + kropw[1] + (uint32_t)kh * 2048u);
+          x0 = lds16(kr[0] + (uint32_t)(kh * 2048));
+          x1 = lds16(kr[1] + (uint32_t)(kh * 2048));
         }
         a[kh] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
@@ -239,12 +247,11 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
   bool over = false;
   const float sm_scale = p.scale_log2 > 0.f ? p.scale_log2 : 1.f;
 
-  // Softmax of one tile's scores: row max and reference, weights, their
-  // exact and rounded sums, and the e4m3 P^T operand of this wave's rows
-  // written to P buffer pb.  live == false: no tile (all masked).
-  auto softmax = [&](f32x16& s0, f32x16& s1, int t, bool live, int pb) __attribute__((always_inline)) {
+  // The scores of one tile as this lane's 32 values (half kh: x[16 kh + r]),
+  // scaled when the scale is not positive, and masked (-inf) where the tile
+  // cuts the causal bound or the end of the keys (live == false: no tile).
+  auto prep = [&](const f32x16& s0, const f32x16& s1, int t, bool live, float* x) __attribute__((always_inline)) {
     const int k0 = t * F8_BN;
-    float x[32];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       x[r] = s0[r];
@@ -263,12 +270,19 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
         x[r] = kk < bound ? x[r] : -INFINITY;
       }
     }
+  };
+
+  // Softmax of prepared scores: row max and reference, weights, their exact
+  // and rounded sums, and the e4m3 P^T operand of this wave's rows written
+  // to P buffer pb.  Branch-free, so that it can be spread over the P.V
+  // products.
+  auto softmax = [&](float* x, int pb) __attribute__((always_inline)) {
     float mt = x[0];
 #pragma unroll
     for (int r = 1; r < 32; ++r) mt = fmaxf(mt, x[r]);
     mt = xhalf_max(mt) * sm_scale;
     m_run = fmaxf(m_run, mt);
-    if (m_ref == -INFINITY) m_ref = mt;
+    m_ref = m_ref == -INFINITY ? mt : m_ref;
     over |= m_run > m_ref + F8_TAU;
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
     int pk[2][4];  // [key half][a]: bytes d = keys 8a + 4h + d of the half
@@ -296,35 +310,99 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
       xa[a] = (int)r[0];
       ya[a] = (int)r[1];
     }
-    const uint32_t dst = lds_p + (uint32_t)(((pb * WAVES + w) * 2) * 1024) + (uint32_t)lane * 16u;
+    const uint32_t dst = lds_pl + (uint32_t)(pb * WAVES + w) * 2048u;
     *reinterpret_cast<__attribute__((address_space(3))) i32x4*>((uintptr_t)dst) = i32x4{xa[0], ya[0], xa[1], ya[1]};
     *reinterpret_cast<__attribute__((address_space(3))) i32x4*>((uintptr_t)(dst + 1024)) =
         i32x4{xa[2], ya[2], xa[3], ya[3]};
   };
 
-  // O^T += V^T P^T over this wave's 128 value columns for all 128 rows;
-  // hook(g) runs after value-column block g (g = 0..3)
-  auto pv = [&](int buf, int pb, auto&& hook) __attribute__((always_inline)) {
+  // O^T += V^T P^T over this wave's 128 value columns for all 128 rows of
+  // tile `buf` with P buffer pb, and beside it the softmax of the next tile's
+  // prepared scores x into P buffer pbn.  With one wave per SIMD the
+  // instructions issue in order, so the softmax is cut into 16 stages, one
+  // after each product, and a scheduling fence after each keeps that order;
+  // each value-column block's V^T is read one block ahead.
+  auto pv_softmax = [&](int buf, int pb, float* x, int pbn) __attribute__((always_inline)) {
     const uint32_t tb = lds_t + (uint32_t)buf * F8_TILE;
+    const uint32_t pr = lds_pl + (uint32_t)pb * (uint32_t)(WAVES * 2048);
     i32x8 pf[WAVES];
 #pragma unroll
     for (int rb = 0; rb < WAVES; ++rb) {
-      const uint32_t src = lds_p + (uint32_t)(((pb * WAVES + rb) * 2) * 1024) + (uint32_t)lane * 16u;
-      const i32x4 x0 = lds16(src), x1 = lds16(src + 1024);
+      const i32x4 x0 = lds16(pr + (uint32_t)(rb * 2048)), x1 = lds16(pr + (uint32_t)(rb * 2048 + 1024));
       pf[rb] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
-    unroll<4>([&](auto J) __attribute__((always_inline)) {
-      constexpr int j = decltype(J)::value;
+    auto read_v = [&](int j) __attribute__((always_inline)) -> i32x8 {
+      uint32_t v0 = tb + vaddr[j][0], v1 = tb + vaddr[j][1];
+      asm("" : "+v"(v0), "+v"(v1));  // keep the block offsets as instruction offsets
       i32x8 vf;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const i32x2 v = lds_tr8(tb + vaddr[j][rr & 1] + (uint32_t)rr * 4096u);
+        const i32x2 v = lds_tr8((rr & 1 ? v1 : v0) + (uint32_t)(rr * 4096));
         vf[2 * rr] = v[0];
         vf[2 * rr + 1] = v[1];
       }
+      return vf;
+    };
+    i32x8 vcur = read_v(0), vnext;
+    // softmax state across the stages
+    float mp[4], mu = 0.f;
+    float e[32];
+    int pk[2][4];
+    unroll<16>([&](auto G) __attribute__((always_inline)) {
+      constexpr int g = decltype(G)::value, j = g / 4, rb = g % 4;
+      if constexpr (rb == 0 && j < 3) vnext = read_v(j + 1);
+      O[rb][j] = mfma8(vcur, pf[rb], O[rb][j]);
+      if constexpr (g < 4) {
+        // partial maxima of 8 scores each
+        float m = fmaxf(fmaxf(x[8 * g], x[8 * g + 1]), fmaxf(x[8 * g + 2], x[8 * g + 3]));
+        m = fmaxf(m, fmaxf(fmaxf(x[8 * g + 4], x[8 * g + 5]), fmaxf(x[8 * g + 6], x[8 * g + 7])));
+        mp[g] = m;
+        if constexpr (g == 3) {
+          float mt = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+          mt = xhalf_max(mt) * sm_scale;
+          m_run = fmaxf(m_run, mt);
+          m_ref = m_ref == -INFINITY ? mt : m_ref;
+          over |= m_run > m_ref + F8_TAU;
+          mu = m_ref == -INFINITY ? 0.f : m_ref;
+        }
+      } else if constexpr (g < 12) {
+        // four weights, their exact sum and the e4m3 pair packing
+        constexpr int q = g - 4;  // 0..7: weights 4q .. 4q+3 (half q / 4, a = q % 4)
 #pragma unroll
-      for (int rb = 0; rb < WAVES; ++rb) O[rb][j] = mfma8(vf, pf[rb], O[rb][j]);
-      hook(J);
+        for (int d = 0; d < 4; ++d) e[4 * q + d] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[4 * q + d], sm_scale, -mu));
+        l_part += (e[4 * q] + e[4 * q + 1]) + (e[4 * q + 2] + e[4 * q + 3]);
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * q], e[4 * q + 1], 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * q + 2], e[4 * q + 3], v, true);
+        pk[q / 4][q % 4] = v;
+      } else {
+        // the rounded weights' sum, the lane exchange, the P write
+        constexpr int q = g - 12;  // 0..3
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const int v = pk[kh][q];
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+          l_rnd += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+        }
+        if constexpr (q == 3) {
+          // lanes n and n + 32 hold 16 keys each of both halves of row n; after
+          // the swap lane n holds the 32 keys of half 0 and lane n + 32 those of half 1
+          int xa[4], ya[4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const auto r = __builtin_amdgcn_permlane32_swap((unsigned)pk[0][a], (unsigned)pk[1][a], false, false);
+            xa[a] = (int)r[0];
+            ya[a] = (int)r[1];
+          }
+          const uint32_t dst = lds_pl + (uint32_t)(pbn * WAVES + w) * 2048u;
+          *reinterpret_cast<__attribute__((address_space(3))) i32x4*>((uintptr_t)dst) = i32x4{xa[0], ya[0], xa[1], ya[1]};
+          *reinterpret_cast<__attribute__((address_space(3))) i32x4*>((uintptr_t)(dst + 1024)) =
+              i32x4{xa[2], ya[2], xa[3], ya[3]};
+        }
+      }
+      if constexpr (rb == 3 && j < 3) vcur = vnext;
+      // keep the row sums of this stage here rather than sunk to the loop's end
+      asm volatile("" ::"v"(l_part), "v"(l_rnd));
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
 
@@ -348,8 +426,10 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
       __syncthreads();
       {
         f32x16 s0, s1;
+        float x[32];
         qk(0, s0, s1);
-        softmax(s0, s1, 0, true, 0);
+        prep(s0, s1, 0, true, x);
+        softmax(x, 0);
       }
       __syncthreads();
       for (int t = 0; t < n_tiles; ++t) {
@@ -359,10 +439,10 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
         if (t + F8_NB - 1 < n_tiles) issue_tile(t + F8_NB - 1, cbuf);
         // past the last tile the product runs on a stale buffer and its scores are all masked
         f32x16 s0, s1;
+        float x[32];
         qk(nbuf, s0, s1);
-        pv(buf, t & 1, [&](auto G) __attribute__((always_inline)) {
-          if constexpr (decltype(G)::value == 1) softmax(s0, s1, t + 1, live, (t + 1) & 1);
-        });
+        prep(s0, s1, t + 1, live, x);
+        pv_softmax(buf, t & 1, x, (t + 1) & 1);
         // tile t+2 must have landed; later copies may stay in flight
         wait_tiles<F8_KI>(min(n_tiles - 1, t + F8_NB - 1) - (t + 2));
         __syncthreads();
