@@ -190,10 +190,17 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
   }
   const uint32_t lds_pl = lds_addr(&sm.p[0][0][0][0]) + (uint32_t)lane * 16u;  // this lane's slot of the P operands
 
+  f32x16 O[WAVES][4];
+  float m_ref = -INFINITY, m_run = -INFINITY, l_part = 0.f, l_rnd = 0.f;
+  bool over = false;
+
   // S^T halves of tile `buf` (lane: query row lr; keys 32kh + 8(r/4) + 4h + r%4).
   // The lane's fragment bases are formed once per tile; the k-step and key
   // half become instruction offsets.
-  auto qk = [&](int buf, f32x16& s0, f32x16& s1) __attribute__((always_inline)) {
+  // pk_prev: the previous softmax's packed e4m3 weights, whose sum (the
+  // rounded row sum) is taken here, between the products, where the VALU is
+  // otherwise idle.
+  auto qk = [&](int buf, f32x16& s0, f32x16& s1, const int (&pk_prev)[2][4]) __attribute__((always_inline)) {
     const uint32_t tb = lds_t + (uint32_t)buf * F8_TILE;
     uint32_t kb[2][2], kr[2];
 #pragma unroll
@@ -202,9 +209,7 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
       kb[e][1] = tb + koff[e][1];
       kr[e] = tb + kropw[e];
     }
-#pragma unroll
-    for (int c = 0; c < F8_KS; ++c) {
-      i32x8 a[2];
+    auto frags = [&](int c, i32x8* a) __attribute__((always_inline)) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         i32x4 x0, x1;
@@ -217,14 +222,32 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
         }
         a[kh] = i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       }
-      if (c == 0) {
-        mfma8_v0(s0, a[0], qf[c]);
-        mfma8_v0(s1, a[1], qf[c]);
+    };
+    // the fragments of k-step c+1 are read before the products of k-step c
+    i32x8 acur[2], anext[2];
+    frags(0, acur);
+    unroll<F8_KS>([&](auto C) __attribute__((always_inline)) {
+      constexpr int c = decltype(C)::value;
+      if constexpr (c + 1 < F8_KS) frags(c + 1, anext);
+      if constexpr (c == 0) {
+        mfma8_v0(s0, acur[0], qf[c]);
+        mfma8_v0(s1, acur[1], qf[c]);
       } else {
-        mfma8_v(s0, a[0], qf[c]);
-        mfma8_v(s1, a[1], qf[c]);
+        mfma8_v(s0, acur[0], qf[c]);
+        mfma8_v(s1, acur[1], qf[c]);
       }
-    }
+      if constexpr (c < 8) {
+        const int v = pk_prev[c >> 2][c & 3];
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+        l_rnd += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+        asm volatile("" ::"v"(l_rnd));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (c + 1 < F8_KS) {
+        acur[0] = anext[0];
+        acur[1] = anext[1];
+      }
+    });
     // the wait states a VALU read of an 8-bit 32x32x64 product's result needs
     asm("s_nop 7\n s_nop 7\n s_nop 7" : "+v"(s0), "+v"(s1));
   };
@@ -242,9 +265,6 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
     wave_vis_end = __builtin_amdgcn_readfirstlane((int32_t)we);
   }
 
-  f32x16 O[WAVES][4];
-  float m_ref = -INFINITY, m_run = -INFINITY, l_part = 0.f, l_rnd = 0.f;
-  bool over = false;
   const float sm_scale = p.scale_log2 > 0.f ? p.scale_log2 : 1.f;
 
   // The scores of one tile as this lane's 32 values (half kh: x[16 kh + r]),
@@ -276,7 +296,7 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
   // and rounded sums, and the e4m3 P^T operand of this wave's rows written
   // to P buffer pb.  Branch-free, so that it can be spread over the P.V
   // products.
-  auto softmax = [&](float* x, int pb) __attribute__((always_inline)) {
+  auto softmax = [&](float* x, int pb, int (&pk)[2][4]) __attribute__((always_inline)) {
     float mt = x[0];
 #pragma unroll
     for (int r = 1; r < 32; ++r) mt = fmaxf(mt, x[r]);
@@ -285,7 +305,7 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
     m_ref = m_ref == -INFINITY ? mt : m_ref;
     over |= m_run > m_ref + F8_TAU;
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-    int pk[2][4];  // [key half][a]: bytes d = keys 8a + 4h + d of the half
+    // pk[key half][a]: bytes d = keys 8a + 4h + d of the half (summed by the next Q.K chain)
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
@@ -297,8 +317,6 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
         int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
         v = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], v, true);
         pk[kh][a] = v;
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
-        l_rnd += (lo[0] + lo[1]) + (hi[0] + hi[1]);
       }
     }
     // lanes n and n + 32 hold 16 keys each of both halves of row n; after the
@@ -322,7 +340,7 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
   // instructions issue in order, so the softmax is cut into 16 stages, one
   // after each product, and a scheduling fence after each keeps that order;
   // each value-column block's V^T is read one block ahead.
-  auto pv_softmax = [&](int buf, int pb, float* x, int pbn) __attribute__((always_inline)) {
+  auto pv_softmax = [&](int buf, int pb, float* x, int pbn, int (&pk)[2][4]) __attribute__((always_inline)) {
     const uint32_t tb = lds_t + (uint32_t)buf * F8_TILE;
     const uint32_t pr = lds_pl + (uint32_t)pb * (uint32_t)(WAVES * 2048);
     i32x8 pf[WAVES];
@@ -347,7 +365,6 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
     // softmax state across the stages
     float mp[4], mu = 0.f;
     float e[32];
-    int pk[2][4];
     unroll<16>([&](auto G) __attribute__((always_inline)) {
       constexpr int g = decltype(G)::value, j = g / 4, rb = g % 4;
       if constexpr (rb == 0 && j < 3) vnext = read_v(j + 1);
@@ -375,14 +392,9 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
         v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * q + 2], e[4 * q + 3], v, true);
         pk[q / 4][q % 4] = v;
       } else {
-        // the rounded weights' sum, the lane exchange, the P write
+        // the lane exchange and the P write (the rounded weights are summed
+        // in the next Q.K chain)
         constexpr int q = g - 12;  // 0..3
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const int v = pk[kh][q];
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
-          l_rnd += (lo[0] + lo[1]) + (hi[0] + hi[1]);
-        }
         if constexpr (q == 3) {
           // lanes n and n + 32 hold 16 keys each of both halves of row n; after
           // the swap lane n holds the 32 keys of half 0 and lane n + 32 those of half 1
@@ -401,7 +413,7 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
       }
       if constexpr (rb == 3 && j < 3) vcur = vnext;
       // keep the row sums of this stage here rather than sunk to the loop's end
-      asm volatile("" ::"v"(l_part), "v"(l_rnd));
+      asm volatile("" ::"v"(l_part));
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -424,12 +436,13 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
       for (int u = 0; u < pre; ++u) issue_tile(u, u);
       wait_tiles<F8_KI>(pre - min(pre, 2));  // tiles 0 and 1 have landed
       __syncthreads();
+      int pk[2][4] = {};  // packed e4m3 weights of the last softmax, not yet summed
       {
         f32x16 s0, s1;
         float x[32];
-        qk(0, s0, s1);
+        qk(0, s0, s1, pk);  // (pk holds zeros: adds nothing)
         prep(s0, s1, 0, true, x);
-        softmax(x, 0);
+        softmax(x, 0, pk);
       }
       __syncthreads();
       for (int t = 0; t < n_tiles; ++t) {
@@ -440,14 +453,21 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
         // past the last tile the product runs on a stale buffer and its scores are all masked
         f32x16 s0, s1;
         float x[32];
-        qk(nbuf, s0, s1);
+        qk(nbuf, s0, s1, pk);
         prep(s0, s1, t + 1, live, x);
-        pv_softmax(buf, t & 1, x, (t + 1) & 1);
+        pv_softmax(buf, t & 1, x, (t + 1) & 1, pk);
         // tile t+2 must have landed; later copies may stay in flight
         wait_tiles<F8_KI>(min(n_tiles - 1, t + F8_NB - 1) - (t + 2));
         __syncthreads();
       }
       asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+      // the last softmax's weights (all masked past the last tile: they add 0)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int v = pk[q >> 2][q & 3];
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+        l_rnd += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+      }
     }
     if (pass == 0) {
       const bool any = __ballot(over) != 0ull;
