@@ -247,43 +247,56 @@ mla_status mla_fwd_group(int32_t n, const mla_fwd_call* calls, void* stream /* h
  * running result between folds is float32, kept in the workspace; only each
  * query chunk's last call writes out (bf16) and its final lse.
  *
- * order: the launches the calls run in (mla_ring_schedule).  Results agree
- * up to rounding between orders: the fold is commutative and associative.
+ * Execution: one kernel launch (for n_chunks > 1).  A work item is one block
+ * of 32 query rows of up to 4 heads of one chunk; its workgroup runs all of
+ * that chunk's calls for those rows in turn, in the chunk's fold order,
+ * taking items from a queue (the last chunk, with the longest chains,
+ * first).  Each call computes exactly what the corresponding mla_fwd call
+ * would (bit for bit), so the result equals the ring of separate calls; the
+ * float32 running result stays in the workspace in the kernel's own layout.
+ *
+ * order: the order each query chunk's calls fold in (mla_ring_schedule:
+ * a chunk's calls fold in increasing step index).  Results agree up to
+ * rounding between orders: the fold is commutative and associative.
  *
  * out [B, H, N, 512] bf16 and lse [B, H, N] fp32, both required.
  * workspace: device memory of at least
  * mla_ring_workspace_size(B, H, N, n_chunks) bytes, 256-byte aligned (may be
  * NULL when that size is 0: one chunk, or an empty problem); contents
- * unspecified on return.  Every argument and every call is validated before
- * anything is enqueued.
+ * unspecified on return.  It also holds the launch's item counter, so two
+ * ring calls in flight at once need two workspaces.  Every argument and
+ * every call is validated before anything is enqueued.
  */
-#define MLA_RING_ORDER 0     /* launch s is ring step s: chunk r meets KV chunk (r - s) mod P */
-#define MLA_RING_BALANCED 1  /* the same calls in equally full launches, the diagonals last */
+#define MLA_RING_ORDER 0     /* step s is ring step s: chunk r meets KV chunk (r - s) mod P */
+#define MLA_RING_BALANCED 1  /* the same calls in equally full steps, the diagonals last */
 mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_t H, int64_t N,
                         int32_t dq, int32_t dv, float scale, int32_t n_chunks, int32_t order,
                         const mla_rows* out, const mla_rows* lse,
                         void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
-/* Bytes of the workspace mla_ring_fwd needs: B*H*n_chunks*C*512*4 with
- * C = ceil(N / n_chunks) for n_chunks > 1; 0 for one chunk or invalid sizes;
- * SIZE_MAX when the product overflows (mla_ring_fwd then fails with
- * MLA_ERR_UNSUPPORTED). */
+/* Bytes of the workspace mla_ring_fwd needs: the float32 running results,
+ * B * ceil(H/4)*4 * n_chunks * ceil(C/32)*32 * 512 * 4 with C = ceil(N / n_chunks),
+ * plus 256 for the item counter, for n_chunks > 1 and N > 0; 0 for one chunk,
+ * no rows or invalid sizes; SIZE_MAX when the product overflows (mla_ring_fwd
+ * then fails with MLA_ERR_UNSUPPORTED). */
 size_t mla_ring_workspace_size(int32_t B, int32_t H, int64_t N, int32_t n_chunks);
 
 /*
- * mla_ring_schedule -- the launches mla_ring_fwd issues for P = n_chunks
- * (host only; nothing is enqueued).  launch_of: host int32 array of
- * P (P + 1) / 2 entries; entry r (r + 1) / 2 + k receives the launch index
- * of the call of query chunk r on KV chunk k (k <= r).  *n_launches receives
- * the number of launches (P).  A query chunk has at most one call per
- * launch, and its calls fold in launch order.
+ * mla_ring_schedule -- the steps of the ring for P = n_chunks, which fix
+ * the order mla_ring_fwd folds each query chunk's calls in (host only;
+ * nothing is enqueued).  launch_of: host int32 array of P (P + 1) / 2
+ * entries; entry r (r + 1) / 2 + k receives the step index of the call of
+ * query chunk r on KV chunk k (k <= r).  *n_launches receives the number of
+ * steps (P).  A query chunk has at most one call per step, and its calls
+ * fold in step order.  (The steps are what a ring of P devices would run
+ * together; on one device mla_ring_fwd runs them all in one launch.)
  *
- * MLA_RING_ORDER: launch s is ring step s, as each device of a P-device
+ * MLA_RING_ORDER: step s is ring step s, as each device of a P-device
  * ring runs it (P diagonal calls, then P - 1, ..., 1 full calls).
  * MLA_RING_BALANCED: each query chunk's full calls (k < r), longest chains
- * first, go to the r least-filled of the first P - 1 launches, and the P
- * diagonal calls (half the work of a full call each) run together last;
- * the launches are then equally full.
+ * first, go to the r least-filled of the first P - 1 steps, and the P
+ * diagonal calls (half the work of a full call each) come last; the steps
+ * are then equally full.
  */
 mla_status mla_ring_schedule(int32_t n_chunks, int32_t order, int32_t* launch_of, int32_t* n_launches);
 

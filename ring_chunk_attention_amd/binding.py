@@ -699,13 +699,13 @@ def ring_order(r: int, n_chunks: int) -> Sequence[int]:
 
 
 def ring_schedule(n_chunks: int, order: str = "balanced") -> List[List[Tuple[int, int]]]:
-    """The launches mla_ring_fwd issues (mla_ring_schedule): a list of
-    launches, each a list of (query chunk r, KV chunk k) calls that run
-    together.  Every pair k <= r appears once; a query chunk has at most one
-    call per launch, and its calls fold in launch order.  ``order``: "ring"
-    (launch s is ring step s: chunk r meets KV chunk (r - s) mod P) or
-    "balanced" (the same calls in equally full launches, the diagonals
-    last)."""
+    """The steps of the ring (mla_ring_schedule): a list of steps, each a
+    list of (query chunk r, KV chunk k) calls that a ring of devices would
+    run together.  Every pair k <= r appears once; a query chunk has at most
+    one call per step, and ring_fwd folds its calls in step order.
+    ``order``: "ring" (step s is ring step s: chunk r meets KV chunk
+    (r - s) mod P) or "balanced" (the same calls in equally full steps, the
+    diagonals last)."""
     if order not in _RING_ORDERS:
         raise ValueError(f"unknown ring schedule {order!r}")
     P = int(n_chunks)
@@ -721,6 +721,13 @@ def ring_schedule(n_chunks: int, order: str = "balanced") -> List[List[Tuple[int
     return launches
 
 
+def ring_workspace_size(B: int, H: int, N: int, n_chunks: int) -> int:
+    """Bytes of the workspace ring_fwd needs (mla_ring_workspace_size): the
+    float32 running results of the chunks and the item queue's counter; 0
+    for one chunk or no rows."""
+    return int(LIB.mla_ring_workspace_size(int(B), int(H), int(N), int(n_chunks)))
+
+
 def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
              head_dim_v: int = 512, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None,
@@ -732,9 +739,11 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
     shorter); query chunk r meets each KV chunk k <= r with global offsets,
     and every call after the first folds into the running result
     (TensorRT-LLM mla.py forward_context_with_chunked_prefill; Ascend
-    RingMLAOperation calcType).  ``order``: see ring_schedule.  ``carry``:
-    the float32 running result between folds, any contiguous GPU tensor of at
-    least mla_ring_workspace_size() bytes (allocated if not given)."""
+    RingMLAOperation calcType).  One launch runs all the calls; ``order``
+    (see ring_schedule) sets the order each chunk's calls fold in.
+    ``carry``: the workspace (the float32 running results between folds and
+    the launch's item counter), any contiguous GPU tensor of at least
+    ring_workspace_size() bytes (allocated if not given)."""
     if order not in _RING_ORDERS:
         raise ValueError(f"unknown ring schedule {order!r}")
     for t, n in ((q, "q"), (kv, "kv")):

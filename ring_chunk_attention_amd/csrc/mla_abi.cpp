@@ -322,9 +322,11 @@ mla_status prepare_group(int32_t n, const mla_fwd_call* calls, mla::GroupParams*
   return MLA_OK;
 }
 
-// One-device ring (the value width of the shared-latent form; the most chunks).
+// One-device ring (the value width of the shared-latent form; the most
+// chunks; the bytes after the carry that hold the item queue's counter).
 constexpr int kRingDv = 512;
-constexpr int kMaxRingChunks = 64;
+constexpr int kMaxRingChunks = mla::kMaxRing;
+constexpr size_t kRingQueueBytes = 256;
 
 // Launch index of each call (r, k), k <= r, at launch_of[r (r + 1) / 2 + k];
 // returns the number of launches.  MLA_RING_ORDER: launch s is ring step s,
@@ -464,9 +466,16 @@ size_t mla_ring_workspace_size(int32_t B, int32_t H, int64_t N, int32_t n_chunks
   if (B < 0 || H <= 0 || N < 0 || n_chunks < 1 || n_chunks > kMaxRingChunks) return 0;
   if (n_chunks == 1) return 0;
   const uint64_t C = (uint64_t)N / n_chunks + ((uint64_t)N % n_chunks != 0);  // chunk length (the last may be shorter)
+  // the carry: per chunk, one block of 4 heads x 32 rows x 512 float32 per
+  // work item (items of ceil(C / 32) row blocks x ceil(H / 4) head groups x B)
   uint64_t bytes = (uint64_t)B;
-  for (uint64_t f : {(uint64_t)H, (uint64_t)n_chunks, C, (uint64_t)kRingDv, (uint64_t)sizeof(float)})
+  for (uint64_t f : {((uint64_t)H + 3) / 4 * 4, (uint64_t)n_chunks, (C + 31) / 32 * 32, (uint64_t)kRingDv,
+                     (uint64_t)sizeof(float)})
     if (__builtin_mul_overflow(bytes, f, &bytes)) return SIZE_MAX;  // no buffer can be that large
+  if (bytes == 0) return 0;  // no rows: nothing is launched
+  // the carry, then the item queue's counter (the carry is a multiple of 2 KB)
+  if (__builtin_add_overflow(bytes, (uint64_t)kRingQueueBytes, &bytes) || bytes > (uint64_t)SIZE_MAX - 1)
+    return SIZE_MAX;
   return (size_t)bytes;
 }
 
@@ -501,7 +510,6 @@ mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_
   const int n_calls = P * (P + 1) / 2;
   std::vector<mla_rows> views(5 * (size_t)n_calls);
   std::vector<mla_fwd_call> calls(n_calls);
-  std::vector<int> call_launch(n_calls);
   std::vector<int> seen(P, 0);
   auto shift = [](const mla_rows* r, int64_t t0, int elem) {
     mla_rows v = *r;
@@ -541,25 +549,54 @@ mla_status mla_ring_fwd(const mla_rows* q, const mla_rows* kv, int32_t B, int32_
         c.prev_lse = first ? nullptr : &v[3];
         c.out = last ? &v[2] : &v[4];
         c.lse = &v[3];
-        call_launch[ci] = L;
         ++ci;
       }
-  // Validate and prepare every group before anything is launched.
-  std::vector<mla::GroupParams> groups;
-  for (int L = 0, i = 0; L < n_launches; ++L) {
-    int j = i;
-    while (j < n_calls && call_launch[j] == L) ++j;
-    for (int g0 = i; g0 < j; g0 += MLA_MAX_GROUP) {
-      mla::GroupParams g;
-      if (mla_status st = prepare_group(std::min(MLA_MAX_GROUP, j - g0), &calls[g0], &g)) return st;
-      if (g.n) groups.push_back(g);
-    }
-    i = j;
+  // Validate every call before anything is launched.
+  for (int i = 0; i < n_calls; i += MLA_MAX_GROUP) {
+    mla::GroupParams g;
+    if (mla_status st = prepare_group(std::min(MLA_MAX_GROUP, n_calls - i), &calls[i], &g)) return st;
   }
-  for (const mla::GroupParams& g : groups)
-    if (mla_status st = hip_status(mla::launch_latent_group(g, static_cast<hipStream_t>(stream)), "ring launch"))
+  if (B == 0 || N == 0) return MLA_OK;
+  if (P == 1) {  // one call, no fold: a plain launch
+    mla::GroupParams g;
+    if (mla_status st = prepare_group(1, &calls[0], &g)) return st;
+    if (g.n == 0) return MLA_OK;
+    return hip_status(mla::launch_latent_group(g, static_cast<hipStream_t>(stream)), "ring launch");
+  }
+
+  // One launch for all the calls.  The base views are those of chunk 0's
+  // only call (the kernel moves them to each call's chunks); each chunk's
+  // calls fold in the order of their launch indices in the schedule.
+  mla::RingParams rp{};
+  {
+    int form = FORM_EMPTY;
+    if (mla_status st = prepare_fwd(q, nullptr, kv, nullptr, nullptr, B, H, 1, len(0), len(0), dq, 0, dv, nullptr, 0,
+                                    scale, MLA_CAUSAL, 0, 0, nullptr, nullptr, out, lse, nullptr, 0, &rp.base, &form))
       return st;
-  return MLA_OK;
+  }
+  rp.carry = static_cast<float*>(workspace);
+  rp.queue = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + (need - kRingQueueBytes));
+  rp.chunk_items = (C + 31) / 32 * (int64_t)rp.base.n_hgrp * B;
+  rp.C = C;
+  rp.N = N;
+  rp.P = P;
+  int64_t items = 0;
+  for (int j = 0; j < P; ++j) {
+    const int r = P - 1 - j;
+    rp.chunk_first[j] = (int32_t)items;
+    items += (len(r) + 31) / 32 * (int64_t)rp.base.n_hgrp * B;
+    if (items > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "the ring has too many work items for one launch");
+  }
+  rp.chunk_first[P] = (int32_t)items;
+  rp.n_items = (int32_t)items;
+  for (int r = 0; r < P; ++r) {
+    uint8_t* fk = rp.fold_k + r * (r + 1) / 2;
+    for (int k = 0; k <= r; ++k) fk[k] = (uint8_t)k;
+    std::stable_sort(fk, fk + r + 1, [&](uint8_t a, uint8_t b) {
+      return launch_of[r * (r + 1) / 2 + a] < launch_of[r * (r + 1) / 2 + b];
+    });
+  }
+  return hip_status(mla::launch_latent_ring(rp, static_cast<hipStream_t>(stream)), "ring launch");
 }
 
 mla_status mla_merge_lse(const mla_rows* out_a, const mla_rows* lse_a, const mla_rows* out_b,

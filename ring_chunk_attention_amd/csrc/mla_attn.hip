@@ -3,6 +3,8 @@
 // queue's reset.  The split form is built in mla_attn_split.hip.
 #include "mla_attn_kernels.inc"
 
+#include <algorithm>
+
 namespace mla {
 namespace {
 
@@ -84,6 +86,16 @@ hipError_t launch_latent_group(const GroupParams& g, hipStream_t s) {
   const int64_t items = g.first[g.n];
   if (items == 0) return hipSuccess;
   hipLaunchKernelGGL((attn_fwd_group_kernel<LatentCfg, LATENT>), dim3((unsigned)items), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_ring(const RingParams& g, hipStream_t s) {
+  if (g.n_items == 0) return hipSuccess;
+  // one workgroup per CU (each fills a CU's LDS), or fewer when the items are fewer
+  const int ncu = cu_count();
+  const int grid = std::min(g.n_items, ncu > 0 ? ncu : 256);
+  hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(1), 0, s, g.queue);
+  hipLaunchKernelGGL((attn_fwd_ring_kernel<LatentCfg, LATENT>), dim3((unsigned)grid), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 

@@ -83,6 +83,30 @@ struct GroupParams {
 };
 static_assert(sizeof(GroupParams) <= 4096, "kernel arguments are limited to 4 KB");
 
+// The one-device ring in one launch (mla_ring_fwd).  A work item is one
+// latent item (32 query rows of up to 4 heads) of query chunk r together with
+// every call of that chunk: its workgroup runs them one after another in the
+// chunk's fold order, each call folding into the float32 carry the one
+// before it wrote.  Items are taken from a queue, the last chunk (the longest
+// chains) first.
+constexpr int kMaxRing = 64;
+// The running result of an item is kept between its calls in the output
+// accumulators' own layout (kRingCarryFloats floats per item: wave w's
+// float4 k of lane l at ((w * 64 + k) * 64 + l) * 4), so that each lane
+// writes and reads back its own accumulators in whole 1 KB wave accesses.
+constexpr int64_t kRingCarryFloats = 4 * 64 * 64 * 4;
+struct RingParams {
+  AttnParams base;           // the call of query chunk 0 on KV chunk 0 (views at row 0)
+  float* carry;              // [P][chunk_items][kRingCarryFloats] float32 running results
+  unsigned* queue;           // the item counter (zeroed before the launch)
+  int64_t chunk_items;       // items of a full chunk (the carry's chunk stride)
+  int64_t C, N;              // chunk length (the last chunks may be shorter or empty), rows
+  int32_t P, n_items;        // chunks; items of all chunks
+  int32_t chunk_first[kMaxRing + 1];  // items of chunk P-1-j: [chunk_first[j], chunk_first[j+1])
+  uint8_t fold_k[kMaxRing * (kMaxRing + 1) / 2];  // chunk r's s-th call meets KV chunk fold_k[r(r+1)/2 + s]
+};
+static_assert(sizeof(RingParams) <= 4096, "kernel arguments are limited to 4 KB");
+
 // Decode split-K reduction: partial results of S key ranges per (b, h),
 // element (b, s, h, d) of po at ((b * S + s) * H + h) * dv + d and its LSE
 // at pl[(b * S + s) * H + h].
@@ -127,6 +151,7 @@ struct GatherParams {
 
 hipError_t launch_latent_dense(const AttnParams& p, hipStream_t s);
 hipError_t launch_latent_group(const GroupParams& g, hipStream_t s);
+hipError_t launch_latent_ring(const RingParams& g, hipStream_t s);
 hipError_t launch_latent_sparse(const AttnParams& p, hipStream_t s);
 hipError_t launch_split(const AttnParams& p, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);

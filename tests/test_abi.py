@@ -399,10 +399,11 @@ def test_ring_rejects_invalid_arguments(lib, kw, code, msg):
 
 
 def test_ring_workspace_size_and_empty_ring(lib):
-    assert lib.mla_ring_workspace_size(1, 16, 4096, 4) == 16 * 4096 * 512 * 4
+    # the float32 carry, then 256 bytes for the item queue's counter
+    assert lib.mla_ring_workspace_size(1, 16, 4096, 4) == 16 * 4096 * 512 * 4 + 256
     assert lib.mla_ring_workspace_size(1, 16, 4096, 1) == 0
     # a ragged length: chunks of ceil(4095 / 4) = 1024 rows, the last 1023
-    assert lib.mla_ring_workspace_size(1, 16, 4095, 4) == 16 * 4 * 1024 * 512 * 4
+    assert lib.mla_ring_workspace_size(1, 16, 4095, 4) == 16 * 4 * 1024 * 512 * 4 + 256
     # no rows: nothing is launched, and every view may be NULL
     assert call_ring(lib, N=0, q=NULL_ROWS, kv=NULL_ROWS, out=NULL_ROWS, lse=NULL_ROWS, workspace=None,
                      workspace_bytes=0) == MLA_OK

@@ -284,6 +284,38 @@ def test_ring4_config_sampled(mla, order):
     assert report("ring4 LSE", host(lse[:, heads][:, :, rows]), l_ref) <= LSE_TOL
 
 
+@pytest.mark.parametrize("order", ["ring", "balanced"])
+@pytest.mark.parametrize("B,H,N,P", [(1, 8, 640, 5), (2, 4, 250, 4), (1, 4, 70, 8), (1, 2, 10, 8)])
+def test_ring_bit_identical_to_its_calls(mla, order, B, H, N, P):
+    """The ring's single launch runs, for each query chunk, the calls the
+    pages describe: the same bits as those calls made one by one through
+    mla_fwd in the chunk's fold order (the schedule's step order), with a
+    float32 running result between them and the bf16 output from the last.
+    Ragged and empty chunks included (N = 70 in 8 chunks of 9: the last one
+    has 7 rows; N = 10 in 8 chunks of 2: the last three are empty)."""
+    c = W.dense_case(B=B, H=H, N=N, seed=90 + P)
+    q, kv = dev_bf16(c.q), dev_bf16(c.kv)
+    out, lse = mla.ring_fwd(q, kv, P, scale=c.scale, order=order)
+    step_of = {rk: s for s, calls in enumerate(mla.ring_schedule(P, order)) for rk in calls}
+    C = -(-N // P)
+    ref_o, ref_l = torch.empty_like(out), torch.empty_like(lse)
+    for r in range(P):
+        r0, r1 = r * C, min((r + 1) * C, N)
+        if r1 <= r0:
+            continue
+        carry = torch.empty((B, H, r1 - r0, 512), dtype=torch.float32, device="cuda")
+        lse_r = torch.empty((B, H, r1 - r0), dtype=torch.float32, device="cuda")
+        for s, k in enumerate(sorted(range(r + 1), key=lambda k: step_of[(r, k)])):
+            k0, k1 = k * C, min((k + 1) * C, N)
+            o_r = ref_o[:, :, r0:r1] if s == r else carry
+            mla.fwd(q[:, :, r0:r1], kv[:, :, k0:k1], scale=c.scale, causal=True, q_offset=r0, kv_offset=k0,
+                    prev=None if s == 0 else (carry, lse_r), out=o_r, lse=lse_r, workspace=None)
+        ref_l[:, :, r0:r1] = lse_r
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
+    assert torch.equal(lse, ref_l)
+
+
 # ---------------------------------------------------------------------------
 # split q/k varlen ring step
 # ---------------------------------------------------------------------------
@@ -860,15 +892,15 @@ def test_decode_longest_cache(mla):
 
 
 def test_ring_hip_graph_replays_match_eager(mla):
-    """The ring driver captured in a HIP graph (its group launches allocate
-    nothing and record no memset):
+    """The ring driver captured in a HIP graph (it allocates nothing and
+    records no memset: a kernel clears the item counter):
     several replays, with eager work and synchronisations between them, each
     bit-identical to the eager result."""
     c = W.dense_case(B=1, H=8, N=1024, seed=97)
     q, kv = dev_bf16(c.q), dev_bf16(c.kv)
     out = torch.empty((1, 8, 1024, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((1, 8, 1024), dtype=torch.float32, device="cuda")
-    carry = torch.empty((4, 1, 8, 256, 512), dtype=torch.float32, device="cuda")
+    carry = torch.empty(mla.ring_workspace_size(1, 8, 1024, 4), dtype=torch.uint8, device="cuda")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):   # the eager result, off the capture stream
