@@ -170,35 +170,46 @@ def split_mla(q1, q2, k1, k2, v, seq_lens, scale: float, causal: bool = True,
               seqs: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Tokens of several sequences packed along axis 0 ([T, H, D] layouts).
 
-    The score is scale * (q1.k1 + q2.k2): the query and key arrive split into
-    the part without positional encoding and the rotary part.  V is separate.
-    Sequence b occupies tokens [cu[b], cu[b] + len[b]) for query and keys
-    alike and sees only its own keys, causally (TRIU) if ``causal``.  Query
-    head h reads KV head h // (H / Hkv).  With ``prev_out`` [T, H, dv] and
-    ``prev_lse`` [H, T] the new result is folded into the previous one.
-    Returns out [T, H, dv] and lse [H, T] (restricted to ``heads``/``seqs``
-    when given: other entries are left as zeros / -inf).
+    Ascend RingMLAOperation, member table (querySplit1/2, keySplit1/2, value,
+    seqLen, maskType, prevOut/prevLse).  The score is scale * (q1.k1 + q2.k2):
+    the query and key arrive split into the part without positional encoding
+    and the rotary part.  V is separate.  ``seq_lens`` is either [batch]
+    (sequence b owns the same token range [cu[b], cu[b] + len[b]) of the
+    query and the key tensors) or [2, batch] (row 0 the query lengths, row 1
+    the key lengths, each packed along its own tensor).  A query sees only
+    keys of its own sequence; with ``causal`` (TRIU) the last query row and
+    the last key row of a sequence share a position, so query i of a
+    sequence with Lq queries and Lk keys sees key j iff j <= i + Lk - Lq
+    (equal lengths: j <= i).  Query head h reads KV head h // (H / Hkv).
+    With ``prev_out`` [Tq, H, dv] and ``prev_lse`` [H, Tq] the new result is
+    folded into the previous one.  Returns out [Tq, H, dv] and lse [H, Tq]
+    (restricted to ``heads``/``seqs`` when given: other entries are left as
+    zeros / -inf).
     """
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    q_lens, k_lens = (seq_lens, seq_lens) if seq_lens.ndim == 1 else (seq_lens[0], seq_lens[1])
     T, H = q1.shape[0], q1.shape[1]
     Hkv = k1.shape[1]
     group = H // Hkv
     dv = v.shape[2]
-    cu = np.concatenate([[0], np.cumsum(seq_lens)])
-    if cu[-1] != T:
-        raise ValueError("sequence lengths do not add up to the token count")
+    cq = np.concatenate([[0], np.cumsum(q_lens)])
+    ck = np.concatenate([[0], np.cumsum(k_lens)])
+    if cq[-1] != T or ck[-1] != k1.shape[0]:
+        raise ValueError("sequence lengths do not add up to the token counts")
     heads = range(H) if heads is None else heads
-    seqs = range(len(seq_lens)) if seqs is None else seqs
+    seqs = range(len(q_lens)) if seqs is None else seqs
     out = np.zeros((T, H, dv))
     lse = np.full((H, T), NEG_INF)
     for b in seqs:
-        t0, t1 = int(cu[b]), int(cu[b + 1])
-        pos = np.arange(t1 - t0)
+        t0, t1 = int(cq[b]), int(cq[b + 1])
+        u0, u1 = int(ck[b]), int(ck[b + 1])
+        kpos = np.arange(u1 - u0)
+        qpos = np.arange(t1 - t0) + (u1 - u0) - (t1 - t0)  # the last rows share a position
         for h in heads:
             kvh = h // group
             qq = np.concatenate([_f64(q1[t0:t1, h]), _f64(q2[t0:t1, h])], axis=1)
-            kk = np.concatenate([_f64(k1[t0:t1, kvh]), _f64(k2[t0:t1, kvh])], axis=1)
-            o, l = attention(qq, kk, _f64(v[t0:t1, kvh]), scale, causal, pos, pos)
+            kk = np.concatenate([_f64(k1[u0:u1, kvh]), _f64(k2[u0:u1, kvh])], axis=1)
+            o, l = attention(qq, kk, _f64(v[u0:u1, kvh]), scale, causal, qpos, kpos)
             if prev_out is not None:
                 o, l = merge(prev_out[t0:t1, h], prev_lse[h, t0:t1], o, l)
             out[t0:t1, h], lse[h, t0:t1] = o, l

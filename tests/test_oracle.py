@@ -410,6 +410,105 @@ def test_split_prev_fold_is_merge():
     np.testing.assert_allclose(empty[1], fresh[1], atol=1e-15)
 
 
+def _split_cat(c, toks, heads_of, which):
+    """Rows ``toks`` of the split tensors joined into whole vectors (q: q1|q2
+    of the given heads; k: k1|k2; v)."""
+    f = W.bf16_bits_to_f64
+    if which == "q":
+        return np.concatenate([f(c.q1[toks][:, heads_of]), f(c.q2[toks][:, heads_of])], -1)
+    if which == "k":
+        return np.concatenate([f(c.k1[toks][:, heads_of]), f(c.k2[toks][:, heads_of])], -1)
+    return f(c.v[toks][:, heads_of])
+
+
+def test_split_two_row_lengths_brute_force():
+    """[2, batch] lengths (Ascend seqLen, second form): sequence b's queries
+    come from its own range of the query tensor, its keys from its own range
+    of the key tensors; under TRIU the last query and the last key of a
+    sequence share a position.  Pure-Python loops over every (query, key)
+    pair, including sequences with fewer keys than queries (their first
+    queries see no key) and with no keys or no queries at all."""
+    ql, kl = [3, 5, 0, 4, 2], [6, 2, 3, 4, 0]
+    c = W.split_case(seq_lens=ql, kv_lens=kl, H=2, Hkv=1, d_nope=8, d_rope=4, dv=6, seed=31)
+    for causal in (True, False):
+        out, lse = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale, causal=causal)
+        tq = tk = 0
+        for Lq, Lk in zip(ql, kl):
+            for h in range(2):
+                for i in range(Lq):
+                    q = _split_cat(c, [tq + i], [h], "q")[0, 0]
+                    vis = [j for j in range(Lk) if not causal or j <= i + Lk - Lq]
+                    if not vis:
+                        assert np.all(out[tq + i, h] == 0) and np.isneginf(lse[h, tq + i])
+                        continue
+                    s = [c.scale * float(q @ _split_cat(c, [tk + j], [0], "k")[0, 0]) for j in vis]
+                    m = max(s)
+                    w = [math.exp(x - m) for x in s]
+                    o = sum(wj * _split_cat(c, [tk + j], [0], "v")[0, 0] for wj, j in zip(w, vis)) / sum(w)
+                    np.testing.assert_allclose(out[tq + i, h], o, atol=1e-12)
+                    assert abs(lse[h, tq + i] - (m + math.log(sum(w)))) < 1e-12
+            tq += Lq
+            tk += Lk
+
+
+def test_split_two_row_equal_lengths_is_one_row():
+    c = W.split_case(seq_lens=[4, 7, 2], H=2, Hkv=2, d_nope=8, d_rope=4, dv=8, seed=32)
+    one = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale)
+    two = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, np.stack([c.seq_lens, c.seq_lens]), c.scale)
+    assert np.array_equal(one[0], two[0]) and np.array_equal(one[1], two[1])
+
+
+def _chunk_of(c, lens, parts):
+    """Per sequence, the token ranges of the chunks ``parts`` ([(start, stop)]
+    within the sequence) gathered from the packed tensors."""
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    return [int(cu[b]) + t for b, (a, z) in enumerate(parts) for t in range(a, z)]
+
+
+def test_split_ring_step_over_a_past_chunk():
+    """The Ascend ring on split tensors: each sequence's current chunk of
+    queries meets an earlier chunk of keys with no mask (a non-first card's
+    step, [2, batch] lengths), then its own chunk under TRIU with the first
+    result as prevOut/prevLse.  Folded, the two steps give the rows of the
+    plain causal call over the whole sequences, restricted to the current
+    chunk."""
+    lens = [9, 6, 11]
+    whole = W.split_case(seq_lens=lens, H=2, Hkv=1, d_nope=8, d_rope=4, dv=6, seed=33, with_prev=False)
+    ref_o, ref_l = oracle.split_mla(whole.q1, whole.q2, whole.k1, whole.k2, whole.v, whole.seq_lens,
+                                    whole.scale)
+    past = [(0, 4), (0, 2), (0, 7)]   # each sequence's earlier chunk
+    cur = [(4, 9), (2, 6), (7, 11)]   # and its current one
+    qt, kt = _chunk_of(whole, lens, cur), _chunk_of(whole, lens, past)
+    ql = [z - a for a, z in cur]
+    kl = [z - a for a, z in past]
+    sub = lambda x, t: x[t]
+    o1, l1 = oracle.split_mla(sub(whole.q1, qt), sub(whole.q2, qt), sub(whole.k1, kt), sub(whole.k2, kt),
+                              sub(whole.v, kt), np.stack([ql, kl]), whole.scale, causal=False)
+    o2, l2 = oracle.split_mla(sub(whole.q1, qt), sub(whole.q2, qt), sub(whole.k1, qt), sub(whole.k2, qt),
+                              sub(whole.v, qt), ql, whole.scale, causal=True, prev_out=o1, prev_lse=l1)
+    np.testing.assert_allclose(o2, ref_o[qt], atol=1e-12)
+    np.testing.assert_allclose(l2, ref_l[:, qt], atol=1e-12)
+
+
+def test_split_two_row_causal_is_chunked_prefill():
+    """Queries of each sequence's last chunk against the keys of the whole
+    sequence so far, under TRIU with [2, batch] lengths: the rows of the plain
+    causal call over the whole sequences (TensorRT-LLM chunked prefill: a new
+    chunk attends its cached prefix and itself causally).  Pins the alignment
+    of the last rows."""
+    lens = [8, 5, 12, 3]
+    whole = W.split_case(seq_lens=lens, H=4, Hkv=2, d_nope=8, d_rope=4, dv=6, seed=34, with_prev=False)
+    ref_o, ref_l = oracle.split_mla(whole.q1, whole.q2, whole.k1, whole.k2, whole.v, whole.seq_lens,
+                                    whole.scale)
+    cur = [(5, 8), (0, 5), (9, 12), (2, 3)]
+    qt = _chunk_of(whole, lens, cur)
+    ql = [z - a for a, z in cur]
+    o, l = oracle.split_mla(whole.q1[qt], whole.q2[qt], whole.k1, whole.k2, whole.v, np.stack([ql, lens]),
+                            whole.scale, causal=True)
+    np.testing.assert_allclose(o, ref_o[qt], atol=1e-12)
+    np.testing.assert_allclose(l, ref_l[:, qt], atol=1e-12)
+
+
 def test_split_default_draw_lengths():
     """The seeded length draw of the 8-sequence workload (uniform in
     [1024, 8192])."""
@@ -649,3 +748,16 @@ def test_planted_decode_short_by_one_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "decode_mla", mutant)
     with pytest.raises(AssertionError):
         test_decode_zero_scale_prefix_mean()
+
+
+def test_planted_split_top_left_alignment_is_caught(monkeypatch):
+    """Queries aligned to the first key instead of the last (positions
+    restarting at 0 for both) must fail the chunked-prefill pin."""
+    orig = mla_ref.attention
+
+    def mutant(q, k, v, scale, causal, q_pos, k_pos):
+        q_pos = np.asarray(q_pos)
+        return orig(q, k, v, scale, causal, q_pos - (q_pos.min() if q_pos.size else 0), k_pos)
+    monkeypatch.setattr(mla_ref, "attention", mutant)
+    with pytest.raises(AssertionError):
+        test_split_two_row_causal_is_chunked_prefill()

@@ -88,12 +88,12 @@ class DenseCase:
 @dataclass
 class SplitCase:
     """Split query/key ring step with per-sequence lengths, [T, H, D] layouts."""
-    seq_lens: np.ndarray   # int32 [n_seqs]
+    seq_lens: np.ndarray   # int32 [n_seqs], or [2, n_seqs]: query lengths, then key lengths
     q1: np.ndarray         # [T, H, 128]
     q2: np.ndarray         # [T, H, 64]
-    k1: np.ndarray         # [T, Hkv, 128]
-    k2: np.ndarray         # [T, Hkv, 64]
-    v: np.ndarray          # [T, Hkv, 128]
+    k1: np.ndarray         # [Tk, Hkv, 128] (Tk = T unless key lengths are given)
+    k2: np.ndarray         # [Tk, Hkv, 64]
+    v: np.ndarray          # [Tk, Hkv, 128]
     prev_out: Optional[np.ndarray]   # [T, H, 128] bf16 bits
     prev_lse: Optional[np.ndarray]   # [H, T] float32
     scale: float
@@ -140,18 +140,25 @@ def split_case(seq_lens: Optional[List[int]] = None, n_seqs: int = 8, len_lo: in
                len_hi: int = 8192, H: int = 32, Hkv: int = 32, d_nope: int = 128,
                d_rope: int = 64, dv: int = 128, seed: int = 0, scale: float = SCALE_192,
                causal: bool = True, with_prev: bool = True, lse_hi: float = 12.0,
-               name: str = "") -> SplitCase:
+               name: str = "", kv_lens: Optional[List[int]] = None) -> SplitCase:
+    """With ``kv_lens`` the key tensors hold their own per-sequence lengths
+    (seq_lens becomes [2, n_seqs]: query lengths, then key lengths)."""
     rng = np.random.default_rng(seed)
     if seq_lens is None:
         lens = rng.integers(len_lo, len_hi, n_seqs, endpoint=True).astype(np.int32)
     else:
         lens = np.asarray(seq_lens, dtype=np.int32)
     T = int(lens.sum())
+    Tk = T if kv_lens is None else int(np.sum(kv_lens))
     q1 = normal_bf16(rng, (T, H, d_nope))
     q2 = normal_bf16(rng, (T, H, d_rope))
-    k1 = normal_bf16(rng, (T, Hkv, d_nope))
-    k2 = normal_bf16(rng, (T, Hkv, d_rope))
-    v = normal_bf16(rng, (T, Hkv, dv))
+    k1 = normal_bf16(rng, (Tk, Hkv, d_nope))
+    k2 = normal_bf16(rng, (Tk, Hkv, d_rope))
+    v = normal_bf16(rng, (Tk, Hkv, dv))
+    if kv_lens is not None:
+        if len(kv_lens) != len(lens):
+            raise ValueError("one key length per sequence")
+        lens = np.stack([lens, np.asarray(kv_lens, dtype=np.int32)])
     prev_out = prev_lse = None
     if with_prev:
         prev_out = normal_bf16(rng, (T, H, dv))
