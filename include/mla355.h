@@ -90,6 +90,7 @@ typedef struct {
 #define MLA_OUT_F32 2u       /* out holds float32 instead of bf16 */
 #define MLA_PREV_OUT_F32 4u  /* prev_out holds float32 instead of bf16 */
 #define MLA_VALID_LENS 8u    /* seq_lens holds the valid rows of each batch of padded tensors */
+#define MLA_SEQ_LENS_QK 16u  /* seq_lens holds 2 * n_seqs lengths: queries, then keys */
 
 /*
  * mla_fwd -- one attention call (one ring step).
@@ -116,6 +117,18 @@ typedef struct {
  * Lengths must be >= 0 and sum to T; the device reads them, so this is not
  * checked before launch (a negative length counts as 0, the sum is clipped to
  * T, and tokens past the sum are left unwritten).
+ *
+ * Separate query and key lengths (MLA_SEQ_LENS_QK; Ascend seqLen of shape
+ * [2, batch], as a non-first card of the ring meets another chunk's keys):
+ * seq_lens is a device int32 [2, n_seqs] array, row 0 the query lengths and
+ * row 1 the key lengths.  The queries are packed along t of q (Nq rows) and
+ * the keys along t of kv, k_rope and v (Nkv rows), each sequence's keys in
+ * the same order as its queries.  With MLA_CAUSAL the last query and the
+ * last key of a sequence share a position: query i of a sequence with Lq
+ * queries and Lk keys sees key j iff j <= i + Lk - Lq, so its first
+ * Lq - Lk queries see no key when Lk < Lq (a query chunk meeting its cached
+ * prefix and itself, as in chunked prefill; equal lengths give the plain
+ * TRIU).  A length is clipped to the rows left in its tensor, as above.
  *
  * Padded batches (MLA_VALID_LENS; shared-latent form): seq_lens is a device
  * int32 [B] array (n_seqs == B) of valid lengths: batch b's query rows
@@ -148,7 +161,7 @@ typedef struct {
  *   - shared latent:  Hkv == 1, v == NULL, dq + dr == 576, dv == 512
  *     (dr == 0 or 64), no packed seq_lens (MLA_VALID_LENS is supported);
  *   - split:          v != NULL, q_rope and k_rope given, dq == 128, dr == 64,
- *     dv == 128, Hq % Hkv == 0, with or without seq_lens.
+ *     dv == 128, Hq % Hkv == 0, with or without seq_lens (of one or two rows).
  * Other shapes return MLA_ERR_UNSUPPORTED.
  */
 mla_status mla_fwd(const mla_rows* q, const mla_rows* q_rope,

@@ -21,6 +21,7 @@ MLA_CAUSAL = 1
 MLA_OUT_F32 = 2
 MLA_PREV_OUT_F32 = 4
 MLA_VALID_LENS = 8
+MLA_SEQ_LENS_QK = 16
 MLA_OUT_MX4 = 1  # mla_sparse_fwd
 MLA_RING_ORDER = 0
 MLA_RING_BALANCED = 1
@@ -404,25 +405,29 @@ def split_fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Te
               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
               workspace="auto") -> Tuple[torch.Tensor, torch.Tensor]:
     """Split query/key ring step over [T, H, D] tensors (mla_fwd, Ascend
-    RingMLAOperation layout): q1 [T, H, 128], q2 [T, H, 64], k1 [T, Hkv, 128],
-    k2 [T, Hkv, 64], v [T, Hkv, 128]; seq_lens int32 [batch] on the GPU;
-    prev = (prev_out [T, H, 128], prev_lse [H, T]).  Returns out [T, H, 128]
-    and lse [H, T].  ``out`` and ``prev_out`` may be float32 tensors (their
-    dtype selects MLA_OUT_F32 / MLA_PREV_OUT_F32).  ``workspace`` as for
-    fwd."""
+    RingMLAOperation layout): q1 [T, H, 128], q2 [T, H, 64], k1 [Tk, Hkv, 128],
+    k2 [Tk, Hkv, 64], v [Tk, Hkv, 128]; seq_lens int32 on the GPU, [batch]
+    (Tk == T: each sequence owns the same tokens of both) or [2, batch]
+    (query lengths, then key lengths: MLA_SEQ_LENS_QK); prev = (prev_out
+    [T, H, 128], prev_lse [H, T]).  Returns out [T, H, 128] and lse [H, T].
+    ``out`` and ``prev_out`` may be float32 tensors (their dtype selects
+    MLA_OUT_F32 / MLA_PREV_OUT_F32).  ``workspace`` as for fwd."""
     for t, n in ((q1, "q1"), (q2, "q2"), (k1, "k1"), (k2, "k2"), (v, "v")):
         _need(t, n, torch.bfloat16)
         if t.dim() != 3:
             raise ValueError(f"{n}: expected [T, H, D]")
     T, H, dq = q1.shape
-    Hkv = k1.shape[1]
+    Tk, Hkv = k1.shape[0], k1.shape[1]
     dr = q2.shape[2]
     dv = v.shape[2]
     dev_ = q1.device
+    two_rows = seq_lens is not None and seq_lens.dim() == 2
+    if Tk != T and not two_rows:
+        raise ValueError(f"k1: {Tk} key tokens, expected {T} (the query tokens) unless seq_lens is [2, batch]")
     _shape(q2, "q2", (T, H, dr), dev_)
-    _shape(k1, "k1", (T, Hkv, dq), dev_)
-    _shape(k2, "k2", (T, Hkv, dr), dev_)
-    _shape(v, "v", (T, Hkv, dv), dev_)
+    _shape(k1, "k1", (Tk, Hkv, dq), dev_)
+    _shape(k2, "k2", (Tk, Hkv, dr), dev_)
+    _shape(v, "v", (Tk, Hkv, dv), dev_)
     if out is None:
         out = torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev_)
     if lse is None:
@@ -431,8 +436,8 @@ def split_fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Te
     _shape(lse, "lse", (H, T), dev_)
     if seq_lens is not None:
         _need(seq_lens, "seq_lens", torch.int32)
-        if seq_lens.dim() != 1 or not seq_lens.is_contiguous():
-            raise ValueError("seq_lens: expected a contiguous [batch] tensor")
+        if seq_lens.dim() not in (1, 2) or (two_rows and seq_lens.shape[0] != 2) or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens: expected a contiguous [batch] or [2, batch] tensor")
         if seq_lens.device != dev_:
             raise ValueError(f"seq_lens: on {seq_lens.device}, expected {dev_}")
     out_f32 = out.dtype == torch.float32
@@ -450,12 +455,12 @@ def split_fwd(q1: torch.Tensor, q2: torch.Tensor, k1: torch.Tensor, k2: torch.Te
     vout = _rows_thd(out, "out", torch.float32 if out_f32 else torch.bfloat16)
     vl = _lse_ht(lse, "lse")
     flags = ((MLA_CAUSAL if causal else 0) | (MLA_OUT_F32 if out_f32 else 0)
-             | (MLA_PREV_OUT_F32 if prev_f32 else 0))
+             | (MLA_PREV_OUT_F32 if prev_f32 else 0) | (MLA_SEQ_LENS_QK if two_rows else 0))
     _check(LIB.mla_fwd(ctypes.byref(views[0]), ctypes.byref(views[1]), ctypes.byref(views[2]),
                        ctypes.byref(views[3]), ctypes.byref(views[4]),
-                       1, H, Hkv, T, T, dq, dr, dv,
+                       1, H, Hkv, T, Tk, dq, dr, dv,
                        seq_lens.data_ptr() if seq_lens is not None else None,
-                       seq_lens.numel() if seq_lens is not None else 0,
+                       seq_lens.shape[-1] if seq_lens is not None else 0,
                        float(scale), flags, 0, 0,
                        _ref(vpo), _ref(vpl), ctypes.byref(vout), ctypes.byref(vl),
                        *_workspace(dev_, workspace), _stream(dev_)))

@@ -180,7 +180,7 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
   if (Hq % Hkv) return fail(MLA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (dq <= 0 || dr < 0 || dv <= 0 || dq % 8 || dr % 8 || dv % 8)
     return fail(MLA_ERR_INVALID_ARG, "head dims must be positive multiples of 8 (dq=%d dr=%d dv=%d)", dq, dr, dv);
-  if (flags & ~(MLA_CAUSAL | MLA_OUT_F32 | MLA_PREV_OUT_F32 | MLA_VALID_LENS))
+  if (flags & ~(MLA_CAUSAL | MLA_OUT_F32 | MLA_PREV_OUT_F32 | MLA_VALID_LENS | MLA_SEQ_LENS_QK))
     return fail(MLA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (!std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite");
   if ((st = check_workspace(workspace, workspace_bytes))) return st;
@@ -213,7 +213,9 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
     return fail(MLA_ERR_INVALID_ARG, "out may alias prev_out only as the identical view");
   if (prev_lse && lse && lse->data && lse->data == prev_lse->data && !same_view(lse, prev_lse))
     return fail(MLA_ERR_INVALID_ARG, "lse may alias prev_lse only as the identical view");
-  const bool valid_lens = flags & MLA_VALID_LENS;
+  const bool valid_lens = flags & MLA_VALID_LENS, lens_qk = flags & MLA_SEQ_LENS_QK;
+  if (lens_qk && (valid_lens || !seq_lens))
+    return fail(MLA_ERR_INVALID_ARG, "MLA_SEQ_LENS_QK needs packed seq_lens (and no MLA_VALID_LENS)");
   if (valid_lens) {
     if (!seq_lens) return fail(MLA_ERR_INVALID_ARG, "MLA_VALID_LENS needs seq_lens (valid rows per batch)");
     if (n_seqs != B) return fail(MLA_ERR_INVALID_ARG, "MLA_VALID_LENS needs n_seqs == B (one length per batch)");
@@ -221,7 +223,8 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
   } else if (seq_lens) {
     if (B != 1) return fail(MLA_ERR_INVALID_ARG, "seq_lens requires B == 1 (tokens packed along t)");
     if (n_seqs <= 0) return fail(MLA_ERR_INVALID_ARG, "seq_lens given with n_seqs <= 0");
-    if (Nq != Nkv) return fail(MLA_ERR_INVALID_ARG, "seq_lens requires Nq == Nkv (same lengths for query and key)");
+    if (!lens_qk && Nq != Nkv)
+      return fail(MLA_ERR_INVALID_ARG, "seq_lens of one row requires Nq == Nkv (same lengths for query and key)");
     if (q_offset || kv_offset) return fail(MLA_ERR_INVALID_ARG, "seq_lens requires q_offset == kv_offset == 0");
     if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(MLA_ERR_INVALID_ARG, "seq_lens must be 4-byte aligned");
   }
@@ -238,6 +241,7 @@ mla_status prepare_fwd(const mla_rows* q, const mla_rows* q_rope, const mla_rows
   p.lse = lm(lse);
   p.prev_lse = lc(prev_lse);
   p.seq_lens = valid_lens ? nullptr : seq_lens;
+  p.kv_seq_lens = lens_qk ? seq_lens + n_seqs : nullptr;
   p.n_seqs = seq_lens && !valid_lens ? n_seqs : 0;
   p.valid_lens = valid_lens ? seq_lens : nullptr;
   p.da = dq;

@@ -48,6 +48,7 @@ struct AttnParams {
   LseC prev_lse;
   const int32_t* idx;       // sparse: [B, S, K] contiguous
   const int32_t* seq_lens;  // split varlen: [n_seqs] or nullptr
+  const int32_t* kv_seq_lens;  // split varlen: the key lengths [n_seqs], or nullptr (the same as seq_lens)
   const int32_t* valid_lens;  // latent: valid rows of each batch [B] (padded tensors), or nullptr
   int32_t n_seqs;
   int32_t da;               // columns in part A

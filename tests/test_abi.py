@@ -82,7 +82,11 @@ def call_fwd(lib, q=None, kv=None, out=None, lse=None, v=None, q_rope=None, k_ro
     (dict(Hq=6, Hkv=4), MLA_ERR_INVALID_ARG, "multiple of Hkv"),
     (dict(Hq=0), MLA_ERR_INVALID_ARG, "sizes"),
     (dict(dv=500), MLA_ERR_INVALID_ARG, "multiples of 8"),
-    (dict(flags=16), MLA_ERR_INVALID_ARG, "flag"),
+    (dict(flags=32), MLA_ERR_INVALID_ARG, "flag"),
+    (dict(flags=17), MLA_ERR_INVALID_ARG, "MLA_SEQ_LENS_QK needs packed seq_lens"),
+    (dict(flags=25, seq_lens=FAKE, n_seqs=1), MLA_ERR_INVALID_ARG, "MLA_SEQ_LENS_QK needs packed seq_lens"),
+    (dict(flags=17, seq_lens=FAKE, n_seqs=2, Nkv=100), MLA_ERR_UNSUPPORTED, "no kernel"),
+    (dict(flags=17, seq_lens=FAKE, n_seqs=2, q_off=3), MLA_ERR_INVALID_ARG, "q_offset == kv_offset == 0"),
     (dict(flags=5), MLA_ERR_INVALID_ARG, "without prev_out"),
     (dict(scale=float("nan")), MLA_ERR_INVALID_ARG, "scale"),
     (dict(q=Rows(FAKE + 2, 0, 576, 576)), MLA_ERR_INVALID_ARG, "aligned"),

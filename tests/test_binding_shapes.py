@@ -104,6 +104,23 @@ def test_split_mismatched_tensors(over, kw):
     rejected(bd.split_fwd, a["q1"], a["q2"], a["k1"], a["k2"], a["v"], scale=0.07, workspace=None, **kw)
 
 
+def test_split_two_row_lengths_take_other_key_counts():
+    """With [2, batch] seq_lens the key tensors may hold another token count
+    (the call reaches the library); the key tensors must still agree with one
+    another, and seq_lens must have two rows."""
+    a = split_args(k1=m(T + 7, HKV, 128), k2=m(T + 7, HKV, 64), v=m(T + 7, HKV, 128))
+    with pytest.raises(AssertionError, match="library was called"):
+        bd.split_fwd(a["q1"], a["q2"], a["k1"], a["k2"], a["v"], scale=0.07, workspace=None,
+                     seq_lens=i32(2, 3))
+    rejected(bd.split_fwd, a["q1"], a["q2"], a["k1"], a["k2"], a["v"], scale=0.07, workspace=None,
+             seq_lens=i32(3))
+    rejected(bd.split_fwd, a["q1"], a["q2"], a["k1"], a["k2"], a["v"], scale=0.07, workspace=None,
+             seq_lens=i32(3, 3))
+    b = split_args(k1=m(T + 7, HKV, 128), k2=m(T + 7, HKV, 64), v=m(T + 6, HKV, 128))
+    rejected(bd.split_fwd, b["q1"], b["q2"], b["k1"], b["k2"], b["v"], scale=0.07, workspace=None,
+             seq_lens=i32(2, 3))
+
+
 def test_split_accepts_fp32_out_and_prev_up_to_the_library():
     """fp32 out and prev_out pass the binding's checks (the call then reaches
     the library, which the fixture turns into an AssertionError)."""

@@ -366,6 +366,54 @@ def test_split_non_causal(mla, with_prev):
     assert report("split non-causal LSE", host(lse), l_ref) <= LSE_TOL
 
 
+@pytest.mark.parametrize("causal,with_prev", [(True, True), (True, False), (False, True)])
+def test_split_two_row_lengths(mla, causal, with_prev):
+    """[2, batch] lengths (MLA_SEQ_LENS_QK, Ascend seqLen's second form):
+    each sequence's keys come from its own range of the key tensors.  The
+    lengths cover more keys than queries, fewer (under TRIU the first
+    Lq - Lk queries see no key), no keys, no queries (whose keys must still
+    be skipped), one of each, and blocks past 128 rows."""
+    ql = [130, 5, 0, 257, 64, 1, 200]
+    kl = [300, 2, 7, 129, 0, 1, 450]
+    c = W.split_case(seq_lens=ql, kv_lens=kl, H=4, Hkv=2, seed=91, with_prev=with_prev)
+    out, o32, lse = _split_twin(mla, c, with_prev, causal=causal)
+    o_ref, l_ref = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale, causal=causal,
+                                    prev_out=c.prev_out if with_prev else None,
+                                    prev_lse=c.prev_lse if with_prev else None)
+    _twin("split two-row", out, o32, o_ref)
+    assert report("split two-row LSE", host(lse), l_ref) <= LSE_TOL
+
+
+def test_split_ring_step_over_a_past_chunk(mla):
+    """The Ascend ring on split tensors: each sequence's current query chunk
+    meets an earlier key chunk without a mask ([2, batch] lengths, a float32
+    carry), then its own chunk under TRIU folded into that carry.  The result
+    is the rows of the causal call over the whole sequences."""
+    lens = [700, 300, 1200]
+    past, cur = [(0, 400), (0, 100), (0, 512)], [(400, 700), (100, 300), (512, 1200)]
+    c = W.split_case(seq_lens=lens, H=4, Hkv=2, seed=92, with_prev=False)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    qt = np.concatenate([np.arange(a, z) + cu[b] for b, (a, z) in enumerate(cur)])
+    kt = np.concatenate([np.arange(a, z) + cu[b] for b, (a, z) in enumerate(past)])
+    ql = np.array([z - a for a, z in cur], np.int32)
+    kl = np.array([z - a for a, z in past], np.int32)
+    g = lambda x, t: dev_bf16(np.ascontiguousarray(x[t]))
+    q1, q2 = g(c.q1, qt), g(c.q2, qt)
+    T, H = len(qt), c.q1.shape[1]
+    carry = torch.empty((T, H, 128), dtype=torch.float32, device="cuda")
+    o1, l1 = mla.split_fwd(q1, q2, g(c.k1, kt), g(c.k2, kt), g(c.v, kt), scale=c.scale,
+                           seq_lens=dev(np.stack([ql, kl])), causal=False, out=carry)
+    own = (q1, q2, g(c.k1, qt), g(c.k2, qt), g(c.v, qt))
+    out, lse = mla.split_fwd(*own, scale=c.scale, seq_lens=dev(ql), causal=True, prev=(o1, l1))
+    o32, l32 = mla.split_fwd(*own, scale=c.scale, seq_lens=dev(ql), causal=True, prev=(o1, l1),
+                             out=torch.empty_like(carry))
+    torch.cuda.synchronize()
+    assert torch.equal(lse, l32)
+    o_ref, l_ref = oracle.split_mla(c.q1, c.q2, c.k1, c.k2, c.v, c.seq_lens, c.scale)
+    _twin("split ring step", out, o32, o_ref[qt])
+    assert report("split ring step LSE", host(lse), l_ref[:, qt]) <= LSE_TOL
+
+
 def test_split_config_sampled(mla):
     """8 sequences (seed-0 lengths, T = 27610), 32 heads, prev fold: sampled
     tokens of each sequence for four heads against the oracle."""
