@@ -100,10 +100,12 @@ void merge_kernel(const MergeParams p) {
   }
 }
 
-// Split-K reduction of token generation (Mojo mha_single_batch_pipelined: a
-// split over the keys needs a separate reduction kernel at the end): for
-// each (b, h), L = log sum_s exp(L_s) and out = sum_s exp(L_s - L) O_s over
-// the S partial results (a partial with L_s = -inf has weight 0).  HBM-bound: one wave per row; lane s holds split s's LSE for the
+// Split-K reduction of token generation (Mojo mha_single_batch_pipelined,
+// token-generation description: the partial results of a key split are
+// combined afterwards by a kernel of their own): for each (b, h),
+// L = log sum_s exp(L_s) and out = sum_s exp(L_s - L) O_s over the S
+// partial results (a partial with L_s = -inf has weight 0).  HBM-bound: one
+// wave per row; lane s holds split s's LSE for the
 // wave reductions, then each lane sums 8 columns over the splits (two
 // 16-byte reads per split, a coalesced 2 KB per split and row).
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
