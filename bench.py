@@ -35,6 +35,9 @@ PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA: 256 CU x 8192 flop/clk x 2.
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "causal MLA prefill TFLOP/s and % of bf16 MFMA peak on 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_latent_dsv3_prefill_hbm_traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fwd_latent_dsv3_prefill_counters.md")
+COUNTER_CLOCK_KERNEL = "LatentCfg, 0"   # the headline kernel's name in the counter runs
+N_XCD = 8
 KERNEL_SRCS = [os.path.join(ROOT, "ring_chunk_attention_amd", "csrc", f)
                for f in ("mla_attn.hip", "mla_attn_kernels.inc", "mla_attn_body.inc", "mla_qk_chain.inc")]
 
@@ -214,6 +217,21 @@ ROW_TRAFFIC = {   # row -> (kernel name substring, committed traffic summary)
 }
 
 
+def counter_clock(path=COUNTERS_FILE):
+    """The headline kernel's shader clock (MHz) from its committed counter
+    summary (GRBM_GUI_ACTIVE per XCD over the dispatch), or None when the
+    summary was taken on other kernel code."""
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    h = re.search(r"Kernel code hash: `([0-9a-f]+)`", text)
+    m = re.search(r"\| shader clock over the dispatch \(MHz\) \| ([0-9.]+) \|", text)
+    if not h or not m or h.group(1) != kernel_hash():
+        return None
+    return float(m.group(1))
+
+
 def measured_traffic(path=TRAFFIC_FILE, full=False):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel source (``full``: the whole summary)."""
@@ -288,27 +306,36 @@ def summarize_counters(folders, kernel, out_path, cmds):
     as the clock count)."""
     import csv
     vals = {}
+    clock_mhz = None
     for folder in folders:
         files = _csvs(folder, "counter_collection.csv")
         if not files:
             sys.exit(f"no *counter_collection.csv under {folder}")
-        per = {}
+        per, dur = {}, {}
         for r in csv.DictReader(open(files[0])):
             if kernel not in r["Kernel_Name"]:
                 continue
             d = per.setdefault(int(r["Dispatch_Id"]), {})
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if r.get("End_Timestamp") and r.get("Start_Timestamp"):
+                dur[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         if not per:
             sys.exit(f"no dispatch of a kernel named like {kernel!r} in {folder}")
-        vals.update(per[max(per)])
+        last = max(per)
+        vals.update(per[last])
+        if clock_mhz is None and "GRBM_GUI_ACTIVE" in per[last] and dur.get(last, 0) > 0:
+            # GRBM_GUI_ACTIVE counts shader-clock cycles per XCD (summed over the 8)
+            clock_mhz = per[last]["GRBM_GUI_ACTIVE"] / N_XCD / dur[last] * 1e3
     lines = ["# Counters: " + os.path.basename(out_path).rsplit(".", 1)[0], "",
              "Commands (from the repository root, on one MI355X; one pass each):", ""]
     lines += ["    " + c for c in cmds]
     lines += ["", f"Last dispatch of the kernel named like `{kernel}`; values summed over the units "
               "rocprofv3 reports.", "", "| counter | value |", "|---|---:|"]
     lines += [f"| `{k}` | {v:.4g} |" for k, v in sorted(vals.items())]
-    clk = vals.get("GRBM_GUI_ACTIVE", 0.0) / 8.0   # per XCD
+    clk = vals.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD   # per XCD
     derived = []
+    if clock_mhz:
+        derived.append(("shader clock over the dispatch (MHz)", clock_mhz))
     if clk:
         if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
             derived.append(("MFMA busy (per SIMD)", vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (clk * 1024)))
@@ -327,7 +354,9 @@ def summarize_counters(folders, kernel, out_path, cmds):
                 derived.append((f"{k} per MFMA", vals[k] / vals["SQ_INSTS_MFMA"]))
     if derived:
         lines += ["", "| derived | value |", "|---|---:|"]
-        lines += [f"| {k} | {v:.3g} |" for k, v in derived]
+        lines += [f"| {k} | {v:.4g} |" if "MHz" in k else f"| {k} | {v:.3g} |" for k, v in derived]
+    if kernel == COUNTER_CLOCK_KERNEL:
+        lines += ["", f"Kernel code hash: `{kernel_hash()}`"]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -505,11 +534,23 @@ def main():
                      "launch_ms_mean": round(launch_ms, 4), "launch_ms_min": round(launch_min_ms, 4)},
         "engine_clock": clock,
     }
-    if clock:
-        # the same achieved rate against the peak at the clock the engine ran at
-        peak_at = PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0
+    # The same achieved rate against the peak at the shader clock the kernel
+    # ran at.  The driver's DPM level (pp_dpm_sclk, sampled above) reads well
+    # below that clock under this load, so the fraction takes the clock the
+    # kernel's own cycle counter gives over a dispatch in its committed
+    # counter summary, and falls back to the DPM median without one.
+    shader = counter_clock()
+    if clock or shader:
+        mhz = shader if shader else clock["median_mhz"]
+        peak_at = PEAK_BF16_TFLOPS * mhz / 2400.0
         result["roofline"]["frac_at_measured_clock"] = round(achieved / peak_at, 4)
         result["roofline"]["peak_at_measured_clock"] = round(peak_at, 1)
+        result["roofline"]["clock_mhz"] = round(mhz, 1)
+        result["roofline"]["clock_source"] = (
+            "GRBM_GUI_ACTIVE per XCD over a dispatch of this kernel code (profiles/"
+            + os.path.basename(COUNTERS_FILE) + ")" if shader else "pp_dpm_sclk median during the timed region")
+    if clock:
+        clock["note"] = "driver DPM level; reads below the shader clock under MFMA load"
     del q, kv, out, lse
     torch.cuda.empty_cache()
 

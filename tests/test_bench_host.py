@@ -12,7 +12,8 @@ sys.path.insert(0, ROOT)
 def _write_counters(folder, rows):
     os.makedirs(folder, exist_ok=True)
     with open(os.path.join(folder, "p_counter_collection.csv"), "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                                          "Start_Timestamp", "End_Timestamp"])
         w.writeheader()
         for r in rows:
             w.writerow(r)
@@ -45,6 +46,25 @@ def test_counter_summary_takes_the_last_dispatch_and_derives_ratios(tmp_path):
     assert "| waves waiting on a memory counter | 0.25 |" in text
     assert "| L2 hit rate | 0.75 |" in text
     assert "    cmd one" in text and "    cmd two" in text
+
+
+def test_counter_clock_from_grbm_cycles_and_the_code_hash(tmp_path, monkeypatch):
+    """The shader clock of a dispatch is GRBM_GUI_ACTIVE per XCD over its
+    duration; bench takes it for the at-clock fraction only from a summary of
+    the same kernel code."""
+    import bench
+    a = str(tmp_path / "a")
+    # 8 XCDs x 1.8e6 cycles in 1 ms: 1800 MHz
+    _write_counters(a, [dict(Dispatch_Id=3, Kernel_Name="attn_fwd_kernel<LatentCfg, 0>", Counter_Name="GRBM_GUI_ACTIVE",
+                             Counter_Value=1.8e6, Start_Timestamp=1000, End_Timestamp=1000 + 1000000)] * 8)
+    out = str(tmp_path / "c.md")
+    bench.summarize_counters([a], "LatentCfg, 0", out, ["cmd"])
+    text = open(out).read()
+    assert "| shader clock over the dispatch (MHz) | 1800 |" in text
+    assert f"Kernel code hash: `{bench.kernel_hash()}`" in text
+    assert bench.counter_clock(out) == 1800.0
+    monkeypatch.setattr(bench, "kernel_hash", lambda: "0" * 16)
+    assert bench.counter_clock(out) is None
 
 
 def test_more_than_one_gpu_is_refused():
