@@ -341,8 +341,34 @@ def tile_step_lines():
     return lines
 
 
-def emit_tile_step():
+# The LDS addresses of the step move to the next step's buffers inside the
+# block: each register gets its buffer delta (a scalar operand) added right
+# after its last use, where the MFMAs hide the add, instead of between the
+# blocks.  (An LDS read takes its address when it issues.)
+TS_ROTATE = ([(f"a{k}", "da") for k in range(4)] + [(f"b{k}", "db") for k in range(4)]
+             + [(f"vb{par}{h}", "dv") for par in range(2) for h in range(2)])
+
+
+def rotate_addresses(lines):
+    adds = {}
+    for reg, delta in TS_ROTATE + [("pa", "dp")]:
+        last = max(i for i, l in enumerate(lines) if f"%[{reg}]" in l)
+        adds.setdefault(last, []).append(f"v_add_u32 %[{reg}], %[{delta}], %[{reg}]")
+    last = max(i for i, l in enumerate(lines) if "%[pr]" in l)
+    adds.setdefault(last, []).append("v_subrev_u32 %[pr], %[dp], %[pr]")   # pr - dp
+    out = []
+    for i, l in enumerate(lines):
+        out.append(l)
+        out += adds.get(i, [])
+    return out
+
+
+def emit_tile_step(rotate):
+    """The tile step as a function: tile_step takes the step's LDS addresses;
+    tile_step_rot also moves them to the next step's buffers (rotate_addresses)."""
     lines = tile_step_lines()
+    if rotate:
+        lines = rotate_addresses(lines)
     body = "\n".join(f'      "{l}\\n"' for l in lines)
     outs = ['[s] "=&v"(s)', f'[x] "+{{v[{XR}:{XR + 15}]}}"(x)']
     outs += [f'[t{k}] "=&v"(t{k})' for k in range(TS_NBUF)]
@@ -353,18 +379,31 @@ def emit_tile_step():
     outs += [f'[o{rb}{j}] "+a"(O[{rb}][{j}])' for rb in range(4) for j in range(4)]
     outs += ['[m0sv] "=&s"(m0sv)']
     ins = [f'[q{c}] "v"(qf[{c}])' for c in range(KS)]
-    ins += [f'[a{k}] "v"(a{k})' for k in range(4)] + [f'[b{k}] "v"(b{k})' for k in range(4)]
-    ins += ['[sc] "s"(sc)', '[pa] "v"(pw)', '[pr] "v"(pr)']
-    ins += [f'[vb{par}{h}] "v"(vb[{2 * par + h}])' for par in range(2) for h in range(2)]
+    ins += ['[sc] "s"(sc)']
     ins += ['[oa] "v"(oa)', '[ob] "v"(ob)', '[ra] "s"(ra)', '[rb] "s"(rb)', '[m0a] "s"(m0a)', '[m0b] "s"(m0b)']
-    params = ("f32x16& x, f32x16 (&O)[4][4], const bf16x8* qf,\n"
-              "    uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t b0, uint32_t b1, uint32_t b2,\n"
-              "    uint32_t b3, float sc, float& m_ref, float& m_run, float& l_part, float& l_rnd, uint32_t pw,\n"
-              "    uint32_t pr, const uint32_t* vb, uint32_t oa, uint32_t ob, const u32x4& ra, const u32x4& rb,\n"
-              "    uint32_t m0a, uint32_t m0b")
+    if rotate:
+        outs += [f'[a{k}] "+v"(a[{k}])' for k in range(4)] + [f'[b{k}] "+v"(b[{k}])' for k in range(4)]
+        outs += ['[pa] "+v"(pw)', '[pr] "+v"(pr)']
+        outs += [f'[vb{par}{h}] "+v"(vb[{2 * par + h}])' for par in range(2) for h in range(2)]
+        ins += ['[da] "s"(da)', '[db] "s"(db)', '[dv] "s"(dv)', '[dp] "s"(dp)']
+        name = "tile_step_rot"
+        params = ("f32x16& x, f32x16 (&O)[4][4], const bf16x8* qf,\n"
+                  "    uint32_t (&a)[4], uint32_t (&b)[4], float sc, float& m_ref, float& m_run, float& l_part,\n"
+                  "    float& l_rnd, uint32_t& pw, uint32_t& pr, uint32_t (&vb)[4], uint32_t oa, uint32_t ob,\n"
+                  "    const u32x4& ra, const u32x4& rb, uint32_t m0a, uint32_t m0b, int da, int db, int dv, int dp")
+    else:
+        ins += [f'[a{k}] "v"(a{k})' for k in range(4)] + [f'[b{k}] "v"(b{k})' for k in range(4)]
+        ins += ['[pa] "v"(pw)', '[pr] "v"(pr)']
+        ins += [f'[vb{par}{h}] "v"(vb[{2 * par + h}])' for par in range(2) for h in range(2)]
+        name = "tile_step"
+        params = ("f32x16& x, f32x16 (&O)[4][4], const bf16x8* qf,\n"
+                  "    uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t b0, uint32_t b1, uint32_t b2,\n"
+                  "    uint32_t b3, float sc, float& m_ref, float& m_run, float& l_part, float& l_rnd, uint32_t pw,\n"
+                  "    uint32_t pr, const uint32_t* vb, uint32_t oa, uint32_t ob, const u32x4& ra, const u32x4& rb,\n"
+                  "    uint32_t m0a, uint32_t m0b")
     pre = ("  f32x16 s;\n  u32x4 t0, t1, t2, t3, pf0, pf1, pf2, pf3, vfa, vfb;\n"
            "  float m, tmp, mu, r0, r1;\n  uint32_t m0sv;\n")
-    return (f"__device__ __forceinline__ void tile_step({params}) {{\n{pre}"
+    return (f"__device__ __forceinline__ void {name}({params}) {{\n{pre}"
             f"  asm volatile(\n{body}\n"
             f"      : {', '.join(outs)}\n"
             f"      : {', '.join(ins)}\n"
@@ -383,11 +422,14 @@ def render():
             + "// place); x returns the new scores.\n"
             + emit_function("qk_chain_softmax", True) + "\n"
             + "// One key-loop step of the shared-latent form: P V of tile t into O (P at\n"
-            + "// pr, V of the tile by the four bases vb), the Q.K chain of tile t+2 with\n"
-            + "// the softmax of S(t+1) = x in it (P to pw, new scores to x), and the nine\n"
-            + "// copies of tile t+3 (buffer resources ra/rb, offsets oa/ob, LDS bases for\n"
-            + "// M0 m0a/m0b), all interleaved.\n"
-            + emit_tile_step())
+            + "// pr, V of the tile by the four bases vb), the Q.K chain of tile t+2 (K\n"
+            + "// fragments by a, b) with the softmax of S(t+1) = x in it (P to pw, new\n"
+            + "// scores to x), and the nine copies of tile t+3 (buffer resources ra/rb,\n"
+            + "// offsets oa/ob, LDS bases for M0 m0a/m0b), all interleaved.\n"
+            + emit_tile_step(False) + "\n"
+            + "// The same step that also returns a, b, vb and pw moved by da, db, dv and\n"
+            + "// dp, and pr by -dp: the next step's addresses, added inside the block.\n"
+            + emit_tile_step(True))
 
 
 def main():
