@@ -582,17 +582,23 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
         # (each timed behind a hold, so that the ring driver's host-side
         # validation of its 10 calls is not timed as GPU idle time)
         # The two schedules and the same workload unchunked (for the cost of
-        # chunking) are timed in turn, three rounds, and each reported as its
-        # median: short runs on a GPU whose clock moves with load and heat
-        # vary by several percent from one run to the next.
+        # chunking) are timed in turn, five rounds with the order rotated (each
+        # variant takes each place in a round), after all three have run
+        # untimed; each is reported as its median.  Short runs on a GPU whose
+        # clock moves with load and heat vary by several percent from one run
+        # to the next, and the first runs after the long headline read slow.
         carry = torch.empty(mla.ring_workspace_size(1, 16, 4096, 4), dtype=torch.uint8, device="cuda")
         variants = {
             "balanced": lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l, carry=carry),
             "ring": lambda: mla.ring_fwd(q, kv, 4, scale=c.scale, out=o, lse=l, carry=carry, order="ring"),
             "unchunked": lambda: mla.fwd(q, kv, scale=c.scale, out=o, lse=l)}
         times = {k: [] for k in variants}
-        for rnd in range(3):
-            for k in (("balanced", "ring", "unchunked") if rnd % 2 == 0 else ("unchunked", "ring", "balanced")):
+        order = ("balanced", "ring", "unchunked")
+        for k in order:
+            for _ in range(steps):
+                variants[k]()
+        for rnd in range(5):
+            for k in order[rnd % 3:] + order[:rnd % 3]:
                 times[k].append(time_launches(variants[k], steps, warmup, hold=True, per_launch=False)[0])
         ms, ms_ring, ms1 = (float(np.median(times[k])) for k in ("balanced", "ring", "unchunked"))
         fl = 16 * causal_pairs(4096, 4096) * 2176
@@ -601,7 +607,7 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
                                    "calls": 10, "launches": 1, "folds": 6, "schedule": "balanced",
                                    "ring_order_ms": round(ms_ring, 4), "unchunked_ms": round(ms1, 4),
                                    "vs_unchunked": round(ms / ms1, 3), "ring_order_vs_unchunked": round(ms_ring / ms1, 3),
-                                   "timing": "median of 3 interleaved rounds of %d steps each" % steps}
+                                   "timing": "median of 5 interleaved rounds of %d steps each" % steps}
         del q, kv, o, l
     if only in (None, "merge"):
         # standalone merge of two [1, 16, 1024, 512] partials (HBM-bound): two
