@@ -90,6 +90,29 @@ def test_dense_ragged(mla, B, H, N, Nkv, q_off, kv_off, causal, seed):
     assert report("LSE", host(lse), l_ref) <= LSE_TOL
 
 
+@pytest.mark.parametrize("q_off", [0, 37])
+def test_unseen_key_rows_do_not_reach_the_output(mla, q_off):
+    """Key rows that no query of the call can see (causal, past the last
+    query's position) are never part of the result, whatever they hold: NaN
+    there (bf16 0x7fc0), in the rows right after the last visible one inside
+    its tile and in every later tile, leaves the outputs equal to the call on
+    the clean rows (bitwise) and to the oracle."""
+    N, Nkv = 100, 300
+    c = W.dense_case(B=1, H=4, N=N, Nkv=Nkv, seed=41, q_offset=q_off)
+    first_unseen = q_off + N  # the last query sits at q_off + N - 1
+    dirty = c.kv.copy()
+    dirty[:, :, first_unseen:, :] = 0x7fc0
+    q = dev_bf16(c.q)
+    a, la = mla.fwd(q, dev_bf16(c.kv), scale=c.scale, q_offset=q_off)
+    b, lb = mla.fwd(q, dev_bf16(dirty), scale=c.scale, q_offset=q_off)
+    torch.cuda.synchronize()
+    assert not torch.isnan(b).any() and not torch.isnan(lb).any()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    o_ref, l_ref = oracle.dense_mla(c.q, c.kv, 512, c.scale, q_offset=q_off)
+    assert report_o("unseen rows O", host(b), o_ref) <= 1.0
+    assert report("unseen rows LSE", host(lb), l_ref) <= LSE_TOL
+
+
 def test_dense_rope_split_equals_single_tensor(mla):
     """Passing the 64 RoPE columns as separate q_rope/k_rope tensors reads the
     same values: bitwise equal to the single 576-column call."""
