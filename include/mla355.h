@@ -107,7 +107,9 @@ typedef struct {
  * Masking: with MLA_CAUSAL, query row i sits at global position q_offset + i
  * and key row j at kv_offset + j, and j is visible iff its position is not
  * after i's (TT-NN logical_n: positions are global; Ascend maskType 1 = TRIU).
- * Without it every key is visible.
+ * Without it every key is visible.  Key rows that no query row of the call
+ * can see are never read into the result, so they may hold any bits (NaN
+ * included).
  *
  * Varlen (Ascend seqLen of shape [batch]): when seq_lens (device int32
  * [n_seqs]) is given, B must be 1 and Nq == Nkv == the token count T; the
