@@ -86,7 +86,7 @@ def hold_stream():
 def time_launches(fn, steps: int, warmup: int, hold: bool = False, per_launch: bool = True):
     """Warm up, then time `steps` calls with HIP events on the current stream;
     returns (ms per step over the whole region, mean ms per launch, min ms per
-    launch).  ``per_launch`` False: only the region is bracketed by events
+    launch, median ms per launch).  ``per_launch`` False: only the region is bracketed by events
     (each event record is a packet of its own on the queue, a few
     microseconds beside short calls) and the per-launch figures are the
     region's mean.  ``hold``: the calls also queue up behind hold_stream()
@@ -115,9 +115,9 @@ def time_launches(fn, steps: int, warmup: int, hold: bool = False, per_launch: b
     torch.cuda.synchronize()
     region = t0.elapsed_time(t1) / steps
     if not per_launch:
-        return region, region, region
+        return region, region, region, region
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return region, float(np.mean(per)), float(np.min(per))
+    return region, float(np.mean(per)), float(np.min(per)), float(np.median(per))
 
 
 SCLK_FILES = ("/sys/class/drm/card0/device/pp_dpm_sclk",)
@@ -500,7 +500,7 @@ def main():
 
     print("bench: timing", file=sys.stderr, flush=True)
     with ClockSampler() as clk:
-        region_ms, launch_ms, launch_min_ms = time_launches(step, args.steps, args.warmup)
+        region_ms, launch_ms, launch_min_ms, launch_med_ms = time_launches(step, args.steps, args.warmup)
     flops = B * H * causal_pairs(N, N) * (2 * dk + 2 * 512)
     value = flops / (region_ms * 1e-3) / 1e12
     achieved = flops / (launch_ms * 1e-3) / 1e12
@@ -531,7 +531,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "attn_fwd_kernel<LatentCfg, LATENT>",
-                     "launch_ms_mean": round(launch_ms, 4), "launch_ms_min": round(launch_min_ms, 4)},
+                     "launch_ms_mean": round(launch_ms, 4), "launch_ms_min": round(launch_min_ms, 4),
+                     "launch_ms_median": round(launch_med_ms, 4)},
         "engine_clock": clock,
     }
     # The same achieved rate against the peak at the shader clock the kernel
@@ -618,8 +619,8 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
         a, b = o[:, :, :1024].contiguous(), o[:, :, 1024:2048].contiguous()
         la, lb = l[:, :, :1024].contiguous(), l[:, :, 1024:2048].contiguous()
         mo, ml = torch.empty_like(a), torch.empty_like(la)
-        ms, _, _ = time_launches(lambda: mla.merge(a, la, b, lb, out=mo, lse=ml), steps, warmup, hold=True,
-                                 per_launch=False)
+        ms = time_launches(lambda: mla.merge(a, la, b, lb, out=mo, lse=ml), steps, warmup, hold=True,
+                                 per_launch=False)[0]
         nbytes = 3 * a.numel() * 2 + 3 * la.numel() * 4
         rows["merge_h16_1024x512"] = {"ms": round(ms, 4), "GBps": round(nbytes / ms / 1e6, 1),
                                       "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
@@ -635,8 +636,8 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
         T = int(c.seq_lens.sum())
         so = torch.empty((T, 32, 128), dtype=torch.bfloat16, device="cuda")
         sL = torch.empty((32, T), dtype=torch.float32, device="cuda")
-        ms, _, _ = time_launches(lambda: mla.split_fwd(*args, scale=c.scale, seq_lens=sl, prev=prev,
-                                                       out=so, lse=sL), steps, warmup, per_launch=False)
+        ms = time_launches(lambda: mla.split_fwd(*args, scale=c.scale, seq_lens=sl, prev=prev,
+                                                       out=so, lse=sL), steps, warmup, per_launch=False)[0]
         fl = 32 * sum(causal_pairs(int(L), int(L)) for L in c.seq_lens) * (2 * 192 + 2 * 128)
         rows["split_varlen_8seq_h32"] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
                                          "pct_of_peak": round(100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
@@ -651,7 +652,7 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
         idx = torch.from_numpy(c.idx).cuda()
         so = torch.empty((1, 4096, 128 * 512), dtype=torch.bfloat16, device="cuda")
         sL = torch.empty((1, 4096, 128), dtype=torch.float32, device="cuda")
-        ms, _, _ = time_launches(lambda: mla.sparse_fwd(*t, idx, scale=c.scale, out=so, lse=sL), steps, warmup, per_launch=False)
+        ms = time_launches(lambda: mla.sparse_fwd(*t, idx, scale=c.scale, out=so, lse=sL), steps, warmup, per_launch=False)[0]
         fl = 4096 * 128 * 2048 * 2176
         gathered = 4096 * 2048 * 1152
         rows["sparse_topk_s4096_k2048_h128"] = {
@@ -676,8 +677,8 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
         B, H = c.q.shape[:2]
         do = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
         dl = torch.empty((B, H), dtype=torch.float32, device="cuda")
-        ms, _, _ = time_launches(lambda: mla.decode_fwd(q, kv, scale=c.scale, kv_lens=lens, out=do, lse=dl),
-                                 steps, warmup, per_launch=False)
+        ms = time_launches(lambda: mla.decode_fwd(q, kv, scale=c.scale, kv_lens=lens, out=do, lse=dl),
+                                 steps, warmup, per_launch=False)[0]
         keys = int(c.kv_lens.astype(np.int64).sum())
         fl = H * keys * 2176
         # algorithmic HBM bytes: each cache row once, the queries, outputs and LSEs
@@ -701,7 +702,7 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
         o, w = to_dev(c.o), to_dev(c.w_uv)
         B, H, T, L = c.o.shape
         vo = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
-        ms, _, _ = time_launches(lambda: mla.vup(o, w, out=vo), steps, warmup, per_launch=False)
+        ms = time_launches(lambda: mla.vup(o, w, out=vo), steps, warmup, per_launch=False)[0]
         fl = B * H * T * L * 128 * 2
         nbytes = o.numel() * 2 + w.numel() * 2 + vo.numel() * 2   # each operand once
         rows["vup_h128_t8192"] = {
@@ -720,8 +721,8 @@ def measure_rows(mla, W, to_dev, steps, warmup, per_launch=False, only=None):
         B, H, N, _ = c.q8.shape
         fo = torch.empty((B, H, N, 512), dtype=torch.bfloat16, device="cuda")
         fl_ = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-        ms, _, _ = time_launches(lambda: mla.fwd_fp8(q8, kv8, scale=c.scale, out=fo, lse=fl_), steps, warmup,
-                                 per_launch=False)
+        ms = time_launches(lambda: mla.fwd_fp8(q8, kv8, scale=c.scale, out=fo, lse=fl_), steps, warmup,
+                                 per_launch=False)[0]
         fl = B * H * causal_pairs(N, N) * 2176
         rows["prefill_fp8_dsv3_h128_n8192"] = {
             "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 2),
