@@ -348,6 +348,8 @@ def summarize_counters(folders, kernel, out_path, cmds):
                 derived.append((label, vals[k] / vals["SQ_WAVE_CYCLES"]))
     if vals.get("TCC_HIT_sum") is not None and vals.get("TCC_MISS_sum"):
         derived.append(("L2 hit rate", vals["TCC_HIT_sum"] / (vals["TCC_HIT_sum"] + vals["TCC_MISS_sum"])))
+    if vals.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_LDS" in vals:
+        derived.append(("waves waiting on an LDS instruction", vals["SQ_WAIT_INST_LDS"] / vals["SQ_WAVE_CYCLES"]))
     if vals.get("SQ_INSTS_MFMA"):
         for k in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
             if k in vals:
