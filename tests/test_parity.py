@@ -1020,7 +1020,8 @@ def test_ring_two_batches_strided_q(mla):
 def test_random_shapes_all_forms(mla, seed):
     """Random sizes, offsets, masks, head groupings, sequence lengths (zero
     included), prev folds and decode valid lengths, drawn from a fixed seed:
-    the dense, sparse, split and decode forms against the oracle."""
+    the dense, sparse, split (one- and two-row lengths), decode and ring forms
+    against the oracle."""
     r = np.random.default_rng(1000 + seed)
     # dense: batches, heads, query and key counts, offsets, mask
     B, H = int(r.integers(1, 3)), int(r.integers(1, 10))
@@ -1064,3 +1065,24 @@ def test_random_shapes_all_forms(mla, seed):
     o_ref, l_ref = oracle.decode_mla(cd.q, cd.kv, cd.kv_lens, 512, cd.scale)
     assert report_o("random decode O", host(o), o_ref) <= 1.0
     assert report("random decode LSE", host(l), l_ref) <= LSE_TOL
+    # split with separate key lengths ([2, batch]; zeros allowed), with or without the mask
+    nq = len(lens)
+    ql2 = [int(x) for x in r.integers(0, 200, nq)]
+    kl2 = [int(x) for x in r.integers(0, 260, nq)]
+    ql2[0], kl2[0] = max(ql2[0], 1), max(kl2[0], 1)
+    causal2 = bool(r.integers(0, 2))
+    c2 = W.split_case(seq_lens=ql2, kv_lens=kl2, H=Hsp, Hkv=Hkv, seed=seed + 50, with_prev=bool(r.integers(0, 2)))
+    o, o32, l = _split_twin(mla, c2, causal=causal2)
+    o_ref, l_ref = oracle.split_mla(c2.q1, c2.q2, c2.k1, c2.k2, c2.v, c2.seq_lens, c2.scale, causal=causal2,
+                                    prev_out=c2.prev_out, prev_lse=c2.prev_lse)
+    _twin("random split two-row", o, o32, o_ref)
+    assert report("random split two-row LSE", host(l), l_ref) <= LSE_TOL
+    # the one-device ring: length, chunk count, heads, schedule
+    Nr, P, Hr = int(r.integers(1, 600)), int(r.integers(1, 7)), int(r.integers(1, 9))
+    order = str(r.choice(["ring", "balanced"]))
+    cr = W.dense_case(B=1, H=Hr, N=Nr, seed=seed + 100)
+    o, l = mla.ring_fwd(dev_bf16(cr.q), dev_bf16(cr.kv), P, scale=cr.scale, order=order)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_mla(cr.q, cr.kv, 512, cr.scale)
+    assert report_o(f"random ring P={P} {order} O", host(o), o_ref) <= 1.0
+    assert report("random ring LSE", host(l), l_ref) <= LSE_TOL
