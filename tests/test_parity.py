@@ -90,14 +90,16 @@ def test_dense_ragged(mla, B, H, N, Nkv, q_off, kv_off, causal, seed):
     assert report("LSE", host(lse), l_ref) <= LSE_TOL
 
 
-@pytest.mark.parametrize("q_off", [0, 37])
-def test_unseen_key_rows_do_not_reach_the_output(mla, q_off):
+@pytest.mark.parametrize("N,q_off", [(100, 0), (100, 37), (40, 0), (40, 37), (7, 0)])
+def test_unseen_key_rows_do_not_reach_the_output(mla, N, q_off):
     """Key rows that no query of the call can see (causal, past the last
     query's position) are never part of the result, whatever they hold: NaN
     there (bf16 0x7fc0), in the rows right after the last visible one inside
     its tile and in every later tile, leaves the outputs equal to the call on
-    the clean rows (bitwise) and to the oracle."""
-    N, Nkv = 100, 300
+    the clean rows (bitwise) and to the oracle.  With N = 40 and 7 the last
+    visible key falls in one of the first three key tiles, which the key loop
+    copies before it starts."""
+    Nkv = 300
     c = W.dense_case(B=1, H=4, N=N, Nkv=Nkv, seed=41, q_offset=q_off)
     first_unseen = q_off + N  # the last query sits at q_off + N - 1
     dirty = c.kv.copy()
