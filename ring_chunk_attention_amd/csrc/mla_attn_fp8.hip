@@ -152,7 +152,9 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
   }
   auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
     const int64_t k0 = (int64_t)t * F8_BN;
-    const uint32_t nrows = (uint32_t)min<int64_t>(F8_BN, kv_len - k0);
+    // rows [k0, min(k0 + BN, kv_end)): those past it, which no row of the
+    // workgroup sees, read zeros (whatever they hold stays out of P.V)
+    const uint32_t nrows = (uint32_t)min<int64_t>(F8_BN, kv_end - k0);
     const u32x4 rs = make_rsrc(Kb + k0 * stK, nrows * (uint32_t)stK);
     const uint32_t base = lds_t + (uint32_t)buf * F8_TILE;
     copy_rows<4>(rs, base, w, voA0);

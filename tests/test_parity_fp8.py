@@ -176,3 +176,19 @@ def test_fp8_dsv3_full_size_sampled(mla):
     o_ref, l_ref, bound = _ref(c, rows=rows, heads=heads)
     _check("fp8 dsv3", out[:, heads][:, :, rows], lse[:, heads][:, :, rows], o_ref, l_ref, bound)
     assert not torch.isnan(out).any() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("N,q_off", [(100, 0), (40, 37), (7, 0)])
+def test_fp8_unseen_key_rows_do_not_reach_the_output(mla, N, q_off):
+    """As for the bf16 form: key rows past the last query's position hold
+    e4m3 NaN codes (0x7f) from the first unseen row on, inside the last
+    visible tile and after it; the outputs equal the call on the clean rows
+    bitwise and hold no NaN."""
+    c = W.fp8_dense_case(B=1, H=4, N=N, Nkv=300, seed=71, q_offset=q_off)
+    dirty = c.kv8.copy()
+    dirty[:, :, q_off + N:, :] = 0x7F
+    a, la = mla.fwd_fp8(_codes(c.q8), _codes(c.kv8), scale=c.scale, q_offset=q_off)
+    b, lb = mla.fwd_fp8(_codes(c.q8), _codes(dirty), scale=c.scale, q_offset=q_off)
+    torch.cuda.synchronize()
+    assert not torch.isnan(b).any() and not torch.isnan(lb).any()
+    assert torch.equal(a, b) and torch.equal(la, lb)
