@@ -391,6 +391,32 @@ def test_split_non_causal(mla, with_prev):
     assert report("split non-causal LSE", host(lse), l_ref) <= LSE_TOL
 
 
+@pytest.mark.parametrize("gpu_lens,eff_lens", [
+    ([50, -3, 40], [50, 40]),    # a negative length counts as 0; tokens past the sum stay unwritten
+    ([100, 60], [100, 20]),      # the lengths are clipped to the tokens there are
+    ([0, 70, 0], [70]),          # empty sequences around one
+])
+def test_split_lengths_read_on_the_device(mla, gpu_lens, eff_lens):
+    """seq_lens is read on the device, unchecked before launch: a negative
+    length counts as 0, the sum is clipped to T, and tokens past it keep what
+    the output held."""
+    T = 120
+    c = W.split_case(seq_lens=eff_lens + ([T - sum(eff_lens)] if sum(eff_lens) < T else []), H=4, Hkv=2,
+                     seed=93, with_prev=False)
+    args = [dev_bf16(x) for x in (c.q1, c.q2, c.k1, c.k2, c.v)]
+    out = torch.full((T, 4, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((4, T), 7.0, dtype=torch.float32, device="cuda")
+    mla.split_fwd(*args, scale=c.scale, seq_lens=dev(np.array(gpu_lens, np.int32)), out=out, lse=lse)
+    torch.cuda.synchronize()
+    n = sum(eff_lens)
+    o_ref, l_ref = oracle.split_mla(c.q1[:n], c.q2[:n], c.k1[:n], c.k2[:n], c.v[:n],
+                                    np.array(eff_lens, np.int32), c.scale)
+    o, l = host(out), host(lse)
+    assert report_o("split device lengths O", o[:n], o_ref) <= 1.0
+    assert report("split device lengths LSE", l[:, :n], l_ref) <= LSE_TOL
+    assert np.all(o[n:] == 7.0) and np.all(l[:, n:] == 7.0)
+
+
 @pytest.mark.parametrize("causal,with_prev", [(True, True), (True, False), (False, True)])
 def test_split_two_row_lengths(mla, causal, with_prev):
     """[2, batch] lengths (MLA_SEQ_LENS_QK, Ascend seqLen's second form):
@@ -719,6 +745,27 @@ def test_decode_small(mla, B, H, Nkv, lens, n_splits):
     o_ref, l_ref = oracle.decode_mla(c.q, c.kv, c.kv_lens, 512, c.scale)
     assert report_o("decode O", host(out), o_ref) <= 1.0
     assert report("decode LSE", host(lse), l_ref) <= LSE_TOL
+
+
+@pytest.mark.parametrize("n_splits", [0, 2])
+def test_decode_lengths_clamped_and_rows_past_them_unread(mla, n_splits):
+    """kv_lens outside [0, Nkv] are clamped (-5 reads nothing, 5000 reads all
+    3000 rows), and cache rows past a sequence's valid length are never read:
+    NaN there (bf16 0x7fc0) leaves the result bitwise that of the clean
+    cache."""
+    c = W.decode_case(B=4, H=16, Nkv=3000, kv_lens=[-5, 5000, 17, 2048], seed=76)
+    dirty = c.kv.copy()
+    for b, n in enumerate(np.clip(c.kv_lens, 0, 3000)):
+        dirty[b, n:] = 0x7fc0
+    q, lens = dev_bf16(c.q), dev(c.kv_lens)
+    o1, l1 = mla.decode_fwd(q, dev_bf16(c.kv), scale=c.scale, kv_lens=lens, n_splits=n_splits)
+    o2, l2 = mla.decode_fwd(q, dev_bf16(dirty), scale=c.scale, kv_lens=lens, n_splits=n_splits)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o2).any()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, l_ref = oracle.decode_mla(c.q, c.kv, np.clip(c.kv_lens, 0, 3000), 512, c.scale)
+    assert report_o("decode clamped O", host(o1), o_ref) <= 1.0
+    assert report("decode clamped LSE", host(l1), l_ref) <= LSE_TOL
 
 
 def test_decode_split_rope_tensors_bit_identical(mla):
