@@ -2,12 +2,13 @@
 // separate nope and RoPE parts of q and k, a separate V, varlen seqLen, the
 // prevOut/prevLse fold), in a translation unit of its own so that it can be
 // built with the MFMA accumulators in ordinary VGPRs
-// (-mllvm=-amdgpu-mfma-vgpr-form, device side only).  The form needs about
-// 190 registers, so both the score and the output accumulators fit the VGPR
-// file at two waves per SIMD; with the score accumulator in AGPRs, as the
-// compiler otherwise places it, every key tile cost 16 AGPR->VGPR reads
-// before the softmax and 16 AGPR writes to clear it.  The latent and sparse
-// forms keep their output accumulators in AGPRs (mla_attn.hip).
+// (-mllvm=-amdgpu-mfma-vgpr-form, device side only).  The form is held to
+// 256 registers (two waves per SIMD), which the score accumulators of two
+// key tiles and the output accumulators fit; with the score accumulator in
+// AGPRs, as the compiler otherwise placed it, every key tile cost 16
+// AGPR->VGPR reads before the softmax and 16 AGPR writes to clear it.  The
+// latent and sparse forms keep their output accumulators in AGPRs
+// (mla_attn.hip).
 #include "mla_attn_kernels.inc"
 
 namespace mla {
