@@ -391,6 +391,55 @@ def test_split_non_causal(mla, with_prev):
     assert report("split non-causal LSE", host(lse), l_ref) <= LSE_TOL
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,Nkv,q_off,kv_off,causal,with_prev", [
+    (2, 4, 2, 150, 170, 20, 0, True, False),
+    (1, 8, 1, 40, 300, 0, 0, True, True),       # most key rows past every query
+    (2, 2, 2, 200, 90, 0, 50, False, True),     # no mask
+    (1, 4, 4, 33, 33, 0, 0, True, False),
+])
+def test_split_form_batched_with_offsets(mla, B, Hq, Hkv, N, Nkv, q_off, kv_off, causal, with_prev):
+    """The split form through mla_fwd without seq_lens: [B, H, N, D] views
+    with separate nope/RoPE parts and V, query and key offsets and the mask,
+    as the plain attention of the concatenated parts.  Key and value rows past
+    every query's position hold NaN, which must not reach the result."""
+    rng = np.random.default_rng(500 + N)
+    q1, q2 = W.normal_bf16(rng, (B, Hq, N, 128)), W.normal_bf16(rng, (B, Hq, N, 64))
+    k1, k2 = W.normal_bf16(rng, (B, Hkv, Nkv, 128)), W.normal_bf16(rng, (B, Hkv, Nkv, 64))
+    v = W.normal_bf16(rng, (B, Hkv, Nkv, 128))
+    scale = W.SCALE_192
+    prev = None
+    if with_prev:
+        prev_o = W.normal_bf16(rng, (B, Hq, N, 128))
+        prev_l = rng.uniform(0, 8, (B, Hq, N)).astype(np.float32)
+    dirty = [x.copy() for x in (k1, k2, v)]
+    first_unseen = q_off + N - kv_off  # key index of the first row no query sees
+    if causal and first_unseen < Nkv:
+        for x in dirty:
+            x[:, :, max(first_unseen, 0):] = 0x7fc0
+
+    def run(ks, f32=False):
+        pv = (dev_bf16(prev_o), dev(prev_l)) if with_prev else None
+        out = torch.empty((B, Hq, N, 128), dtype=torch.float32, device="cuda") if f32 else None
+        o, l = mla.fwd(dev_bf16(q1), dev_bf16(ks[0]), scale=scale, causal=causal, q_offset=q_off,
+                       kv_offset=kv_off, q_rope=dev_bf16(q2), k_rope=dev_bf16(ks[1]), v=dev_bf16(ks[2]),
+                       prev=pv, out=out)
+        torch.cuda.synchronize()
+        return o, l
+
+    out, lse = run((k1, k2, v))
+    o32, l32 = run((k1, k2, v), f32=True)
+    od, ld = run(dirty)
+    assert torch.equal(lse, l32)
+    assert not torch.isnan(od).any() and torch.equal(od, out) and torch.equal(ld, lse)
+    cat = lambda a, b: np.concatenate([a, b], axis=-1)
+    o_ref, l_ref = oracle.dense_mla(cat(q1, q2), cat(k1, k2), 128, scale, causal=causal, q_offset=q_off,
+                                    kv_offset=kv_off, v=v)
+    if with_prev:
+        o_ref, l_ref = oracle.merge(prev_o, prev_l, o_ref, l_ref)
+    _twin("split batched", out, o32, o_ref)
+    assert report("split batched LSE", host(lse), l_ref) <= LSE_TOL
+
+
 @pytest.mark.parametrize("gpu_lens,eff_lens", [
     ([50, -3, 40], [50, 40]),    # a negative length counts as 0; tokens past the sum stay unwritten
     ([100, 60], [100, 20]),      # the lengths are clipped to the tokens there are
@@ -1069,8 +1118,8 @@ def test_ring_two_batches_strided_q(mla):
 def test_random_shapes_all_forms(mla, seed):
     """Random sizes, offsets, masks, head groupings, sequence lengths (zero
     included), prev folds and decode valid lengths, drawn from a fixed seed:
-    the dense, sparse, split (one- and two-row lengths), decode and ring forms
-    against the oracle."""
+    the dense, sparse, split (one- and two-row lengths, and batched views
+    with offsets), decode and ring forms against the oracle."""
     r = np.random.default_rng(1000 + seed)
     # dense: batches, heads, query and key counts, offsets, mask
     B, H = int(r.integers(1, 3)), int(r.integers(1, 10))
@@ -1126,6 +1175,20 @@ def test_random_shapes_all_forms(mla, seed):
                                     prev_out=c2.prev_out, prev_lse=c2.prev_lse)
     _twin("random split two-row", o, o32, o_ref)
     assert report("random split two-row LSE", host(l), l_ref) <= LSE_TOL
+    # the split form over [B, H, N, D] views: batches, head grouping, offsets, mask
+    Bb, Nb, Nkb = int(r.integers(1, 3)), int(r.integers(1, 200)), int(r.integers(1, 260))
+    qob, kob, cb = int(r.integers(0, 100)), int(r.integers(0, 100)), bool(r.integers(0, 2))
+    qs = [W.normal_bf16(r, (Bb, Hsp, Nb, d)) for d in (128, 64)]
+    ks = [W.normal_bf16(r, (Bb, Hkv, Nkb, d)) for d in (128, 64, 128)]
+    kw = dict(scale=W.SCALE_192, causal=cb, q_offset=qob, kv_offset=kob, q_rope=dev_bf16(qs[1]),
+              k_rope=dev_bf16(ks[1]), v=dev_bf16(ks[2]))
+    o, l = mla.fwd(dev_bf16(qs[0]), dev_bf16(ks[0]), **kw)
+    o32, _ = mla.fwd(dev_bf16(qs[0]), dev_bf16(ks[0]), out=_f32(o), **kw)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_mla(np.concatenate(qs, -1), np.concatenate(ks[:2], -1), 128, W.SCALE_192,
+                                    causal=cb, q_offset=qob, kv_offset=kob, v=ks[2])
+    _twin("random split batched", o, o32, o_ref)
+    assert report("random split batched LSE", host(l), l_ref) <= LSE_TOL
     # the one-device ring: length, chunk count, heads, schedule
     Nr, P, Hr = int(r.integers(1, 600)), int(r.integers(1, 7)), int(r.integers(1, 9))
     order = str(r.choice(["ring", "balanced"]))
