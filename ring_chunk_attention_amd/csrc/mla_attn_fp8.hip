@@ -91,6 +91,14 @@ __device__ __forceinline__ void mfma8_v(f32x16& acc, const i32x8& a, const i32x8
   asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
+// max of three by one v_max3_f32, without the quieting of signalling NaN
+// inputs that fmaxf asks for (MFMA results are never signalling)
+__device__ __forceinline__ float f8_max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_fp8_kernel(const AttnParams p) {
   __shared__ SmemF8 sm;
@@ -373,11 +381,12 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
       O[rb][j] = mfma8(vcur, pf[rb], O[rb][j]);
       if constexpr (g < 4) {
         // partial maxima of 8 scores each
-        float m = fmaxf(fmaxf(x[8 * g], x[8 * g + 1]), fmaxf(x[8 * g + 2], x[8 * g + 3]));
-        m = fmaxf(m, fmaxf(fmaxf(x[8 * g + 4], x[8 * g + 5]), fmaxf(x[8 * g + 6], x[8 * g + 7])));
-        mp[g] = m;
+        float m = f8_max3(x[8 * g], x[8 * g + 1], x[8 * g + 2]);
+        m = f8_max3(m, x[8 * g + 3], x[8 * g + 4]);
+        m = f8_max3(m, x[8 * g + 5], x[8 * g + 6]);
+        mp[g] = f8_max3(m, x[8 * g + 7], x[8 * g + 7]);
         if constexpr (g == 3) {
-          float mt = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+          float mt = f8_max3(f8_max3(mp[0], mp[1], mp[2]), mp[3], mp[3]);
           mt = xhalf_max(mt) * sm_scale;
           m_run = fmaxf(m_run, mt);
           m_ref = m_ref == -INFINITY ? mt : m_ref;
