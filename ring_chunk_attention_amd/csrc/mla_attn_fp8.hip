@@ -399,7 +399,10 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) e[4 * q + d] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[4 * q + d], sm_scale, -mu));
         l_part += (e[4 * q] + e[4 * q + 1]) + (e[4 * q + 2] + e[4 * q + 3]);
-        int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * q], e[4 * q + 1], 0, false);
+        // (the pair conversions write one half each, so the register's old
+        // value, the previous tile's weights already summed, is overwritten
+        // whole: no zeroing move)
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * q], e[4 * q + 1], pk[q / 4][q % 4], false);
         v = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * q + 2], e[4 * q + 3], v, true);
         pk[q / 4][q % 4] = v;
       } else {
