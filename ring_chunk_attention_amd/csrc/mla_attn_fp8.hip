@@ -202,6 +202,7 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
 
   f32x16 O[WAVES][4];
   float m_ref = -INFINITY, m_run = -INFINITY, l_part = 0.f, l_rnd = 0.f;
+  float mu_fix = 0.f;  // the weights' reference past tile 0
   bool over = false;
 
   // S^T halves of tile `buf` (lane: query row lr; keys 32kh + 8(r/4) + 4h + r%4).
@@ -388,10 +389,11 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
         if constexpr (g == 3) {
           float mt = f8_max3(f8_max3(mp[0], mp[1], mp[2]), mp[3], mp[3]);
           mt = xhalf_max(mt) * sm_scale;
-          m_run = fmaxf(m_run, mt);
-          m_ref = m_ref == -INFINITY ? mt : m_ref;
-          over |= m_run > m_ref + F8_TAU;
-          mu = m_ref == -INFINITY ? 0.f : m_ref;
+          // Past tile 0 the reference is fixed (a row that sees any key
+          // sees key 0) and m_run only grows: the overflow check waits for
+          // the end of the tile loop.
+          m_run = f8_max3(m_run, mt, mt);
+          mu = mu_fix;
         }
       } else if constexpr (g < 12) {
         // four weights, their exact sum and the e4m3 pair packing
@@ -458,6 +460,7 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
         prep(s0, s1, 0, true, x);
         softmax(x, 0, pk);
       }
+      mu_fix = m_ref == -INFINITY ? 0.f : m_ref;
       __syncthreads();
       for (int t = 0; t < n_tiles; ++t) {
         const int buf = t & (F8_NB - 1), nbuf = (t + 1) & (F8_NB - 1), cbuf = (t + F8_NB - 1) & (F8_NB - 1);
@@ -482,6 +485,7 @@ void attn_fwd_fp8_kernel(const AttnParams p) {
         const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
         l_rnd += (lo[0] + lo[1]) + (hi[0] + hi[1]);
       }
+      over |= m_run > m_ref + F8_TAU;
     }
     if (pass == 0) {
       const bool any = __ballot(over) != 0ull;
